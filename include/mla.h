@@ -1,0 +1,170 @@
+/*
+ * mla.h - C ABI of the MI355X (gfx950) absorbed multi-head latent attention
+ * (MLA) decode library.
+ *
+ * Two operations:
+ *
+ *  mla_decode  Absorbed MLA decode for one query token per sequence.  All H
+ *              query heads of a sequence attend to the same latent KV rows of
+ *              576 values (512 latent "nope" columns, then 64 rope columns):
+ *                  S[h,t] = scale * (q[h,0:512].k[t,0:512] + q[h,512:576].k[t,512:576])
+ *                  LSE[h] = ln sum_t exp(S[h,t]),  O[h,:] = sum_t exp(S[h,t]-LSE[h]) k[t,0:512]
+ *              Sources: the "STAGE_D2" MQA decode design note (section "DSV4 is
+ *              MQA": one shared K/V for all query heads; "Strategy A: Head-Packed
+ *              M Dimension": all heads of a token share one K/V read, softmax per
+ *              head row), and FlashMLA issue "dual gemm" (the 64 rope columns
+ *              are an extra block of the same QK^T product; invalid KV slots are
+ *              masked when P is formed).  V is the 512 latent columns of the same
+ *              row.  Variants: dense paged bf16 cache, FP8 e4m3 cache with one
+ *              fp32 scale per 128 latent columns (rope kept in bf16), and top-k
+ *              sparse index lists.
+ *
+ *  mla_query   The query front end of the vLLM MlaQuery kernel (API page of
+ *              vllm.models.kimi_k3...mla.query, class MlaQuery, method
+ *              `kernel`): RMSNorm of the 1536-wide q_a part of qkv with w_qa,
+ *              Q_B projection to 192 rows per head (128 nope + 64 rope), W_UK
+ *              absorption of the nope rows into 512 latent columns, and e4m3
+ *              encoding of [absorbed 512 | rope 64] after multiplying by
+ *              q_scale_inv.  Intermediates are rounded to bf16 after RMSNorm,
+ *              after Q_B and after W_UK, as on that page.
+ *
+ * Conventions (all entry points):
+ *  - Every data pointer is device memory owned by the caller.  The library
+ *    keeps no per-call state and allocates no device memory in these calls;
+ *    scratch space is the caller's `workspace`, sized by the *_workspace_size
+ *    call.  Host structs are read during the call only.
+ *  - Calls are asynchronous on `stream` (a hipStream_t; NULL = the legacy
+ *    default stream) and may be issued from several host threads on different
+ *    streams.  Two calls that share a workspace must be ordered on one stream.
+ *  - Arguments are validated on the host before any HIP call; on a validation
+ *    error nothing is launched and outputs are untouched.  Return value 0 on
+ *    success, a negative MLA_ERR_* code otherwise; mla_status_string() names it.
+ *  - Device-side preconditions that cannot be checked without reading device
+ *    memory are stated per argument; the kernels clamp every table-derived
+ *    index into its documented range so that a violated precondition yields
+ *    wrong values, never an out-of-bounds access.
+ *  - Layouts are row-major and contiguous unless a stride is given.
+ *  - bf16 = IEEE binary32 upper half; FP8 = OCP e4m3fn (max 448, 0x7F/0xFF NaN).
+ */
+#ifndef MLA_H_
+#define MLA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ---- status codes ---- */
+#define MLA_OK 0
+#define MLA_ERR_INVALID_ARG (-1)  /* null pointer, non-positive size, bad enum */
+#define MLA_ERR_UNSUPPORTED (-2)  /* shape/dtype combination not implemented */
+#define MLA_ERR_WORKSPACE (-3)    /* workspace NULL or smaller than required */
+#define MLA_ERR_LAUNCH (-4)       /* a kernel launch failed (hipGetLastError) */
+#define MLA_ERR_DEVICE (-5)       /* no usable HIP device / device query failed */
+
+/* ---- element types ---- */
+#define MLA_DTYPE_BF16 1
+#define MLA_DTYPE_FP8_E4M3 2
+
+/* ---- fixed geometry ---- */
+#define MLA_D_QK 576        /* latent row width: 512 nope + 64 rope */
+#define MLA_D_V 512         /* value width: the 512 nope columns */
+#define MLA_PAGE_SIZE 64    /* tokens per KV page */
+#define MLA_FP8_ROW_BYTES 640 /* FP8 cache row: 512 e4m3 codes + 64 bf16 rope */
+#define MLA_MAX_HEADS 128
+#define MLA_MAX_BATCH 8192
+
+typedef struct mla_decode_params {
+  int32_t batch;             /* B >= 1, <= MLA_MAX_BATCH */
+  int32_t heads;             /* H: 8, 16, 32, 64 or 128 query heads (one token each) */
+  int32_t num_pages;         /* pages in the KV pool, >= 1 */
+  int32_t max_pages_per_seq; /* columns of block_table, >= 1 */
+  int32_t topk;              /* 0: dense over [0, seqlen); > 0: entries per row of topk_idx */
+  int32_t q_dtype;           /* MLA_DTYPE_BF16 or MLA_DTYPE_FP8_E4M3 */
+  int32_t kv_dtype;          /* MLA_DTYPE_BF16 or MLA_DTYPE_FP8_E4M3 */
+  float softmax_scale;       /* multiplies the full 576-wide dot, e.g. 192^-0.5 */
+  float q_descale;           /* FP8 queries: value = code * q_descale (= 1/q_scale_inv); ignored for bf16 */
+} mla_decode_params;
+
+/*
+ * Bytes of scratch that mla_decode needs for `p` on the current HIP device
+ * (split-KV partial results).  Writes *bytes; queries the device's compute
+ * unit count, so it returns MLA_ERR_DEVICE without a GPU.
+ */
+int32_t mla_decode_workspace_size(const mla_decode_params* p, size_t* bytes);
+
+/*
+ * Absorbed MLA decode, one query token per sequence.
+ *
+ *  q           [B, H, 576] bf16, or e4m3 codes when q_dtype is FP8 (the
+ *              MlaQuery output layout: cols 0..511 absorbed latent q, 512..575
+ *              rope q).  Row stride 576 elements.
+ *  kv_cache    bf16 cache: [num_pages, 64, 576] bf16.
+ *              FP8 cache:  [num_pages, 64, 640] bytes per row = 512 e4m3 codes
+ *              of the latent columns, then the 64 rope values as bf16.
+ *  block_table [B, max_pages_per_seq] int32: physical page of logical page j of
+ *              sequence b; logical position t lives in row
+ *              block_table[b, t/64]*64 + t%64 (the page/offset split of a slot
+ *              in MlaQuery.insert).  Precondition: entries in [0, num_pages).
+ *  seqlens     [B] int32: tokens of each sequence.  Precondition:
+ *              0 <= seqlens[b] <= 64*max_pages_per_seq.  A sequence with nothing
+ *              to attend gets O = 0 and LSE = -inf.
+ *  topk_idx    NULL when topk == 0; else [B, topk] int32 logical positions
+ *              (sparse decode).  Entries that are -1 or outside [0, seqlens[b])
+ *              are masked (contribute nothing); duplicates count once per entry.
+ *  kv_scales   NULL for a bf16 cache; for an FP8 cache [num_pages, 64, 4] fp32,
+ *              one scale per row and 128-column tile: k[d] = code[d]*scale[d/128]
+ *              for d < 512.
+ *  out         [B, H, 512] bf16 (round to nearest even).
+ *  lse         [B, H] fp32, natural-log log-sum-exp of the scaled scores.
+ *  workspace   device scratch of at least mla_decode_workspace_size bytes;
+ *              contents need no initialisation and are clobbered.
+ */
+int32_t mla_decode(const mla_decode_params* p, const void* q, const void* kv_cache,
+                   const int32_t* block_table, const int32_t* seqlens,
+                   const int32_t* topk_idx, const float* kv_scales, void* out,
+                   float* lse, void* workspace, size_t workspace_bytes, void* stream);
+
+typedef struct mla_query_params {
+  int32_t batch;       /* tokens B >= 1, <= MLA_MAX_BATCH */
+  int32_t heads;       /* H >= 1, <= MLA_MAX_HEADS */
+  int32_t qkv_stride;  /* elements between rows of qkv, >= 1536 */
+  float eps;           /* RMSNorm epsilon, >= 0 */
+} mla_query_params;
+
+/* Bytes of scratch that mla_query needs for `p` (the bf16 nope rows of Q_B). */
+int32_t mla_query_workspace_size(const mla_query_params* p, size_t* bytes);
+
+/*
+ * MLA query front end.
+ *
+ *  qkv         [B, qkv_stride] bf16; columns 0..1535 (q_a) are read.
+ *  w_qa        [1536] bf16 RMSNorm weight.
+ *  w_qb        [H*192, 1536] bf16; row h*192 + r is head h's Q_B row r
+ *              (r < 128 nope, 128 <= r < 192 rope).
+ *  w_uk        [H, 128, 512] bf16; absorbed q[h, c] = sum_p qb_nope[h, p] * w_uk[h, p, c].
+ *  q_scale_inv device fp32 scalar; FP8 output = e4m3(value * q_scale_inv[0]),
+ *              rounded to nearest even and saturated to +-448 (never 0xFF).
+ *  out         [B, H, 576] e4m3 codes: cols 0..511 the absorbed latent query,
+ *              512..575 the rope query.
+ *  workspace   at least mla_query_workspace_size bytes.
+ *
+ *  RMSNorm: rr = 1/sqrt(sum(x^2)/1536 + eps), xn = bf16((x*rr)*w_qa).
+ */
+int32_t mla_query(const mla_query_params* p, const void* qkv, const void* w_qa,
+                  const void* w_qb, const void* w_uk, const float* q_scale_inv,
+                  void* out, void* workspace, size_t workspace_bytes, void* stream);
+
+/* Static text for a status code. */
+const char* mla_status_string(int32_t status);
+
+/* Library ABI version (major*10000 + minor*100 + patch). */
+int32_t mla_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MLA_H_ */

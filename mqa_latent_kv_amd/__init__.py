@@ -1,1 +1,261 @@
-"""MI355X-native absorbed MLA decode library (binding loaded lazily)."""
+"""MI355X-native absorbed MLA decode: thin Python binding of libmla.so.
+
+The binding only marshals arguments (tensor checks, pointers, the current HIP
+stream) into the C ABI declared in include/mla.h; every step of the
+computation runs in the library's gfx950 kernels.  PyTorch provides device
+memory and streams.  The functions raise if libmla.so is missing or a call
+returns an error status; there is no fallback path.
+
+Entry points (same names as the C ABI):
+    mla_decode(q, kv_cache, block_table, seqlens, topk_idx=None, kv_scales=None,
+               out=None, lse=None, ...)
+    mla_query(qkv, w_qa, w_qb, w_uk, q_scale_inv, out=None, ...)
+    mla_decode_workspace_size(params), mla_query_workspace_size(params)
+    mla_status_string(code), mla_version()
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libmla.so")
+
+MLA_DTYPE_BF16 = 1
+MLA_DTYPE_FP8_E4M3 = 2
+D_QK = 576
+D_V = 512
+PAGE_SIZE = 64
+FP8_ROW_BYTES = 640
+
+
+class MlaError(RuntimeError):
+    pass
+
+
+class DecodeParams(ctypes.Structure):
+    _fields_ = [
+        ("batch", ctypes.c_int32),
+        ("heads", ctypes.c_int32),
+        ("num_pages", ctypes.c_int32),
+        ("max_pages_per_seq", ctypes.c_int32),
+        ("topk", ctypes.c_int32),
+        ("q_dtype", ctypes.c_int32),
+        ("kv_dtype", ctypes.c_int32),
+        ("softmax_scale", ctypes.c_float),
+        ("q_descale", ctypes.c_float),
+    ]
+
+
+class QueryParams(ctypes.Structure):
+    _fields_ = [
+        ("batch", ctypes.c_int32),
+        ("heads", ctypes.c_int32),
+        ("qkv_stride", ctypes.c_int32),
+        ("eps", ctypes.c_float),
+    ]
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """Load libmla.so (built in-tree by mqa_latent_kv_amd.build)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise MlaError(f"{LIB_PATH} is missing: build it with `python -m mqa_latent_kv_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        vp, i32, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t
+        L.mla_version.restype = i32
+        L.mla_version.argtypes = []
+        L.mla_status_string.restype = ctypes.c_char_p
+        L.mla_status_string.argtypes = [i32]
+        L.mla_decode_workspace_size.restype = i32
+        L.mla_decode_workspace_size.argtypes = [ctypes.POINTER(DecodeParams), ctypes.POINTER(sz)]
+        L.mla_decode.restype = i32
+        L.mla_decode.argtypes = [ctypes.POINTER(DecodeParams), vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+        L.mla_query_workspace_size.restype = i32
+        L.mla_query_workspace_size.argtypes = [ctypes.POINTER(QueryParams), ctypes.POINTER(sz)]
+        L.mla_query.restype = i32
+        L.mla_query.argtypes = [ctypes.POINTER(QueryParams), vp, vp, vp, vp, vp, vp, vp, sz, vp]
+        _lib = L
+    return _lib
+
+
+def mla_version() -> int:
+    return int(lib().mla_version())
+
+
+def mla_status_string(code: int) -> str:
+    return lib().mla_status_string(int(code)).decode()
+
+
+def _check(code: int, what: str) -> None:
+    if code != 0:
+        raise MlaError(f"{what} failed: {mla_status_string(code)} ({code})")
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream_handle(stream, device):
+    import torch
+
+    s = torch.cuda.current_stream(device) if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _expect(t, name, dtypes, shape=None):
+    import torch
+
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if t.dtype not in dtypes:
+        raise TypeError(f"{name} has dtype {t.dtype}, expected one of {dtypes}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+
+
+def decode_params(*, batch, heads, num_pages, max_pages_per_seq, topk=0, q_fp8=False, kv_fp8=False,
+                  softmax_scale=192.0**-0.5, q_descale=1.0) -> DecodeParams:
+    return DecodeParams(
+        batch, heads, num_pages, max_pages_per_seq, topk,
+        MLA_DTYPE_FP8_E4M3 if q_fp8 else MLA_DTYPE_BF16,
+        MLA_DTYPE_FP8_E4M3 if kv_fp8 else MLA_DTYPE_BF16,
+        float(softmax_scale), float(q_descale),
+    )
+
+
+def mla_decode_workspace_size(params: DecodeParams) -> int:
+    n = ctypes.c_size_t(0)
+    _check(lib().mla_decode_workspace_size(ctypes.byref(params), ctypes.byref(n)), "mla_decode_workspace_size")
+    return int(n.value)
+
+
+def mla_decode(q, kv_cache, block_table, seqlens, topk_idx=None, kv_scales=None, out=None, lse=None, *,
+               softmax_scale=192.0**-0.5, q_descale=1.0, workspace=None, stream=None):
+    """Absorbed MLA decode (see include/mla.h).
+
+    q: [B, H, 576] torch.bfloat16, or uint8 / float8_e4m3fn codes.
+    kv_cache: bf16 [P, 64, 576], or uint8 [P, 64, 640] FP8 rows (then kv_scales
+    float32 [P, 64, 4]).  block_table int32 [B, max_pages], seqlens int32 [B],
+    topk_idx int32 [B, topk] or None.  Returns (out bf16 [B, H, 512], lse fp32 [B, H]).
+    """
+    import torch
+
+    if q.dim() == 4:
+        q = q.reshape(q.shape[0], q.shape[2], q.shape[3]) if q.shape[1] == 1 else q
+    _expect(q, "q", (torch.bfloat16, torch.uint8, torch.float8_e4m3fn))
+    B, H, dq = q.shape
+    if dq != D_QK:
+        raise ValueError("q must have 576 columns")
+    q_fp8 = q.dtype != torch.bfloat16
+    kv_fp8 = kv_cache.dtype in (torch.uint8, torch.float8_e4m3fn)
+    if kv_fp8:
+        _expect(kv_cache, "kv_cache", (torch.uint8, torch.float8_e4m3fn))
+        if tuple(kv_cache.shape[1:]) != (PAGE_SIZE, FP8_ROW_BYTES):
+            raise ValueError("FP8 kv_cache must be [P, 64, 640]")
+        _expect(kv_scales, "kv_scales", (torch.float32,), (kv_cache.shape[0], PAGE_SIZE, 4))
+    else:
+        _expect(kv_cache, "kv_cache", (torch.bfloat16,))
+        if tuple(kv_cache.shape[1:]) != (PAGE_SIZE, D_QK):
+            raise ValueError("bf16 kv_cache must be [P, 64, 576]")
+        if kv_scales is not None:
+            raise ValueError("kv_scales is only for an FP8 cache")
+    P = kv_cache.shape[0]
+    _expect(block_table, "block_table", (torch.int32,))
+    if block_table.dim() != 2 or block_table.shape[0] != B:
+        raise ValueError("block_table must be [B, max_pages]")
+    _expect(seqlens, "seqlens", (torch.int32,), (B,))
+    topk = 0
+    if topk_idx is not None:
+        topk_idx = topk_idx.reshape(B, -1)
+        _expect(topk_idx, "topk_idx", (torch.int32,))
+        topk = topk_idx.shape[1]
+    dev = q.device
+    if out is None:
+        out = torch.empty((B, H, D_V), dtype=torch.bfloat16, device=dev)
+    if lse is None:
+        lse = torch.empty((B, H), dtype=torch.float32, device=dev)
+    _expect(out, "out", (torch.bfloat16,), (B, H, D_V))
+    _expect(lse, "lse", (torch.float32,), (B, H))
+    params = decode_params(batch=B, heads=H, num_pages=P, max_pages_per_seq=block_table.shape[1], topk=topk,
+                           q_fp8=q_fp8, kv_fp8=kv_fp8, softmax_scale=softmax_scale, q_descale=q_descale)
+    need = mla_decode_workspace_size(params)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    _expect(workspace, "workspace", (torch.uint8,))
+    code = lib().mla_decode(
+        ctypes.byref(params), _ptr(q), _ptr(kv_cache), _ptr(block_table), _ptr(seqlens), _ptr(topk_idx),
+        _ptr(kv_scales), _ptr(out), _ptr(lse), _ptr(workspace), ctypes.c_size_t(workspace.numel()),
+        _stream_handle(stream, dev),
+    )
+    _check(code, "mla_decode")
+    return out, lse
+
+
+def mla_query_workspace_size(params: QueryParams) -> int:
+    n = ctypes.c_size_t(0)
+    _check(lib().mla_query_workspace_size(ctypes.byref(params), ctypes.byref(n)), "mla_query_workspace_size")
+    return int(n.value)
+
+
+def mla_query(qkv, w_qa, w_qb, w_uk, q_scale_inv, out=None, *, eps=1e-6, workspace=None, stream=None):
+    """MLA query front end (see include/mla.h).  qkv bf16 [B, >=1536];
+    w_qa bf16 [1536]; w_qb bf16 [H*192, 1536]; w_uk bf16 [H, 128, 512];
+    q_scale_inv float32 [1] on the device.  Returns uint8 e4m3 codes [B, H, 576]."""
+    import torch
+
+    _expect(qkv, "qkv", (torch.bfloat16,))
+    B, width = qkv.shape
+    _expect(w_uk, "w_uk", (torch.bfloat16,))
+    H = w_uk.shape[0]
+    _expect(w_uk, "w_uk", (torch.bfloat16,), (H, 128, D_V))
+    _expect(w_qa, "w_qa", (torch.bfloat16,), (1536,))
+    _expect(w_qb, "w_qb", (torch.bfloat16,), (H * 192, 1536))
+    _expect(q_scale_inv, "q_scale_inv", (torch.float32,))
+    dev = qkv.device
+    if out is None:
+        out = torch.empty((B, H, D_QK), dtype=torch.uint8, device=dev)
+    _expect(out, "out", (torch.uint8, torch.float8_e4m3fn), (B, H, D_QK))
+    params = QueryParams(B, H, width, float(eps))
+    need = mla_query_workspace_size(params)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    code = lib().mla_query(
+        ctypes.byref(params), _ptr(qkv), _ptr(w_qa), _ptr(w_qb), _ptr(w_uk), _ptr(q_scale_inv), _ptr(out),
+        _ptr(workspace), ctypes.c_size_t(workspace.numel()), _stream_handle(stream, dev),
+    )
+    _check(code, "mla_query")
+    return out
+
+
+def to_device(inp: dict, device="cuda"):
+    """Move a seeded decode input (numpy raw bits, see synth) to device tensors."""
+    import numpy as np
+    import torch
+
+    def u16_to_bf16(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(device)
+
+    res = {}
+    if inp["q_format"] == "bf16":
+        res["q"] = u16_to_bf16(inp["q"])
+    else:
+        res["q"] = torch.from_numpy(np.ascontiguousarray(inp["q"])).to(device)
+    if inp["kv_format"] == "bf16":
+        res["kv"] = u16_to_bf16(inp["kv"])
+        res["kv_scales"] = None
+    else:
+        res["kv"] = torch.from_numpy(np.ascontiguousarray(inp["kv"])).to(device)
+        res["kv_scales"] = torch.from_numpy(np.ascontiguousarray(inp["kv_scales"])).to(device)
+    res["block_table"] = torch.from_numpy(np.ascontiguousarray(inp["block_table"])).to(device)
+    res["seqlens"] = torch.from_numpy(np.ascontiguousarray(inp["seqlens"])).to(device)
+    res["topk_idx"] = None if inp.get("topk_idx") is None else torch.from_numpy(np.ascontiguousarray(inp["topk_idx"])).to(device)
+    return res

@@ -1,0 +1,155 @@
+"""The C-ABI library without a GPU: it loads, exports every declared entry
+point, and rejects bad arguments on the host before any HIP call."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import mqa_latent_kv_amd as mla
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "mla.h")
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(mla.LIB_PATH):
+        from mqa_latent_kv_amd import build
+
+        build.build()
+    return mla.lib()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(mla_\w+)\s*\(", text, flags=re.M)))
+
+
+def test_header_declares_the_entry_points():
+    fns = declared_functions()
+    for name in ("mla_decode", "mla_decode_workspace_size", "mla_query", "mla_query_workspace_size",
+                 "mla_status_string", "mla_version"):
+        assert name in fns
+
+
+def test_library_exports_every_declared_symbol(L):
+    for name in declared_functions():
+        assert hasattr(L, name), name
+
+
+def test_version_and_status_strings(L):
+    assert mla.mla_version() >= 100
+    assert mla.mla_status_string(0) == "ok"
+    for code in (-1, -2, -3, -4, -5):
+        assert mla.mla_status_string(code) not in ("ok", "unknown status")
+    assert mla.mla_status_string(-99) == "unknown status"
+
+
+def test_struct_layouts_match_header():
+    # all members are 4-byte: the C structs have no padding
+    assert ctypes.sizeof(mla.DecodeParams) == 9 * 4
+    assert ctypes.sizeof(mla.QueryParams) == 4 * 4
+
+
+def _params(**kw):
+    base = dict(batch=2, heads=128, num_pages=8, max_pages_per_seq=4)
+    base.update(kw)
+    return mla.decode_params(**base)
+
+
+FAKE = ctypes.c_void_p(0x1000)  # never dereferenced: validation fails first
+
+
+def _decode(L, p, **ptrs):
+    args = dict(q=FAKE, kv=FAKE, bt=FAKE, sl=FAKE, topk=None, scales=None, out=FAKE, lse=FAKE, ws=FAKE)
+    args.update(ptrs)
+    return L.mla_decode(ctypes.byref(p) if p is not None else None, args["q"], args["kv"], args["bt"], args["sl"],
+                        args["topk"], args["scales"], args["out"], args["lse"], args["ws"], ctypes.c_size_t(1 << 30),
+                        None)
+
+
+@pytest.mark.parametrize(
+    "kw,code",
+    [
+        (dict(batch=0), -1),
+        (dict(heads=0), -1),
+        (dict(num_pages=0), -1),
+        (dict(max_pages_per_seq=0), -1),
+        (dict(topk=-1), -1),
+        (dict(softmax_scale=0.0), -1),
+        (dict(softmax_scale=float("nan")), -1),
+        (dict(heads=7), -2),
+        (dict(heads=256), -2),
+        (dict(batch=100000), -2),
+        (dict(max_pages_per_seq=1 << 26), -2),
+    ],
+)
+def test_decode_param_validation(L, kw, code):
+    assert _decode(L, _params(**kw)) == code
+    n = ctypes.c_size_t(0)
+    assert L.mla_decode_workspace_size(ctypes.byref(_params(**kw)), ctypes.byref(n)) == code
+
+
+def test_decode_rejects_bad_dtype_enum(L):
+    p = _params()
+    p.q_dtype = 7
+    assert _decode(L, p) == -1
+    p = _params()
+    p.kv_dtype = 0
+    assert _decode(L, p) == -1
+
+
+def test_decode_null_pointers(L):
+    assert _decode(L, None) == -1
+    for name in ("q", "kv", "bt", "sl", "out", "lse"):
+        assert _decode(L, _params(), **{name: None}) == -1, name
+    assert _decode(L, _params(), ws=None) == -3
+
+
+def test_decode_optional_arguments_must_match_params(L):
+    # a top-k list without topk > 0, and topk > 0 without a list
+    assert _decode(L, _params(), topk=FAKE) == -1
+    assert _decode(L, _params(topk=64)) in (-1, -2)
+    # FP8 cache needs scales; a bf16 cache must not get them
+    assert _decode(L, _params(kv_fp8=True)) in (-1, -2)
+    assert _decode(L, _params(), scales=FAKE) == -1
+
+
+def test_query_validation(L):
+    def q(p, **ptrs):
+        a = dict(qkv=FAKE, wqa=FAKE, wqb=FAKE, wuk=FAKE, qsi=FAKE, out=FAKE, ws=FAKE)
+        a.update(ptrs)
+        return L.mla_query(ctypes.byref(p) if p is not None else None, a["qkv"], a["wqa"], a["wqb"], a["wuk"],
+                           a["qsi"], a["out"], a["ws"], ctypes.c_size_t(1 << 30), None)
+
+    good = mla.QueryParams(64, 8, 1536, 1e-6)
+    assert q(None) == -1
+    assert q(mla.QueryParams(0, 8, 1536, 1e-6)) == -1
+    assert q(mla.QueryParams(64, 8, 1000, 1e-6)) == -1
+    assert q(mla.QueryParams(64, 8, 1536, -1.0)) == -1
+    assert q(mla.QueryParams(64, 500, 1536, 1e-6)) == -2
+    for name in ("qkv", "wqa", "wqb", "wuk", "qsi", "out"):
+        assert q(good, **{name: None}) == -1, name
+    assert q(good, ws=None) == -3
+    n = ctypes.c_size_t(0)
+    assert L.mla_query_workspace_size(ctypes.byref(good), ctypes.byref(n)) == 0 and n.value > 0
+
+
+def test_workspace_size_needs_a_device(L):
+    import torch
+
+    n = ctypes.c_size_t(0)
+    code = L.mla_decode_workspace_size(ctypes.byref(_params()), ctypes.byref(n))
+    if torch.cuda.is_available():
+        assert code == 0 and n.value > 0
+    else:
+        assert code == -5
+
+
+def test_binding_raises_without_library(monkeypatch):
+    monkeypatch.setattr(mla, "_lib", None)
+    monkeypatch.setattr(mla, "LIB_PATH", "/nonexistent/libmla.so")
+    with pytest.raises(mla.MlaError):
+        mla.lib()

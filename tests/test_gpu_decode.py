@@ -1,0 +1,154 @@
+"""GPU parity of mla_decode against the float64 oracle (run on an MI355X).
+
+Every case draws seeded inputs from mqa_latent_kv_amd.synth, runs the HIP path
+through the C ABI and compares element by element with oracle.mla_decode on
+the same bits.  Bars: bf16 O max-abs <= 2e-2 and fp32 LSE max-abs <= 1e-3;
+gathers (block-table lookups, sequence boundaries) are checked bit-exactly
+through one-hot queries.
+"""
+import numpy as np
+import pytest
+import torch
+
+import mqa_latent_kv_amd as mla
+from mqa_latent_kv_amd import synth
+from oracle import codecs
+from oracle import mla_oracle as mo
+
+pytestmark = pytest.mark.gpu
+
+O_TOL = 2e-2
+LSE_TOL = 1e-3
+
+
+def _say(msg):
+    print(msg, flush=True)
+
+
+def run_gpu(inp, **kw):
+    d = mla.to_device(inp)
+    out, lse = mla.mla_decode(d["q"], d["kv"], d["block_table"], d["seqlens"], d["topk_idx"], d["kv_scales"],
+                              q_descale=inp["q_descale"], **kw)
+    torch.cuda.synchronize()
+    return out, lse
+
+
+def run_oracle(inp, batches=None):
+    return mo.mla_decode(inp["q"], inp["kv"], inp["block_table"], inp["seqlens"], inp["topk_idx"], inp["kv_scales"],
+                         q_format=inp["q_format"], kv_format=inp["kv_format"], q_descale=inp["q_descale"],
+                         batches=batches)
+
+
+def compare(inp, out, lse, batches=None):
+    ref = run_oracle(inp, batches)
+    o = out.float().cpu().numpy().astype(np.float64)
+    l = lse.cpu().numpy().astype(np.float64)
+    sel = slice(None) if batches is None else list(batches)
+    ro, rl = ref["O"][sel], ref["LSE"][sel]
+    go, gl = o[sel], l[sel]
+    assert np.all(np.isfinite(go)), "non-finite output"
+    err_o = np.max(np.abs(go - ro))
+    empty = np.isneginf(rl)
+    assert np.array_equal(np.isneginf(gl), empty), "LSE -inf pattern differs"
+    err_l = np.max(np.abs(gl[~empty] - rl[~empty])) if np.any(~empty) else 0.0
+    _say(f"   max|dO|={err_o:.3e}  max|dLSE|={err_l:.3e}")
+    assert err_o <= O_TOL
+    assert err_l <= LSE_TOL
+    return ref
+
+
+CASES = {
+    # name: make_decode_inputs kwargs
+    "tiny_dense_b1_h16_s128": dict(seed=1, batch=1, heads=16, seqlens=[128], num_pages=2, pages_per_seq=2),
+    "h128_ragged": dict(seed=11, batch=3, heads=128, seqlens=[1, 200, 2100], pages_per_seq=34, num_pages=120),
+    "h64_ragged": dict(seed=12, batch=5, heads=64, seqlen_range=(1, 700)),
+    "h32_ragged": dict(seed=13, batch=4, heads=32, seqlen_range=(30, 900)),
+    "h16_ragged": dict(seed=14, batch=4, heads=16, seqlen_range=(30, 900)),
+    "h8_ragged": dict(seed=15, batch=6, heads=8, seqlen_range=(1, 1300)),
+    "h8_fp8q": dict(seed=16, batch=6, heads=8, seqlen_range=(100, 1300), q_format="fp8", q_descale=8.0),
+    "h128_fp8q": dict(seed=17, batch=2, heads=128, seqlen_range=(500, 1500), q_format="fp8", q_descale=8.0),
+    "many_short_seqs": dict(seed=18, batch=300, heads=64, seqlen_range=(1, 100)),
+    "one_long_seq": dict(seed=19, batch=1, heads=128, seqlens=[20000]),
+    "with_empty_seqs": dict(seed=20, batch=5, heads=64, seqlens=[0, 77, 0, 300, 0], pages_per_seq=5),
+    "exact_pages": dict(seed=21, batch=3, heads=128, seqlens=[64, 128, 4096]),
+}
+
+
+@pytest.mark.parametrize("name", list(CASES))
+def test_decode_matches_oracle(name):
+    kw = dict(CASES[name])
+    inp = synth.make_decode_inputs(kw.pop("seed"), **kw)
+    _say(f"[decode parity] case={name} B={inp['batch']} H={inp['heads']} seqlens[:8]={inp['seqlens'][:8].tolist()}")
+    out, lse = run_gpu(inp)
+    compare(inp, out, lse)
+
+
+def test_outputs_fully_written_and_deterministic():
+    inp = synth.make_decode_inputs(31, batch=7, heads=128, seqlen_range=(1, 3000))
+    d = mla.to_device(inp)
+    _say("[decode] NaN-poisoned outputs, two runs")
+    outs = []
+    for _ in range(2):
+        out = torch.full((7, 128, 512), float("nan"), dtype=torch.bfloat16, device="cuda")
+        lse = torch.full((7, 128), float("nan"), dtype=torch.float32, device="cuda")
+        mla.mla_decode(d["q"], d["kv"], d["block_table"], d["seqlens"], out=out, lse=lse)
+        torch.cuda.synchronize()
+        assert not torch.isnan(out.float()).any() and not torch.isnan(lse).any()
+        outs.append((out.clone(), lse.clone()))
+    assert torch.equal(outs[0][0].view(torch.int16), outs[1][0].view(torch.int16))
+    assert torch.equal(outs[0][1].view(torch.int32), outs[1][1].view(torch.int32))
+
+
+@pytest.mark.parametrize("heads", [128, 64, 8])
+def test_one_hot_gather_is_bit_exact(heads):
+    """q[b,h] = 5 * k[row(j*)] makes position j* win by a logit gap of ~170, so
+    p(j*) = 1 exactly in fp32 and O must equal V[row(j*)] bit for bit: a wrong
+    block-table lookup, tail mask or slot offset shows up as a wrong row."""
+    B = 4
+    inp = synth.make_decode_inputs(41 + heads, batch=B, heads=heads, seqlen_range=(300, 2500))
+    rng = np.random.default_rng(heads)
+    kvf = inp["kv"].reshape(-1, 576)
+    jstar = np.zeros((B, heads), dtype=np.int64)
+    q = np.empty_like(inp["q"])
+    for b in range(B):
+        n = int(inp["seqlens"][b])
+        js = rng.integers(0, n, heads)
+        js[0] = n - 1  # the last valid token (tail of the last page)
+        js[1 % heads] = 0
+        jstar[b] = js
+        rows = mo.physical_rows(inp["block_table"][b], js)
+        q[b] = codecs.f64_to_bf16_bits(5.0 * codecs.bf16_bits_to_f64(kvf[rows]))
+    inp["q"] = q
+    _say(f"[decode one-hot] H={heads}")
+    out, lse = run_gpu(inp)
+    got = out.cpu().view(torch.int16).numpy().view(np.uint16)
+    for b in range(B):
+        rows = mo.physical_rows(inp["block_table"][b], jstar[b])
+        np.testing.assert_array_equal(got[b], kvf[rows][:, :512])
+
+
+def test_page_permutation_invariance_bitwise():
+    inp = synth.make_decode_inputs(51, batch=3, heads=64, seqlen_range=(100, 1500), num_pages=80, pages_per_seq=24)
+    _say("[decode] page permutation")
+    out1, lse1 = run_gpu(inp)
+    P = inp["kv"].shape[0]
+    perm = np.random.default_rng(2).permutation(P)
+    inv = np.argsort(perm)
+    inp2 = dict(inp)
+    inp2["kv"] = np.ascontiguousarray(inp["kv"][perm])
+    inp2["block_table"] = inv[inp["block_table"]].astype(np.int32)
+    out2, lse2 = run_gpu(inp2)
+    assert torch.equal(out1.view(torch.int16), out2.view(torch.int16))
+    assert torch.equal(lse1.view(torch.int32), lse2.view(torch.int32))
+
+
+@pytest.mark.parametrize("name", ["paged_bf16_4096", "paged_bf16", "query_decode"])
+def test_full_size_workloads_sampled(name):
+    """The full-size decode workloads, in the launch configuration the
+    benchmark times, checked on a sample of sequences the oracle computes."""
+    inp = synth.workload_inputs(name)
+    _say(f"[decode full-size] {name} B={inp['batch']} H={inp['heads']}")
+    out, lse = run_gpu(inp)
+    B = inp["batch"]
+    sample = sorted(set([0, B - 1] + list(np.random.default_rng(7).choice(B, 4, replace=False))))
+    compare(inp, out, lse, batches=sample)
