@@ -10,7 +10,8 @@ Entry points (same names as the C ABI):
     mla_decode(q, kv_cache, block_table, seqlens, topk_idx=None, kv_scales=None,
                out=None, lse=None, ...)
     mla_query(qkv, w_qa, w_qb, w_uk, q_scale_inv, out=None, ...)
-    mla_decode_workspace_size(params), mla_query_workspace_size(params)
+    mla_decode_workspace_size(params), mla_decode_workspace_init(params, ws),
+    mla_query_workspace_size(params)
     mla_status_string(code), mla_version()
 """
 from __future__ import annotations
@@ -73,6 +74,8 @@ def lib() -> ctypes.CDLL:
         L.mla_status_string.argtypes = [i32]
         L.mla_decode_workspace_size.restype = i32
         L.mla_decode_workspace_size.argtypes = [ctypes.POINTER(DecodeParams), ctypes.POINTER(sz)]
+        L.mla_decode_workspace_init.restype = i32
+        L.mla_decode_workspace_init.argtypes = [ctypes.POINTER(DecodeParams), vp, sz, vp]
         L.mla_decode.restype = i32
         L.mla_decode.argtypes = [ctypes.POINTER(DecodeParams), vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
         L.mla_query_workspace_size.restype = i32
@@ -138,6 +141,20 @@ def mla_decode_workspace_size(params: DecodeParams) -> int:
     return int(n.value)
 
 
+def mla_decode_workspace_init(params: DecodeParams, workspace, stream=None) -> None:
+    _check(lib().mla_decode_workspace_init(ctypes.byref(params), _ptr(workspace), ctypes.c_size_t(workspace.numel()),
+                                           _stream_handle(stream, workspace.device)), "mla_decode_workspace_init")
+
+
+def decode_workspace(params: DecodeParams, device="cuda", stream=None):
+    """Allocate and prepare a decode workspace (reusable across calls that fit)."""
+    import torch
+
+    ws = torch.empty(max(mla_decode_workspace_size(params), 1), dtype=torch.uint8, device=device)
+    mla_decode_workspace_init(params, ws, stream)
+    return ws
+
+
 def mla_decode(q, kv_cache, block_table, seqlens, topk_idx=None, kv_scales=None, out=None, lse=None, *,
                softmax_scale=192.0**-0.5, q_descale=1.0, workspace=None, stream=None):
     """Absorbed MLA decode (see include/mla.h).
@@ -187,9 +204,8 @@ def mla_decode(q, kv_cache, block_table, seqlens, topk_idx=None, kv_scales=None,
     _expect(lse, "lse", (torch.float32,), (B, H))
     params = decode_params(batch=B, heads=H, num_pages=P, max_pages_per_seq=block_table.shape[1], topk=topk,
                            q_fp8=q_fp8, kv_fp8=kv_fp8, softmax_scale=softmax_scale, q_descale=q_descale)
-    need = mla_decode_workspace_size(params)
     if workspace is None:
-        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+        workspace = decode_workspace(params, dev, stream)
     _expect(workspace, "workspace", (torch.uint8,))
     code = lib().mla_decode(
         ctypes.byref(params), _ptr(q), _ptr(kv_cache), _ptr(block_table), _ptr(seqlens), _ptr(topk_idx),

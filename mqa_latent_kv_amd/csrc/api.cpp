@@ -81,6 +81,17 @@ int32_t mla_decode_workspace_size(const mla_decode_params* p, size_t* bytes) {
   return MLA_OK;
 }
 
+int32_t mla_decode_workspace_init(const mla_decode_params* p, void* workspace, size_t workspace_bytes,
+                                  void* stream) {
+  size_t need = 0;
+  int32_t st = mla_decode_workspace_size(p, &need);
+  if (st != MLA_OK) return st;
+  if (!workspace || workspace_bytes < need) return MLA_ERR_WORKSPACE;
+  if (mla::init_decode_workspace(workspace, p->batch, p->heads, (hipStream_t)stream) != hipSuccess)
+    return MLA_ERR_LAUNCH;
+  return MLA_OK;
+}
+
 int32_t mla_decode(const mla_decode_params* p, const void* q, const void* kv_cache,
                    const int32_t* block_table, const int32_t* seqlens, const int32_t* topk_idx,
                    const float* kv_scales, void* out, float* lse, void* workspace,

@@ -38,8 +38,9 @@
 //    ranges, one per workgroup (a static form of the persistent scheduler the
 //    STAGE_D2 note mentions under "Grid vs. Persistent Tile Scheduler").  A
 //    sequence covered by one range is finished in place; otherwise each piece
-//    writes a normalised fp32 partial and its base-2 LSE, merged by
-//    mla_combine_kernel.
+//    writes a normalised fp32 partial and its base-2 LSE and bumps a counter,
+//    and the last piece to arrive merges them (one launch, no waiting on other
+//    workgroups) and resets the counter for the next call.
 //  * Online softmax in base 2 with a lazy rescale: the running reference max
 //    moves only when a slot's max exceeds it by more than 8, so P <= 256 and
 //    the O rescale is rare.
@@ -83,7 +84,7 @@ struct DecodeArgs {
   float* lse;
   float* ws_o;    // [(ranges + B) slots][H][512] fp32 partials
   float* ws_lse;  // [(ranges + B)][H] base-2 LSE of partials
-  int2* ws_meta;  // [B] (first range, number of pieces)
+  int* ws_count;  // [B][slabs] arrival counters of split sequences; zero between calls
   int32_t batch, heads, num_pages, max_pages, topk;
   int32_t ranges;  // KV ranges (workgroups per head slab)
   int32_t slabs;   // head slabs per range
@@ -379,6 +380,31 @@ __device__ __forceinline__ void ring_step(int s, const Ring& ring, LDS_AS f32x4*
   compute_slot<NSPLIT>(ring.template at<J>(), xch, min(kTS, sg.tok1 - (sg.tok0 + s * kTS)), qf, t, st, a.scale_log2, lane, w);
 }
 
+// Merge the nsplit pieces of sequence b for the heads of one slab:
+// LSE = log2 sum_s 2^lse_s, O = sum_s 2^(lse_s - LSE) O_s.  Piece s of the
+// sequence sits in workspace slot first + s.
+template <int HPS>
+__device__ void merge_pieces(const DecodeArgs& a, int b, int slab, int first, int nsplit) {
+  for (int idx = threadIdx.x; idx < HPS * (kDV / 4); idx += kThreads) {
+    const int head = slab * HPS + idx / (kDV / 4), c4 = idx % (kDV / 4);
+    if (head >= a.heads) break;
+    float mx = -INFINITY;
+    for (int s = 0; s < nsplit; ++s) mx = fmaxf(mx, a.ws_lse[((size_t)first + s) * a.heads + head]);
+    f32x4 acc = {};
+    float wsum = 0.0f;
+    for (int s = 0; s < nsplit; ++s) {
+      const float l = a.ws_lse[((size_t)first + s) * a.heads + head];
+      const float wgt = (l == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(l - mx);
+      const f32x4 v = *(const f32x4*)(a.ws_o + (((size_t)first + s) * a.heads + head) * kDV + 4 * c4);
+      acc += wgt * v;
+      wsum += wgt;
+    }
+    acc *= wsum > 0.0f ? 1.0f / wsum : 0.0f;
+    *(bf16x4*)((__bf16*)a.out + ((size_t)b * a.heads + head) * kDV + 4 * c4) = __builtin_convertvector(acc, bf16x4);
+    if (c4 == 0) a.lse[(size_t)b * a.heads + head] = wsum > 0.0f ? (mx + __builtin_amdgcn_logf(wsum)) * kLn2 : -INFINITY;
+  }
+}
+
 // ---------------------------------------------------------------- the kernel
 
 template <int NSPLIT, bool Q_FP8>
@@ -388,6 +414,9 @@ __global__ void __launch_bounds__(kThreads, 1) mla_decode_bf16_kernel(DecodeArgs
   __shared__ __attribute__((aligned(1024))) char slot2[kSlotBytes];
   __shared__ __attribute__((aligned(1024))) char slot3[kSlotBytes];
   __shared__ __attribute__((aligned(16))) f32x4 xbuf[kWaves * 4 * 64];  // partial S^T exchange, 16 KB
+  // the epilogue's "last piece" flag reuses the exchange buffer: it is written
+  // after a barrier that all waves reach only once their last slot is done
+  volatile int& xlast = *(int*)xbuf;
   const Ring ring{(lds_char*)slot0, (lds_char*)slot1, (lds_char*)slot2, (lds_char*)slot3};
   LDS_AS f32x4* const xch = (LDS_AS f32x4*)xbuf;
 
@@ -402,6 +431,14 @@ __global__ void __launch_bounds__(kThreads, 1) mla_decode_bf16_kernel(DecodeArgs
   // workgroup -> (range, head slab); the slabs of a range sit 8 ids apart so
   // they land on the same XCD.
   const int g = blockIdx.x;
+  // sequences with nothing to attend: O = 0, LSE = -inf (spread over the grid)
+  for (int b = g; b < a.batch; b += gridDim.x) {
+    if (units_of(a, b) == 0) {
+      for (int i = tid; i < a.heads * (kDV / 4); i += kThreads)
+        *(bf16x4*)((__bf16*)a.out + ((size_t)b * a.heads) * kDV + 4 * i) = bf16x4{};
+      for (int i = tid; i < a.heads; i += kThreads) a.lse[(size_t)b * a.heads + i] = -INFINITY;
+    }
+  }
   const int r = (g / (8 * a.slabs)) * 8 + (g % 8);
   const int slab = (g / 8) % a.slabs;
   if (r >= a.ranges) return;
@@ -436,7 +473,6 @@ __global__ void __launch_bounds__(kThreads, 1) mla_decode_bf16_kernel(DecodeArgs
       sg.bt_row = a.block_table + (size_t)b * a.max_pages;
       const int first_r = p / pl.C, last_r = (p + n - 1) / pl.C;
       const int nsplit = last_r - first_r + 1;
-      if (gs == p && slab == 0 && tid == 0) a.ws_meta[b] = make_int2(first_r, nsplit);
 
       // query fragments (B operand of S^T = K.Q^T): head `head`, columns
       // 16*ks + 8*(lane/32) .. +7 for this wave's k-steps
@@ -517,6 +553,19 @@ __global__ void __launch_bounds__(kThreads, 1) mla_decode_bf16_kernel(DecodeArgs
           if (part == 0 && lane < 32) a.ws_lse[pslot * a.heads + head] = lse2;
         }
       }
+      if (nsplit > 1) {
+        // publish this piece; the last of the nsplit pieces merges them
+        __threadfence();
+        __syncthreads();
+        int* cnt = a.ws_count + (size_t)b * a.slabs + slab;
+        if (tid == 0) xlast = atomicAdd(cnt, 1) == nsplit - 1;
+        __syncthreads();
+        if (xlast) {
+          __threadfence();
+          merge_pieces<HG * 32>(a, b, slab, b + first_r, nsplit);
+          if (tid == 0) *cnt = 0;
+        }
+      }
     }
     p += n;
     ++b;
@@ -524,44 +573,14 @@ __global__ void __launch_bounds__(kThreads, 1) mla_decode_bf16_kernel(DecodeArgs
   }
 }
 
-// Merge the pieces of sequences that were split across ranges:
-// LSE = log2 sum_s 2^lse_s, O = sum_s 2^(lse_s - LSE) O_s.  Sequences with no
-// units get O = 0, LSE = -inf; sequences finished in place are skipped.
-__global__ void __launch_bounds__(256) mla_combine_kernel(DecodeArgs a) {
-  const int b = blockIdx.y;
-  const int idx = blockIdx.x * 256 + threadIdx.x;  // (head, 4-column group)
-  const int head = idx / (kDV / 4), c4 = idx % (kDV / 4);
-  if (head >= a.heads) return;
-  __bf16* orow = (__bf16*)a.out + ((size_t)b * a.heads + head) * kDV + 4 * c4;
-  const size_t lidx = (size_t)b * a.heads + head;
-  if (units_of(a, b) == 0) {
-    *(bf16x4*)orow = bf16x4{};
-    if (c4 == 0) a.lse[lidx] = -INFINITY;
-    return;
-  }
-  const int2 meta = a.ws_meta[b];
-  const int nsplit = meta.y;
-  if (nsplit <= 1) return;
-  const size_t first = (size_t)(b + meta.x);
-  float mx = -INFINITY;
-  for (int s = 0; s < nsplit; ++s) mx = fmaxf(mx, a.ws_lse[(first + s) * a.heads + head]);
-  f32x4 acc = {};
-  float wsum = 0.0f;
-  for (int s = 0; s < nsplit; ++s) {
-    const float l = a.ws_lse[(first + s) * a.heads + head];
-    const float wgt = (l == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(l - mx);
-    const f32x4 v = *(const f32x4*)(a.ws_o + ((first + s) * a.heads + head) * kDV + 4 * c4);
-    acc += wgt * v;
-    wsum += wgt;
-  }
-  const float inv = wsum > 0.0f ? 1.0f / wsum : 0.0f;
-  acc *= inv;
-  *(bf16x4*)orow = __builtin_convertvector(acc, bf16x4);
-  if (c4 == 0) a.lse[lidx] = wsum > 0.0f ? (mx + __builtin_amdgcn_logf(wsum)) * kLn2 : -INFINITY;
-}
-
 int nsplit_for_heads(int heads) { return heads > 32 ? 2 : 4; }
 int slabs_for_heads(int heads) { return heads > 64 ? 2 : 1; }
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+__global__ void mla_zero_kernel(int* p, int n) {
+  for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < n; i += gridDim.x * blockDim.x) p[i] = 0;
+}
 
 }  // namespace
 
@@ -573,15 +592,20 @@ int32_t decode_ranges(int32_t cus, int32_t batch, int32_t max_pages, int32_t top
   return (int32_t)r;
 }
 
+// Workspace: [B][slabs] int counters | [(ranges + B)][H] fp32 LSE | [(ranges + B)][H][512] fp32 O.
 size_t decode_workspace_bytes(int32_t ranges, int32_t batch, int32_t heads) {
-  auto align = [](size_t x) { return (x + 255) & ~(size_t)255; };
   const size_t slots = (size_t)ranges + (size_t)batch;
-  return align(sizeof(int2) * (size_t)batch) + align(sizeof(float) * slots * heads) +
-         align(sizeof(float) * slots * heads * kDV);
+  return align256(sizeof(int) * (size_t)batch * slabs_for_heads(heads)) + align256(sizeof(float) * slots * heads) +
+         align256(sizeof(float) * slots * heads * kDV);
+}
+
+hipError_t init_decode_workspace(void* workspace, int32_t batch, int32_t heads, hipStream_t stream) {
+  const int n = batch * slabs_for_heads(heads);
+  hipLaunchKernelGGL(mla_zero_kernel, dim3((n + 255) / 256), dim3(256), 0, stream, (int*)workspace, n);
+  return hipGetLastError();
 }
 
 hipError_t launch_decode(const DecodeLaunch& d, hipStream_t stream) {
-  auto align = [](size_t x) { return (x + 255) & ~(size_t)255; };
   DecodeArgs a;
   a.q = d.q;
   a.kv = (const char*)d.kv;
@@ -591,12 +615,13 @@ hipError_t launch_decode(const DecodeLaunch& d, hipStream_t stream) {
   a.kv_scales = d.kv_scales;
   a.out = d.out;
   a.lse = d.lse;
+  a.slabs = slabs_for_heads(d.heads);
   char* ws = (char*)d.workspace;
   const size_t slots = (size_t)d.ranges + (size_t)d.batch;
-  a.ws_meta = (int2*)ws;
-  ws += align(sizeof(int2) * (size_t)d.batch);
+  a.ws_count = (int*)ws;
+  ws += align256(sizeof(int) * (size_t)d.batch * a.slabs);
   a.ws_lse = (float*)ws;
-  ws += align(sizeof(float) * slots * d.heads);
+  ws += align256(sizeof(float) * slots * d.heads);
   a.ws_o = (float*)ws;
   a.batch = d.batch;
   a.heads = d.heads;
@@ -604,12 +629,11 @@ hipError_t launch_decode(const DecodeLaunch& d, hipStream_t stream) {
   a.max_pages = d.max_pages;
   a.topk = d.topk;
   a.ranges = d.ranges;
-  a.slabs = slabs_for_heads(d.heads);
   a.scale_log2 = d.softmax_scale * kLog2e;
   a.q_descale = d.q_descale;
 
   if (d.kv_fp8 || d.topk > 0) return hipErrorNotSupported;
-  // ranges of each slab are spread 8 per XCD group: round the grid up to that
+  // the slabs of a range are 8 workgroup ids apart: round the grid up to that
   const int groups = (d.ranges + 7) / 8;
   const dim3 grid(groups * 8 * a.slabs), block(kThreads);
   if (nsplit_for_heads(d.heads) == 2) {
@@ -619,10 +643,6 @@ hipError_t launch_decode(const DecodeLaunch& d, hipStream_t stream) {
     if (d.q_fp8) hipLaunchKernelGGL((mla_decode_bf16_kernel<4, true>), grid, block, 0, stream, a);
     else hipLaunchKernelGGL((mla_decode_bf16_kernel<4, false>), grid, block, 0, stream, a);
   }
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  const dim3 cgrid((d.heads * (kDV / 4) + 255) / 256, d.batch);
-  hipLaunchKernelGGL(mla_combine_kernel, cgrid, dim3(256), 0, stream, a);
   return hipGetLastError();
 }
 
