@@ -31,9 +31,9 @@
 //    direct global->LDS DMA (global_load_lds_dwordx4), three slots in flight
 //    while one is consumed.  Rows are XOR-swizzled in 16-byte chunks so the
 //    ds_read_b128 K reads and the ds_read_b64_tr_b16 V^T reads are free of
-//    bank conflicts.  Each ring slot is its own LDS object so the compiler can
-//    tell the DMA target from the slot being read and keeps the loads in
-//    flight.
+//    bank conflicts.  The DMA is issued from inline assembly and accounted
+//    for by explicit vmcnt waits, so the compiler never serialises LDS reads
+//    behind copies still in flight.
 //  * Split-KV: pages of all sequences are laid end to end and cut into equal
 //    ranges, one per workgroup (a static form of the persistent scheduler the
 //    STAGE_D2 note mentions under "Grid vs. Persistent Tile Scheduler").  A
@@ -41,9 +41,13 @@
 //    writes a normalised fp32 partial and its base-2 LSE and bumps a counter,
 //    and the last piece to arrive merges them (one launch, no waiting on other
 //    workgroups) and resets the counter for the next call.
-//  * Online softmax in base 2 with a lazy rescale: the running reference max
-//    moves only when a slot's max exceeds it by more than 8, so P <= 256 and
-//    the O rescale is rare.
+//  * Softmax in base 2 against a fixed reference per head: the first slot's
+//    max.  Later slots may exceed it by up to 16 (P <= 2^16, exact in fp32 and
+//    as relative bf16); if any head's scores rise further, the workgroup
+//    redoes the segment once with the true maxima (then P <= 1).  Realistic
+//    score distributions never trigger the redo.  With no rescale inside the
+//    KV loop the fp32 accumulators are only ever written by MFMAs and stay in
+//    fixed AGPRs.
 #include "mla_internal.h"
 
 namespace mla {
@@ -71,7 +75,7 @@ constexpr int kDmaPerWave = kSlotBytes / 1024 / kWaves;  // 9 x 1 KB per wave pe
 constexpr int kKSteps = kD / 16;                         // 36 MFMA k-steps for QK^T
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
-constexpr float kTau = 8.0f;
+constexpr float kTau = 16.0f;  // largest rise of a head's max over its first-slot reference (base 2)
 
 struct DecodeArgs {
   const void* q;
@@ -229,35 +233,85 @@ __device__ __forceinline__ void make_tables(LaneTables<NSPLIT>& t, int lane, int
   }
 }
 
+// One direct global->LDS copy of 16 bytes per lane: lane i's bytes land at
+// LDS address lds_base + 16*i.  Written as inline assembly so that the
+// compiler's wait-count insertion does not see it: it cannot tell which ring
+// slot a DMA targets and would otherwise wait for every copy in flight before
+// each LDS read.  The ring accounts for these copies itself (explicit vmcnt
+// before each barrier).  The kernel keeps no other value in m0.
+__device__ __forceinline__ void dma16(const char* sbase, uint32_t voff, uint32_t lds_base) {
+  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(sbase), "s"(lds_base)
+               : "memory");
+}
+
+__device__ __forceinline__ const char* uniform_ptr(const char* p) {
+  const uint64_t v = (uint64_t)p;
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+  return (const char*)(((uint64_t)hi << 32) | lo);
+}
+
+__device__ __forceinline__ uint32_t lds_addr(const lds_char* p) { return (uint32_t)(uintptr_t)p; }
+
 // Issue this wave's share of one slot's DMA: 32 rows starting at `src`; rows
 // at and beyond `nvalid` re-read row nvalid-1 (a valid row), so the slot never
 // holds foreign or unwritten data.
 template <int NSPLIT>
 __device__ __forceinline__ void dma_slot(lds_char* dst, const char* src, int nvalid, const LaneTables<NSPLIT>& t,
                                          int w) {
+  const char* base = uniform_ptr(src);
+  const uint32_t lds0 = __builtin_amdgcn_readfirstlane(lds_addr(dst) + w * kDmaPerWave * 1024);
 #pragma unroll
   for (int k = 0; k < kDmaPerWave; ++k) {
-    uint32_t m = t.dma[k] >> 16, off = t.dma[k] & 0xffff;
-    uint32_t mm = m < (uint32_t)nvalid ? m : (uint32_t)(nvalid - 1);
-    __builtin_amdgcn_global_load_lds(src + mm * kRowBytes + off,
-                                     (LDS_AS void*)(dst + (w * kDmaPerWave + k) * 1024), 16, 0, 0);
+    const uint32_t m = t.dma[k] >> 16, off = t.dma[k] & 0xffff;
+    const uint32_t mm = m < (uint32_t)nvalid ? m : (uint32_t)(nvalid - 1);
+    dma16(base, mm * kRowBytes + off, lds0 + k * 1024);
   }
+}
+
+// Block-table entries of the current segment, 64 at a time, one per lane:
+// a page lookup is a readlane, not a memory access inside the ring.
+struct PageCache {
+  int v;     // lane i: block_table[row][base + i]
+  int base;  // first segment page held
+};
+
+__device__ __forceinline__ void page_cache_load(PageCache& pc, const int32_t* bt_seg, int base, int npages, int lane) {
+  pc.base = base;
+  pc.v = (base + lane < npages) ? bt_seg[base + lane] : 0;
+  // complete the load here, on this (rare) path, so that no wait for it is
+  // left pending where the paths merge in the ring
+  wait_vm_lgkm0<0>();
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+__device__ __forceinline__ int page_of(PageCache& pc, const int32_t* bt_seg, int k, int npages, int lane,
+                                       int num_pages) {
+  if (k >= pc.base + 64) page_cache_load(pc, bt_seg, k, npages, lane);  // segments longer than 64 pages
+  return clamp_page(__builtin_amdgcn_readlane(pc.v, k - pc.base), num_pages);
 }
 
 // ---------------------------------------------------------------- compute on one slot
 
 template <int NSPLIT>
-struct WaveState {
-  static constexpr int NCB = 16 / NSPLIT;
-  f32x16 o[NCB];
-  float m_ref;
-  float l_sum;
+struct Acc {
+  f32x16 o[16 / NSPLIT];  // O^T accumulators (AGPRs), relative to the reference max
+};
+
+// Softmax state of one lane's head.  The reference max is fixed after the
+// segment's first slot (or, in a redo, to the true max); the accumulators
+// are only ever zeroed or fed by MFMAs inside the KV loop, which keeps them
+// in fixed AGPRs.
+struct SoftmaxState {
+  float m_ref;   // base-2 reference: p = 2^(x - m_ref)
+  float m_seen;  // largest score seen (base 2)
+  float l_sum;   // this lane's share of sum p
 };
 
 template <int NSPLIT>
 __device__ __forceinline__ void compute_slot(const lds_char* buf, LDS_AS f32x4* xch, int nvalid,
                                              const bf16x8 (&qf)[kKSteps / NSPLIT], const LaneTables<NSPLIT>& t,
-                                             WaveState<NSPLIT>& st, float scale_log2, int lane, int w) {
+                                             SoftmaxState& st, Acc<NSPLIT>& acc, float scale_log2, int lane, int w) {
   constexpr int KS = kKSteps / NSPLIT;
   constexpr int NCB = 16 / NSPLIT;
   // partial S^T[token][head] over this wave's share of the 576 columns
@@ -267,6 +321,14 @@ __device__ __forceinline__ void compute_slot(const lds_char* buf, LDS_AS f32x4* 
     bf16x8 kf = *(const LDS_AS bf16x8*)(buf + t.kaddr[i & 3] + 128 * (i >> 2));
     s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[i], s, 0, 0, 0);
   }
+  // keep three K fragments in flight ahead of the MFMA that consumes them
+  __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);
+#pragma unroll
+  for (int i = 0; i < KS - 3; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+  }
+  __builtin_amdgcn_sched_group_barrier(0x008, 3, 0);
   // exchange partials inside the head group; every wave sums them in the
   // same order so the group holds bit-identical scores
   const int grp = (w / NSPLIT) * NSPLIT;
@@ -299,16 +361,11 @@ __device__ __forceinline__ void compute_slot(const lds_char* buf, LDS_AS f32x4* 
     mx = fmaxf(mx, x[r]);
   }
   mx = fmaxf(mx, __shfl_xor(mx, 32));  // lanes l and l^32 hold the two token halves of a head
-  const bool need = mx > st.m_ref + kTau;
-  if (__any(need)) {
-    const float m_new = need ? mx : st.m_ref;
-    const float alpha = (m_new == st.m_ref) ? 1.0f : __builtin_amdgcn_exp2f(st.m_ref - m_new);
-    st.l_sum *= alpha;
-#pragma unroll
-    for (int c = 0; c < NCB; ++c) st.o[c] *= alpha;
-    st.m_ref = m_new;
-  }
-  const float mref = st.m_ref == -INFINITY ? 0.0f : st.m_ref;
+  // the first slot fixes the reference; later slots may exceed it by up to
+  // kTau without loss (p <= 2^kTau), beyond that the segment is redone
+  if (st.m_ref == -INFINITY) st.m_ref = mx;
+  st.m_seen = fmaxf(st.m_seen, mx);
+  const float mref = st.m_ref;
   f32x8 p0, p1;
   float lsum = 0.0f;
 #pragma unroll
@@ -334,50 +391,51 @@ __device__ __forceinline__ void compute_slot(const lds_char* buf, LDS_AS f32x4* 
     bf16x4 c1 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((LDS_AS bf16x4*)(buf + va + step + 24 * kRowBytes));
     const bf16x8 v0 = __builtin_shufflevector(a0, a1, 0, 1, 2, 3, 4, 5, 6, 7);
     const bf16x8 v1 = __builtin_shufflevector(c0, c1, 0, 1, 2, 3, 4, 5, 6, 7);
-    st.o[cbi] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(v0, pb0, st.o[cbi], 0, 0, 0);
-    st.o[cbi] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(v1, pb1, st.o[cbi], 0, 0, 0);
+    acc.o[cbi] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(v0, pb0, acc.o[cbi], 0, 0, 0);
+    acc.o[cbi] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(v1, pb1, acc.o[cbi], 0, 0, 0);
   }
+  // the four V^T reads of block cbi+1 are in flight while block cbi's two
+  // MFMAs run
+  __builtin_amdgcn_sched_group_barrier(0x100, 4, 1);
+#pragma unroll
+  for (int cbi = 0; cbi < NCB - 1; ++cbi) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
+    __builtin_amdgcn_sched_group_barrier(0x100, 2, 1);
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
+    __builtin_amdgcn_sched_group_barrier(0x100, 2, 1);
+  }
+  __builtin_amdgcn_sched_group_barrier(0x008, 2, 1);
 }
 
-// The four ring slots, each its own LDS object; indexed at compile time only.
-struct Ring {
-  lds_char* s0;
-  lds_char* s1;
-  lds_char* s2;
-  lds_char* s3;
-  template <int J>
-  __device__ __forceinline__ lds_char* at() const {
-    if constexpr ((J & 3) == 0) return s0;
-    else if constexpr ((J & 3) == 1) return s1;
-    else if constexpr ((J & 3) == 2) return s2;
-    else return s3;
-  }
-};
-
 struct SegCtx {
-  const int32_t* bt_row;
-  int tok0, tok1, nslots;
+  const int32_t* bt_seg;  // block-table entries of the segment's pages
+  int tok0, tok1, nslots, npages;
 };
 
-// One step of the ring: wait for slot s (ring index J), free the slot
-// consumed in the previous step and refill it with slot s+3, compute slot s.
-template <int NSPLIT, int J>
-__device__ __forceinline__ void ring_step(int s, const Ring& ring, LDS_AS f32x4* xch, const DecodeArgs& a,
-                                          const SegCtx& sg, const bf16x8 (&qf)[kKSteps / NSPLIT],
-                                          const LaneTables<NSPLIT>& t, WaveState<NSPLIT>& st, int lane, int w) {
-  if (s >= sg.nslots) return;
+// One step of the ring: wait for slot s, free the ring slot consumed in the
+// previous step and refill it with slot s+3, compute slot s.  A plain loop
+// with a run-time slot offset: the DMA is invisible to the compiler, so the
+// slots need no compile-time identity, and a loop body without early exits
+// lets the accumulators stay in fixed AGPRs.
+template <int NSPLIT>
+__device__ __forceinline__ void ring_step(int s, lds_char* ring, LDS_AS f32x4* xch, const DecodeArgs& a,
+                                          const SegCtx& sg, PageCache& pc, const bf16x8 (&qf)[kKSteps / NSPLIT],
+                                          const LaneTables<NSPLIT>& t, SoftmaxState& st, Acc<NSPLIT>& acc,
+                                          int lane, int w) {
   const int later = min(sg.nslots - 1 - s, 2);
   if (later == 2) wait_vm_lgkm0<2 * kDmaPerWave>();
   else if (later == 1) wait_vm_lgkm0<kDmaPerWave>();
   else wait_vm_lgkm0<0>();
   barrier();
   if (s + 3 < sg.nslots) {
-    const int tk = sg.tok0 + (s + 3) * kTS;
-    const int page = clamp_page(sg.bt_row[tk / kPage], a.num_pages);
-    const char* src = a.kv + ((size_t)page * kPage + (tk % kPage)) * kRowBytes;
-    dma_slot<NSPLIT>(ring.template at<J + 3>(), src, min(kTS, sg.tok1 - tk), t, w);
+    const int ns = s + 3;
+    const int tk = sg.tok0 + ns * kTS;
+    const int page = page_of(pc, sg.bt_seg, ns >> 1, sg.npages, lane, a.num_pages);
+    const char* src = a.kv + ((size_t)page * kPage + (ns & 1) * kTS) * kRowBytes;
+    dma_slot<NSPLIT>(ring + (ns & 3) * kSlotBytes, src, min(kTS, sg.tok1 - tk), t, w);
   }
-  compute_slot<NSPLIT>(ring.template at<J>(), xch, min(kTS, sg.tok1 - (sg.tok0 + s * kTS)), qf, t, st, a.scale_log2, lane, w);
+  compute_slot<NSPLIT>(ring + (s & 3) * kSlotBytes, xch, min(kTS, sg.tok1 - (sg.tok0 + s * kTS)), qf, t, st, acc,
+                       a.scale_log2, lane, w);
 }
 
 // Merge the nsplit pieces of sequence b for the heads of one slab:
@@ -409,15 +467,12 @@ __device__ void merge_pieces(const DecodeArgs& a, int b, int slab, int first, in
 
 template <int NSPLIT, bool Q_FP8>
 __global__ void __launch_bounds__(kThreads, 1) mla_decode_bf16_kernel(DecodeArgs a) {
-  __shared__ __attribute__((aligned(1024))) char slot0[kSlotBytes];
-  __shared__ __attribute__((aligned(1024))) char slot1[kSlotBytes];
-  __shared__ __attribute__((aligned(1024))) char slot2[kSlotBytes];
-  __shared__ __attribute__((aligned(1024))) char slot3[kSlotBytes];
+  __shared__ __attribute__((aligned(1024))) char ring_mem[4 * kSlotBytes];  // KV ring, 4 x 36 KB
   __shared__ __attribute__((aligned(16))) f32x4 xbuf[kWaves * 4 * 64];  // partial S^T exchange, 16 KB
   // the epilogue's "last piece" flag reuses the exchange buffer: it is written
   // after a barrier that all waves reach only once their last slot is done
   volatile int& xlast = *(int*)xbuf;
-  const Ring ring{(lds_char*)slot0, (lds_char*)slot1, (lds_char*)slot2, (lds_char*)slot3};
+  lds_char* const ring = (lds_char*)ring_mem;
   LDS_AS f32x4* const xch = (LDS_AS f32x4*)xbuf;
 
   constexpr int KS = kKSteps / NSPLIT;
@@ -444,7 +499,7 @@ __global__ void __launch_bounds__(kThreads, 1) mla_decode_bf16_kernel(DecodeArgs
   if (r >= a.ranges) return;
 
   Plan pl;
-  if (!make_plan(a, r, (int*)slot0, pl)) return;
+  if (!make_plan(a, r, (int*)ring_mem, pl)) return;
 
   const int head = slab * (HG * 32) + hg * 32 + (lane & 31);
   const bool head_ok = head < a.heads;
@@ -470,7 +525,8 @@ __global__ void __launch_bounds__(kThreads, 1) mla_decode_bf16_kernel(DecodeArgs
       sg.tok0 = (gs - p) * kPage;
       sg.tok1 = min((ge - p) * kPage, seqlen);
       sg.nslots = (sg.tok1 - sg.tok0 + kTS - 1) / kTS;
-      sg.bt_row = a.block_table + (size_t)b * a.max_pages;
+      sg.npages = (sg.nslots + 1) / 2;
+      sg.bt_seg = a.block_table + (size_t)b * a.max_pages + (gs - p);
       const int first_r = p / pl.C, last_r = (p + n - 1) / pl.C;
       const int nsplit = last_r - first_r + 1;
 
@@ -493,64 +549,74 @@ __global__ void __launch_bounds__(kThreads, 1) mla_decode_bf16_kernel(DecodeArgs
         }
       }
 
-      // prologue DMA: slots 0..2 (issued after the query loads so the
-      // in-order vmcnt accounting of the ring counts DMA only)
-#pragma unroll
-      for (int s = 0; s < 3; ++s) {
-        if (s < sg.nslots) {
-          const int tk = sg.tok0 + s * kTS;
-          const int page = clamp_page(sg.bt_row[tk / kPage], a.num_pages);
-          const char* src = a.kv + ((size_t)page * kPage + (tk % kPage)) * kRowBytes;
-          lds_char* dst = s == 0 ? ring.at<0>() : (s == 1 ? ring.at<1>() : ring.at<2>());
-          dma_slot<NSPLIT>(dst, src, min(kTS, sg.tok1 - tk), tab, w);
-        }
-      }
+      PageCache pc;
+      page_cache_load(pc, sg.bt_seg, 0, sg.npages, lane);
+      // query and block-table loads complete before any DMA is issued, so the
+      // ring's vmcnt accounting counts DMA only
+      wait_vm_lgkm0<0>();
 
-      WaveState<NSPLIT> st;
-#pragma unroll
-      for (int c = 0; c < NCB; ++c) st.o[c] = f32x16{};
+      SoftmaxState st;
       st.m_ref = -INFINITY;
-      st.l_sum = 0.0f;
-
-      for (int s0 = 0; s0 < sg.nslots; s0 += 4) {
-        ring_step<NSPLIT, 0>(s0 + 0, ring, xch, a, sg, qf, tab, st, lane, w);
-        ring_step<NSPLIT, 1>(s0 + 1, ring, xch, a, sg, qf, tab, st, lane, w);
-        ring_step<NSPLIT, 2>(s0 + 2, ring, xch, a, sg, qf, tab, st, lane, w);
-        ring_step<NSPLIT, 3>(s0 + 3, ring, xch, a, sg, qf, tab, st, lane, w);
+      Acc<NSPLIT> acc;
+      // At most two passes: the second only if some head's scores rose more
+      // than kTau above the reference its first slot set (p would exceed
+      // 2^kTau); it then runs with the true maxima, so all p <= 1.
+      for (int pass = 0; pass < 2; ++pass) {
+#pragma unroll
+        for (int c = 0; c < NCB; ++c) acc.o[c] = f32x16{};
+        st.l_sum = 0.0f;
+        st.m_seen = -INFINITY;
+        // prologue DMA: slots 0..2
+#pragma unroll
+        for (int s = 0; s < 3; ++s) {
+          if (s < sg.nslots) {
+            const int tk = sg.tok0 + s * kTS;
+            const int page = page_of(pc, sg.bt_seg, s >> 1, sg.npages, lane, a.num_pages);
+            const char* src = a.kv + ((size_t)page * kPage + (s & 1) * kTS) * kRowBytes;
+            dma_slot<NSPLIT>(ring + s * kSlotBytes, src, min(kTS, sg.tok1 - tk), tab, w);
+          }
+        }
+        for (int s = 0; s < sg.nslots; ++s) ring_step<NSPLIT>(s, ring, xch, a, sg, pc, qf, tab, st, acc, lane, w);
+        // workgroup vote on a redo (every wave is past its last exchange read)
+        wait_vm_lgkm0<0>();
+        barrier();
+        const int my_vote = __any(st.m_seen > st.m_ref + kTau) ? 1 : 0;  // all lanes vote
+        if (lane == 0) ((volatile int*)xbuf)[w] = my_vote;
+        wait_vm_lgkm0<0>();
+        barrier();
+        const int vote = ((volatile int*)xbuf)[0] | ((volatile int*)xbuf)[1] | ((volatile int*)xbuf)[2] |
+                         ((volatile int*)xbuf)[3];
+        wait_vm_lgkm0<0>();
+        barrier();  // votes read before the buffer is reused
+        if (!__builtin_amdgcn_readfirstlane(vote)) break;
+        st.m_ref = st.m_seen;
+        if (sg.npages > 64) page_cache_load(pc, sg.bt_seg, 0, sg.npages, lane);
       }
 
-      // ---- epilogue: normalise and store this wave's columns
+      // ---- epilogue: normalise and store this wave's columns (final output,
+      // or this piece's partial in its workspace slot)
       const float l_tot = st.l_sum + __shfl_xor(st.l_sum, 32);
       const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
       const float lse2 = l_tot > 0.0f ? st.m_ref + __builtin_amdgcn_logf(l_tot) : -INFINITY;
       if (head_ok) {
-        if (nsplit == 1) {
-          __bf16* orow = (__bf16*)a.out + ((size_t)b * a.heads + head) * kDV;
+        const size_t pslot = (size_t)(b + r);
+        __bf16* orow = (__bf16*)a.out + ((size_t)b * a.heads + head) * kDV;
+        float* prow = a.ws_o + (pslot * a.heads + head) * kDV;
 #pragma unroll
-          for (int cbi = 0; cbi < NCB; ++cbi) {
-            const int cb = part * NCB + cbi;
+        for (int cbi = 0; cbi < NCB; ++cbi) {
+          const int cb = part * NCB + cbi;
 #pragma unroll
-            for (int rg = 0; rg < 4; ++rg) {
-              f32x4 v = {st.o[cbi][4 * rg], st.o[cbi][4 * rg + 1], st.o[cbi][4 * rg + 2], st.o[cbi][4 * rg + 3]};
-              v *= inv;
-              *(bf16x4*)(orow + 32 * cb + 8 * rg + 4 * (lane >> 5)) = __builtin_convertvector(v, bf16x4);
-            }
+          for (int rg = 0; rg < 4; ++rg) {
+            const int col = 32 * cb + 8 * rg + 4 * (lane >> 5);
+            f32x4 v = {acc.o[cbi][4 * rg], acc.o[cbi][4 * rg + 1], acc.o[cbi][4 * rg + 2], acc.o[cbi][4 * rg + 3]};
+            v *= inv;
+            if (nsplit == 1) *(bf16x4*)(orow + col) = __builtin_convertvector(v, bf16x4);
+            else *(f32x4*)(prow + col) = v;
           }
-          if (part == 0 && lane < 32) a.lse[(size_t)b * a.heads + head] = lse2 * kLn2;
-        } else {
-          const size_t pslot = (size_t)(b + r);
-          float* orow = a.ws_o + (pslot * a.heads + head) * kDV;
-#pragma unroll
-          for (int cbi = 0; cbi < NCB; ++cbi) {
-            const int cb = part * NCB + cbi;
-#pragma unroll
-            for (int rg = 0; rg < 4; ++rg) {
-              f32x4 v = {st.o[cbi][4 * rg], st.o[cbi][4 * rg + 1], st.o[cbi][4 * rg + 2], st.o[cbi][4 * rg + 3]};
-              v *= inv;
-              *(f32x4*)(orow + 32 * cb + 8 * rg + 4 * (lane >> 5)) = v;
-            }
-          }
-          if (part == 0 && lane < 32) a.ws_lse[pslot * a.heads + head] = lse2;
+        }
+        if (part == 0 && lane < 32) {
+          if (nsplit == 1) a.lse[(size_t)b * a.heads + head] = lse2 * kLn2;
+          else a.ws_lse[pslot * a.heads + head] = lse2;
         }
       }
       if (nsplit > 1) {

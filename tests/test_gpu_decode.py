@@ -39,7 +39,23 @@ def run_oracle(inp, batches=None):
                          batches=batches)
 
 
-def compare(inp, out, lse, batches=None):
+def abs_weighted_v(inp):
+    """sum_t p_t |V_t| per (b, h, c): the size of the terms that O sums, which
+    bounds the effect of rounding P to bf16 (dense inputs only)."""
+    out = np.zeros((inp["batch"], inp["heads"], 512))
+    for b in range(inp["batch"]):
+        pos = mo.valid_positions(inp["seqlens"][b])
+        kf = mo.dequant_rows(inp["kv"], mo.physical_rows(inp["block_table"][b], pos), inp["kv_format"], inp["kv_scales"])
+        _, _, p = mo.attend(mo.query_rows(inp["q"], b, inp["q_format"], inp["q_descale"]), kf, 192.0**-0.5)
+        out[b] = p @ np.abs(kf[:, :512])
+    return out
+
+
+def compare(inp, out, lse, batches=None, rtol=0.0, scale=None):
+    """Element-wise bars: |dO| <= O_TOL + rtol*scale and |dLSE| <= LSE_TOL.
+    rtol is 0 for the N(0,1) workloads; inputs with large |V| add the bf16
+    rounding of P and of O (unit roundoff 2^-8 each, bf16 keeping 8
+    significant bits) times scale = sum p|V| >= |O|."""
     ref = run_oracle(inp, batches)
     o = out.float().cpu().numpy().astype(np.float64)
     l = lse.cpu().numpy().astype(np.float64)
@@ -51,9 +67,16 @@ def compare(inp, out, lse, batches=None):
     empty = np.isneginf(rl)
     assert np.array_equal(np.isneginf(gl), empty), "LSE -inf pattern differs"
     err_l = np.max(np.abs(gl[~empty] - rl[~empty])) if np.any(~empty) else 0.0
-    _say(f"   max|dO|={err_o:.3e}  max|dLSE|={err_l:.3e}")
-    assert err_o <= O_TOL
+    exc = np.abs(go - ro) - rtol * (scale[sel] if scale is not None else 0.0)
+    excess = np.max(exc)
+    if excess > O_TOL:
+        i = np.unravel_index(np.argmax(exc), exc.shape)
+        _say(f"   worst at {i}: gpu={go[i]:.6g} ref={ro[i]:.6g} scale={None if scale is None else scale[sel][i]:.6g} "
+             f"lse gpu={gl[i[:2]]:.6g} ref={rl[i[:2]]:.6g}")
+    _say(f"   max|dO|={err_o:.3e} (max|O|={np.max(np.abs(ro)):.3e}, max excess over rtol term={excess:.3e})"
+         f"  max|dLSE|={err_l:.3e}")
     assert err_l <= LSE_TOL
+    assert excess <= O_TOL
     return ref
 
 
@@ -81,6 +104,24 @@ def test_decode_matches_oracle(name):
     _say(f"[decode parity] case={name} B={inp['batch']} H={inp['heads']} seqlens[:8]={inp['seqlens'][:8].tolist()}")
     out, lse = run_gpu(inp)
     compare(inp, out, lse)
+
+
+@pytest.mark.parametrize("heads", [128, 64, 8])
+def test_running_max_jumps(heads):
+    """KV rows scaled up along each sequence make every slot's max exceed the
+    running reference by far more than the lazy-rescale threshold, so the
+    set-aside-and-restart path runs on most slots (and across split pieces)."""
+    inp = synth.make_decode_inputs(61 + heads, batch=3, heads=heads, seqlens=[700, 1500, 129], pages_per_seq=24)
+    kv = codecs.bf16_bits_to_f64(inp["kv"]).reshape(-1, 576)
+    bt = inp["block_table"]
+    for b in range(3):
+        n = int(inp["seqlens"][b])
+        rows = mo.physical_rows(bt[b], np.arange(n))
+        kv[rows] *= (1.0 + np.arange(n) / 16.0)[:, None]
+    inp["kv"] = codecs.f64_to_bf16_bits(kv).reshape(inp["kv"].shape)
+    _say(f"[decode growing scores] H={heads}")
+    out, lse = run_gpu(inp)
+    compare(inp, out, lse, rtol=2.0**-7, scale=abs_weighted_v(inp))
 
 
 def test_outputs_fully_written_and_deterministic():
