@@ -90,18 +90,17 @@ typedef struct mla_decode_params {
 
 /*
  * Bytes of scratch that mla_decode needs for `p` on the current HIP device
- * (split-KV partial results and per-sequence arrival counters).  Writes
- * *bytes; queries the device's compute unit count, so it returns
- * MLA_ERR_DEVICE without a GPU.
+ * (split-KV partial results and a record per sequence of where its pieces
+ * are).  Writes *bytes; queries the device's compute unit count, so it
+ * returns MLA_ERR_DEVICE without a GPU.
  */
 int32_t mla_decode_workspace_size(const mla_decode_params* p, size_t* bytes);
 
 /*
- * Prepare a decode workspace for `p`: zeroes its counter area (asynchronously
- * on `stream`, with a kernel, no memset node).  Call once after allocating a
- * workspace, or after using its memory for anything else; every mla_decode
- * call leaves the counters zero again, so a workspace is reusable across calls
- * of any shape that fits in it.
+ * Clear the per-sequence records of a decode workspace for `p`
+ * (asynchronously on `stream`, with a kernel, no memset node).  mla_decode
+ * rewrites every record it reads back in the same call, so this is optional;
+ * it keeps a freshly allocated workspace free of stale bytes.
  */
 int32_t mla_decode_workspace_init(const mla_decode_params* p, void* workspace, size_t workspace_bytes,
                                   void* stream);
@@ -130,10 +129,12 @@ int32_t mla_decode_workspace_init(const mla_decode_params* p, void* workspace, s
  *              for d < 512.
  *  out         [B, H, 512] bf16 (round to nearest even).
  *  lse         [B, H] fp32, natural-log log-sum-exp of the scaled scores.
- *  workspace   device scratch of at least mla_decode_workspace_size bytes,
- *              prepared by mla_decode_workspace_init; apart from the counter
- *              area (left zero) its contents are clobbered.  Calls that share
- *              a workspace must be ordered (one stream).
+ *  workspace   device scratch of at least mla_decode_workspace_size bytes;
+ *              its contents are clobbered.  Calls that share a workspace must
+ *              be ordered (one stream).
+ *
+ * Runs two kernels on `stream`: the split-KV decode and, for sequences it
+ * split over several KV ranges, the merge of their pieces.
  */
 int32_t mla_decode(const mla_decode_params* p, const void* q, const void* kv_cache,
                    const int32_t* block_table, const int32_t* seqlens,

@@ -2,51 +2,54 @@
 //
 // What is computed (one query token per sequence): for every head h of
 // sequence b, scores against the shared 576-wide latent rows (512 nope + 64
-// rope; the rope block is one more slice of the same QK^T, as in FlashMLA
-// issue "dual gemm"), a scaled softmax per head row, and O = P.V with V the
-// 512 nope columns.  Output O in bf16 and the natural-log LSE per head.
+// rope; the rope block is one more slice of the same QK^T), a scaled softmax
+// per head row, and O = P.V with V the 512 nope columns.  Output O in bf16 and
+// the natural-log LSE per head.
 //
-// Design (MI355X-first; the pages' Blackwell designs are prior art only):
-//  * Head-packed tile ("STAGE_D2" note, "Strategy A: Head-Packed M
+// Design (MI355X-first; the pages' Hopper/Blackwell kernels are prior art):
+//  * Head-packed tile (the STAGE_D2 note, "Strategy A: Head-Packed M
 //    Dimension"): a workgroup reads each KV row once for a slab of up to 64
 //    heads of its sequence.  The MFMA is v_mfma_f32_32x32x16_bf16 with the 32
 //    KV tokens of an LDS slot as M and 32 heads as N:
-//        S^T[t][h] = sum_d K[t][d] Q[h][d]          (K = 576 = 36 steps)
+//        S^T[t][h] = sum_d K[t][d] Q[h][d]          (36 steps of 16)
 //        O^T[c][h] += sum_t V^T[c][t] P^T[t][h]     (2 steps per 32 columns)
-//    With tokens on M the S^T accumulator is already the P^T operand of the
-//    PV product (the k <-> token permutation is absorbed in the V^T read), and
-//    all O^T registers of a lane belong to one head, so the online-softmax
-//    rescale is a per-lane scalar multiply.
-//  * Split reduction (the CDNA counterpart of the issue's "dual gemm", which
-//    halves the QK^T K dimension across warpgroups and sums the halves): the
-//    NSPLIT waves of a 32-head group each own 576/NSPLIT of the QK^T
-//    reduction and 512/NSPLIT output columns.  Partial S^T go through LDS and
-//    every wave of the group adds them in the same order, so all of them hold
-//    bit-identical scores and softmax state.  A wave keeps 144/NSPLIT query
-//    VGPRs and 256/NSPLIT accumulator AGPRs, which leaves the compiler room.
-//  * Slabs: H = 128 runs as two 64-head workgroups per KV range; the pair is
-//    placed on one XCD (workgroups are dealt round-robin to the 8 XCDs) so the
-//    second reader of every KV line finds it in that XCD's L2.
+//    With tokens on M the S^T accumulator is the P^T operand of the PV
+//    product as it stands (the k <-> token permutation is absorbed by the V^T
+//    read), and every O^T register of a lane belongs to one head.
+//  * Split reduction (the CDNA counterpart of the FlashMLA "dual gemm" idea of
+//    halving the QK^T reduction across warpgroups): the NSPLIT waves of a
+//    32-head group each own 576/NSPLIT of the QK^T reduction and 512/NSPLIT
+//    output columns.  Partial S^T go through LDS; every wave of the group
+//    adds them in one fixed order (for two parts, own + partner, which is the
+//    same sum in either wave), so all of them hold bit-identical scores and
+//    softmax state.  A wave keeps 144/NSPLIT query VGPRs and 256/NSPLIT
+//    accumulator AGPRs.
+//  * Slabs: H = 128 runs as two 64-head workgroups per KV range, on one XCD,
+//    so the second reader of every KV line finds it in that XCD's L2.
 //  * KV streaming: 32-token slots of 36 KB in a 4-deep LDS ring filled by
-//    direct global->LDS DMA (global_load_lds_dwordx4), three slots in flight
-//    while one is consumed.  Rows are XOR-swizzled in 16-byte chunks so the
-//    ds_read_b128 K reads and the ds_read_b64_tr_b16 V^T reads are free of
-//    bank conflicts.  The DMA is issued from inline assembly and accounted
-//    for by explicit vmcnt waits, so the compiler never serialises LDS reads
-//    behind copies still in flight.
+//    direct global->LDS DMA (global_load_lds_dwordx4), laid out in 128-byte
+//    column groups and XOR-swizzled so that the ds_read_b128 K reads and the
+//    ds_read_b64_tr_b16 V^T reads are free of bank conflicts.  The DMA is
+//    issued from inline assembly and accounted for by explicit vmcnt waits,
+//    so the compiler never serialises LDS reads behind copies in flight.
+//  * Software pipeline: while slot s is exchanged, softmaxed and multiplied
+//    into O, the partial QK^T of slot s+1 runs on the matrix core; two more
+//    slots are in flight from HBM.  Two workgroup barriers per slot: one
+//    publishes the partial scores (and the landed slot), one frees the ring
+//    slot and the exchange buffer.
 //  * Split-KV: pages of all sequences are laid end to end and cut into equal
-//    ranges, one per workgroup (a static form of the persistent scheduler the
-//    STAGE_D2 note mentions under "Grid vs. Persistent Tile Scheduler").  A
-//    sequence covered by one range is finished in place; otherwise each piece
-//    writes a normalised fp32 partial and its base-2 LSE and bumps a counter,
-//    and the last piece to arrive merges them (one launch, no waiting on other
-//    workgroups) and resets the counter for the next call.
+//    ranges, one per workgroup and slab (a static form of the persistent
+//    scheduler the STAGE_D2 note describes under "Grid vs. Persistent Tile
+//    Scheduler").  A sequence inside one range is finished in place;
+//    otherwise each piece writes a normalised fp32 partial and its base-2 LSE
+//    and bumps a counter, and the last piece to arrive merges them (one
+//    launch, no wait on other workgroups) and resets the counter.
 //  * Softmax in base 2 against a fixed reference per head: the first slot's
 //    max.  Later slots may exceed it by up to 16 (P <= 2^16, exact in fp32 and
 //    as relative bf16); if any head's scores rise further, the workgroup
 //    redoes the segment once with the true maxima (then P <= 1).  Realistic
 //    score distributions never trigger the redo.  With no rescale inside the
-//    KV loop the fp32 accumulators are only ever written by MFMAs and stay in
+//    KV loop the fp32 accumulators are only written by MFMAs and stay in
 //    fixed AGPRs.
 #include "mla_internal.h"
 
@@ -69,10 +72,12 @@ constexpr int kPage = 64;
 constexpr int kRowBytes = kD * 2;            // bf16 latent row
 constexpr int kTS = 32;                      // tokens per LDS slot
 constexpr int kSlotBytes = kTS * kRowBytes;  // 36864
+constexpr int kRing = 4;                     // LDS slots
 constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
 constexpr int kDmaPerWave = kSlotBytes / 1024 / kWaves;  // 9 x 1 KB per wave per slot
 constexpr int kKSteps = kD / 16;                         // 36 MFMA k-steps for QK^T
+constexpr int kCB = kDV / 32;                            // 16 O^T column blocks
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kTau = 16.0f;  // largest rise of a head's max over its first-slot reference (base 2)
@@ -88,22 +93,32 @@ struct DecodeArgs {
   float* lse;
   float* ws_o;    // [(ranges + B) slots][H][512] fp32 partials
   float* ws_lse;  // [(ranges + B)][H] base-2 LSE of partials
-  int* ws_count;  // [B][slabs] arrival counters of split sequences; zero between calls
+  int2* ws_seq;   // [B] {workspace slot of piece 0, pieces}; pieces 0: nothing to attend
   int32_t batch, heads, num_pages, max_pages, topk;
-  int32_t ranges;  // KV ranges (workgroups per head slab)
-  int32_t slabs;   // head slabs per range
+  int32_t ranges;    // KV ranges (workgroups per head slab)
+  int32_t slabs;     // head slabs per range
+  int32_t per_xcd;   // ranges per XCD in the block -> (range, slab) mapping
   float scale_log2;  // softmax_scale * log2(e)
   float q_descale;
 };
 
 // ---------------------------------------------------------------- helpers
 
-// Chunk swizzle inside each 128-byte group of a 1152-byte row: the low three
-// bits of the 16-byte chunk index are XORed with f(row).  f maps 8 consecutive
-// rows to 8 distinct values (b128 reads of 8 rows) and 4 consecutive rows
-// starting at a multiple of 4 to 4 values whose XOR with an even chunk pair
-// covers all 8 positions (tr_b16 reads of 4 rows x 32 bytes).
-__device__ __forceinline__ int row_swz(int m) { return ((m & 3) << 1) | ((m >> 2) & 1); }
+// Slot layout in LDS: the 1152-byte rows are cut into 9 column groups of 128
+// bytes (64 latent columns); group c of all 32 rows is stored contiguously,
+// row m at c*4096 + m*128.  Inside a row's 128 bytes the 16-byte chunk x sits
+// at position x ^ row_swz(m).  The 64 banks of 4 bytes see a 256-byte period,
+// so a 16-byte chunk's bank group is 8*(m&1) + position; row_swz makes
+//  * the b128 K reads (16 lanes = 16 consecutive rows, one chunk) hit 16
+//    distinct bank groups: for even rows, and for odd rows, bits 1..3 of m
+//    map one-to-one onto the three bits of the swizzle;
+//  * the tr_b16 V^T reads (32 lanes = rows r, r+1, r+2, r+3 with r % 4 == 0,
+//    chunks 0..3 of a half group) conflict-free: rows r and r+2 share a
+//    parity and differ in swizzle bit 2, so their four chunks fall in
+//    opposite halves of the eight positions.
+__device__ __forceinline__ int row_swz(int m) { return (((m >> 1) & 1) << 2) | (((m >> 3) & 1) << 1) | ((m >> 2) & 1); }
+
+constexpr int kGroupBytes = kTS * 128;  // one 128-byte column group of all 32 rows
 
 template <int N>
 __device__ __forceinline__ void wait_vm_lgkm0() {
@@ -198,38 +213,54 @@ __device__ bool make_plan(const DecodeArgs& a, int r, int* scratch, Plan& pl) {
 
 // ---------------------------------------------------------------- per-lane address tables
 
-template <int NSPLIT>
+// DMA kk (0..8) of wave w fills rows 8w .. 8w+7 of column group kk: lane i
+// writes LDS bytes 16i.. of that 1 KB block, which is row 8w + i/8, position
+// i%8, and so fetches source chunk (i%8) ^ row_swz(row) of column group kk.
+// The per-lane source offset is the same for all nine copies of a wave;
+// the column group is the instruction's immediate offset.  Rows at and
+// beyond row_cap read row row_cap.
+__device__ __forceinline__ uint32_t dma_lane_off(int lane, int w, int row_cap) {
+  int row = 8 * w + (lane >> 3);
+  const int src_chunk = (lane & 7) ^ row_swz(row);
+  row = row < row_cap ? row : row_cap;
+  return (uint32_t)(row * kRowBytes + 16 * src_chunk);
+}
+
 struct LaneTables {
-  uint32_t dma[kDmaPerWave];  // (row << 16) | (source byte offset of the chunk within its row)
-  uint32_t kaddr[4];          // QK A operand for this wave's k-step i: kaddr[i & 3] + 128*(i >> 2)
-  uint32_t vaddr;             // PV A operand (tr reads) for ks = tt = 0 and an even column block
+  uint32_t dma;       // source byte offset of this lane's chunk in a full slot (rows 8w + lane/8)
+  uint32_t kaddr[4];  // QK^T A operand of this wave's k-step i: kaddr[i & 3] + 4096 * (i >> 2)
+  uint32_t vaddr[2];  // PV A operand (tr reads) of this wave's first column block, rows 8tt + 4h + j: [tt]
 };
 
+// Wave part `part` of a head group covers k-steps part*KS .. +KS-1 and column
+// blocks part*NCB .. +NCB-1.
 template <int NSPLIT>
-__device__ __forceinline__ void make_tables(LaneTables<NSPLIT>& t, int lane, int w, int part) {
+__device__ __forceinline__ void make_tables(LaneTables& t, int lane, int w, int part) {
   constexpr int KS = kKSteps / NSPLIT;
-  constexpr int NCB = 16 / NSPLIT;
-  for (int k = 0; k < kDmaPerWave; ++k) {
-    int cl = (w * kDmaPerWave + k) * 64 + lane;  // LDS chunk written by this lane
-    int m = cl / 72, pos = cl % 72;
-    int col = (pos & ~7) | ((pos ^ row_swz(m)) & 7);  // source chunk (the swizzle is an involution)
-    t.dma[k] = ((uint32_t)m << 16) | (uint32_t)(col * 16);
-  }
+  constexpr int NCB = kCB / NSPLIT;
+  t.dma = dma_lane_off(lane, w, kTS);
   {
-    // k-step ks = part*KS + i reads chunk 2*ks + h of row m
+    // global k-step g reads logical chunk 2g + h of row m (dims 16g + 8h ..
+    // +7): column group g / 4, chunk (2g + h) % 8.  Steps g0 + 4q + j differ
+    // from step g0 + j by q column groups.
     const int m = lane & 31, h = lane >> 5;
-    for (int i = 0; i < 4; ++i) {
-      const int chunk = 2 * (part * KS + i) + h;
-      t.kaddr[i] = m * kRowBytes + 16 * ((chunk & ~7) | ((chunk ^ row_swz(m)) & 7));
+    for (int j = 0; j < 4; ++j) {
+      const int g = part * KS + j;
+      t.kaddr[j] = kGroupBytes * (g >> 2) + m * 128 + 16 * ((2 * (g & 3) + h) ^ row_swz(m));
     }
   }
   {
-    // tr read of rows m = 16ks + 8tt + 4h + j (j = row in the 4-row block),
-    // columns 32cb + 16cpart + 4q .. +3 with cb = part*NCB + cbi.
+    // ds_read_b64_tr_b16 for column block cb, k-step 0: within 16-lane group
+    // G lane 4j + q supplies columns 32cb + 16*(G&1) + 4q .. +3 of token row
+    // 8tt + 4*(G>>1) + j.  Odd column blocks flip chunk bit 2 (address ^ 64),
+    // k-step 1 adds 16 rows (2048 bytes), block pair cb/2 is column group
+    // cb/2.  part * NCB is even, so local and global block parity agree.
     const int G = lane >> 4, i = lane & 15, j = i >> 2, q = i & 3, h = G >> 1, cpart = G & 1;
-    const int m = 4 * h + j;  // ks = tt = 0; row_swz(m) is the same for all (ks, tt)
-    const int low = (2 * cpart + (q >> 1)) ^ row_swz(m);
-    t.vaddr = m * kRowBytes + 128 * (part * NCB / 2) + 16 * (low & 7) + 8 * (q & 1);
+    for (int tt = 0; tt < 2; ++tt) {
+      const int m = 8 * tt + 4 * h + j;
+      t.vaddr[tt] = kGroupBytes * (part * NCB / 2) + m * 128 + 16 * ((2 * cpart + (q >> 1)) ^ row_swz(m)) +
+                    8 * (q & 1);
+    }
   }
 }
 
@@ -239,8 +270,10 @@ __device__ __forceinline__ void make_tables(LaneTables<NSPLIT>& t, int lane, int
 // slot a DMA targets and would otherwise wait for every copy in flight before
 // each LDS read.  The ring accounts for these copies itself (explicit vmcnt
 // before each barrier).  The kernel keeps no other value in m0.
+template <int OFF>
 __device__ __forceinline__ void dma16(const char* sbase, uint32_t voff, uint32_t lds_base) {
-  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(sbase), "s"(lds_base)
+  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1 offset:%3" ::"v"(voff), "s"(sbase),
+               "s"(lds_base), "n"(OFF)
                : "memory");
 }
 
@@ -253,19 +286,28 @@ __device__ __forceinline__ const char* uniform_ptr(const char* p) {
 
 __device__ __forceinline__ uint32_t lds_addr(const lds_char* p) { return (uint32_t)(uintptr_t)p; }
 
-// Issue this wave's share of one slot's DMA: 32 rows starting at `src`; rows
-// at and beyond `nvalid` re-read row nvalid-1 (a valid row), so the slot never
-// holds foreign or unwritten data.
-template <int NSPLIT>
-__device__ __forceinline__ void dma_slot(lds_char* dst, const char* src, int nvalid, const LaneTables<NSPLIT>& t,
-                                         int w) {
-  const char* base = uniform_ptr(src);
-  const uint32_t lds0 = __builtin_amdgcn_readfirstlane(lds_addr(dst) + w * kDmaPerWave * 1024);
-#pragma unroll
-  for (int k = 0; k < kDmaPerWave; ++k) {
-    const uint32_t m = t.dma[k] >> 16, off = t.dma[k] & 0xffff;
-    const uint32_t mm = m < (uint32_t)nvalid ? m : (uint32_t)(nvalid - 1);
-    dma16(base, mm * kRowBytes + off, lds0 + k * 1024);
+// This wave's share of one slot's DMA, prepared in scalar registers: nine
+// copies of 1 KB (rows 8w .. 8w+7 of each column group).  Rows at and beyond
+// the slot's valid count re-read its last valid row, so a slot never holds
+// foreign or unwritten data.
+struct DmaJob {
+  const char* base;  // source row 0 of the slot
+  uint32_t off;      // per-lane source offset
+  uint32_t lds0;     // LDS address of rows 8w.. of column group 0
+};
+
+// The instruction's immediate offset moves both the global source and the
+// LDS destination; the M0 base takes it back out of the latter.
+template <int KK>
+__device__ __forceinline__ void dma_issue(const DmaJob& j) {
+  dma16<128 * KK>(j.base, j.off, j.lds0 + KK * (kGroupBytes - 128));
+}
+
+template <int KK = 0>
+__device__ __forceinline__ void dma_issue_all(const DmaJob& j) {
+  if constexpr (KK < kDmaPerWave) {
+    dma_issue<KK>(j);
+    dma_issue_all<KK + 1>(j);
   }
 }
 
@@ -295,7 +337,7 @@ __device__ __forceinline__ int page_of(PageCache& pc, const int32_t* bt_seg, int
 
 template <int NSPLIT>
 struct Acc {
-  f32x16 o[16 / NSPLIT];  // O^T accumulators (AGPRs), relative to the reference max
+  f32x16 o[kCB / NSPLIT];  // O^T accumulators (AGPRs), relative to the reference max
 };
 
 // Softmax state of one lane's head.  The reference max is fixed after the
@@ -308,103 +350,169 @@ struct SoftmaxState {
   float l_sum;   // this lane's share of sum p
 };
 
-template <int NSPLIT>
-__device__ __forceinline__ void compute_slot(const lds_char* buf, LDS_AS f32x4* xch, int nvalid,
-                                             const bf16x8 (&qf)[kKSteps / NSPLIT], const LaneTables<NSPLIT>& t,
-                                             SoftmaxState& st, Acc<NSPLIT>& acc, float scale_log2, int lane, int w) {
+// This wave's partial S^T of one slot: 32 tokens x 32 heads over its KS
+// k-steps, fp32.
+// K fragments are read kRA steps ahead of the MFMA that consumes them; the
+// scheduling fences keep LDS reads and MFMAs in this order and let only
+// VALU work (the softmax of the previous slot) move between them.
+constexpr int kRA = 4;
+constexpr int kFenceValu = 0x2 | 0x400;  // sched_barrier mask: VALU and transcendental may cross
+
+template <int NSPLIT, int I, bool DMA>
+__device__ __forceinline__ void qk_steps(f32x16& s, bf16x8 (&kb)[kRA], const lds_char* buf,
+                                         const bf16x8 (&qf)[kKSteps / NSPLIT], const LaneTables& t,
+                                         const DmaJob& job) {
   constexpr int KS = kKSteps / NSPLIT;
-  constexpr int NCB = 16 / NSPLIT;
-  // partial S^T[token][head] over this wave's share of the 576 columns
+  if constexpr (I < KS) {
+    __builtin_amdgcn_sched_barrier(kFenceValu);
+    s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kb[I % kRA], qf[I], s, 0, 0, 0);
+    if constexpr (I + kRA < KS)
+      kb[I % kRA] = *(const LDS_AS bf16x8*)(buf + t.kaddr[(I + kRA) & 3] + kGroupBytes * ((I + kRA) >> 2));
+    if constexpr (DMA) {
+      // the next slot's copies ride between the MFMAs, so that the wave
+      // never stalls on a full memory queue with nothing else to issue
+      constexpr int R = KS / kDmaPerWave;
+      if constexpr (I % R == R - 1) dma_issue<I / R>(job);
+    }
+    qk_steps<NSPLIT, I + 1, DMA>(s, kb, buf, qf, t, job);
+  }
+}
+
+template <int NSPLIT, bool DMA>
+__device__ __forceinline__ f32x16 qk_partial(const lds_char* buf, const bf16x8 (&qf)[kKSteps / NSPLIT],
+                                             const LaneTables& t, const DmaJob& job) {
+  static_assert((kKSteps / NSPLIT) % kDmaPerWave == 0, "copies spread evenly over the k-steps");
+  bf16x8 kb[kRA];
+#pragma unroll
+  for (int i = 0; i < kRA; ++i) kb[i] = *(const LDS_AS bf16x8*)(buf + t.kaddr[i & 3] + kGroupBytes * (i >> 2));
   f32x16 s = {};
-#pragma unroll
-  for (int i = 0; i < KS; ++i) {
-    bf16x8 kf = *(const LDS_AS bf16x8*)(buf + t.kaddr[i & 3] + 128 * (i >> 2));
-    s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[i], s, 0, 0, 0);
-  }
-  // keep three K fragments in flight ahead of the MFMA that consumes them
-  __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);
-#pragma unroll
-  for (int i = 0; i < KS - 3; ++i) {
-    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-  }
-  __builtin_amdgcn_sched_group_barrier(0x008, 3, 0);
-  // exchange partials inside the head group; every wave sums them in the
-  // same order so the group holds bit-identical scores
-  const int grp = (w / NSPLIT) * NSPLIT;
+  qk_steps<NSPLIT, 0, DMA>(s, kb, buf, qf, t, job);
+  __builtin_amdgcn_sched_barrier(kFenceValu);
+  return s;
+}
+
+// Publish this wave's partial: [wave][r4][lane] 16-byte rows, lane-contiguous.
+__device__ __forceinline__ void put_partial(LDS_AS f32x4* xch, const f32x16& s, int w, int lane) {
 #pragma unroll
   for (int r4 = 0; r4 < 4; ++r4) {
-    f32x4 v = {s[4 * r4], s[4 * r4 + 1], s[4 * r4 + 2], s[4 * r4 + 3]};
+    const f32x4 v = {s[4 * r4], s[4 * r4 + 1], s[4 * r4 + 2], s[4 * r4 + 3]};
     xch[(w * 4 + r4) * 64 + lane] = v;
   }
-  wait_vm_lgkm0<63>();  // lgkmcnt(0): this wave's LDS writes are done
-  barrier();
+}
+
+// Full S^T of the head group.  Two parts: own + partner (fp32 addition is
+// commutative, so both waves get the same bits).  Four parts: (p0 + p1) +
+// (p2 + p3), every term read back from LDS.
+template <int NSPLIT>
+__device__ __forceinline__ f32x16 total_scores(const LDS_AS f32x4* xch, const f32x16& own, int w, int lane) {
   f32x16 tot;
+  if constexpr (NSPLIT == 2) {
 #pragma unroll
-  for (int r4 = 0; r4 < 4; ++r4) {
-    f32x4 acc = xch[(grp * 4 + r4) * 64 + lane];
+    for (int r4 = 0; r4 < 4; ++r4) {
+      const f32x4 v = xch[((w ^ 1) * 4 + r4) * 64 + lane];
 #pragma unroll
-    for (int p = 1; p < NSPLIT; ++p) acc += xch[((grp + p) * 4 + r4) * 64 + lane];
-    tot[4 * r4] = acc[0];
-    tot[4 * r4 + 1] = acc[1];
-    tot[4 * r4 + 2] = acc[2];
-    tot[4 * r4 + 3] = acc[3];
+      for (int e = 0; e < 4; ++e) tot[4 * r4 + e] = own[4 * r4 + e] + v[e];
+    }
+  } else {
+    const int g0 = w & ~3;
+#pragma unroll
+    for (int r4 = 0; r4 < 4; ++r4) {
+      const f32x4 p0 = xch[((g0 + 0) * 4 + r4) * 64 + lane];
+      const f32x4 p1 = xch[((g0 + 1) * 4 + r4) * 64 + lane];
+      const f32x4 p2 = xch[((g0 + 2) * 4 + r4) * 64 + lane];
+      const f32x4 p3 = xch[((g0 + 3) * 4 + r4) * 64 + lane];
+      const f32x4 v = (p0 + p1) + (p2 + p3);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) tot[4 * r4 + e] = v[e];
+    }
   }
-  // online softmax (base 2) over the slot's tokens for this lane's head
+  return tot;
+}
+
+// max over lanes l and l^32 (the two token halves of one head's S^T column)
+__device__ __forceinline__ float max_halves(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
+__device__ __forceinline__ float sum_halves(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// Softmax numerators of one slot as bf16 P^T operands.  Lane l, register r
+// holds token 8*(r/4) + 4*(l/32) + r%4 of head l%32; tokens at and beyond
+// nvalid (only the last slot of a segment has any) get p = 0.
+template <bool MASK>
+__device__ __forceinline__ void softmax_slot(const f32x16& s, int nvalid, SoftmaxState& st, float scale_log2,
+                                             bf16x8& pb0, bf16x8& pb1, int lane) {
   float x[16];
-  float mx = -INFINITY;
   const int hi = lane >> 5;
 #pragma unroll
   for (int r = 0; r < 16; ++r) {
-    const int m = 8 * (r >> 2) + 4 * hi + (r & 3);
-    x[r] = m < nvalid ? tot[r] * scale_log2 : -INFINITY;
-    mx = fmaxf(mx, x[r]);
+    if constexpr (MASK) {
+      const int m = 8 * (r >> 2) + 4 * hi + (r & 3);
+      x[r] = m < nvalid ? s[r] : -INFINITY;
+    } else {
+      x[r] = s[r];
+    }
   }
-  mx = fmaxf(mx, __shfl_xor(mx, 32));  // lanes l and l^32 hold the two token halves of a head
+  float mx = x[0];
+#pragma unroll
+  for (int r = 1; r < 16; ++r) mx = fmaxf(mx, x[r]);
+  mx = max_halves(mx) * scale_log2;  // scale_log2 > 0: the max commutes with the scaling
   // the first slot fixes the reference; later slots may exceed it by up to
   // kTau without loss (p <= 2^kTau), beyond that the segment is redone
-  if (st.m_ref == -INFINITY) st.m_ref = mx;
+  st.m_ref = st.m_ref == -INFINITY ? mx : st.m_ref;
   st.m_seen = fmaxf(st.m_seen, mx);
-  const float mref = st.m_ref;
+  const float nref = -st.m_ref;
   f32x8 p0, p1;
-  float lsum = 0.0f;
 #pragma unroll
   for (int r = 0; r < 8; ++r) {
-    p0[r] = __builtin_amdgcn_exp2f(x[r] - mref);
-    p1[r] = __builtin_amdgcn_exp2f(x[r + 8] - mref);
-    lsum += p0[r] + p1[r];
+    p0[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(x[r], scale_log2, nref));
+    p1[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(x[r + 8], scale_log2, nref));
   }
+  float lsum = 0.0f;
+#pragma unroll
+  for (int r = 0; r < 8; ++r) lsum += p0[r] + p1[r];
   st.l_sum += lsum;
-  const bf16x8 pb0 = __builtin_convertvector(p0, bf16x8);
-  const bf16x8 pb1 = __builtin_convertvector(p1, bf16x8);
-  // O^T[c][head] += V^T . P^T over this wave's column blocks.  k-step 0 of a
-  // block covers tokens 0..15 in the order the S^T layout hands them to this
-  // lane (rows 4h+j and 8+4h+j), k-step 1 tokens 16..31.
-  const uint32_t va0 = t.vaddr, va1 = t.vaddr ^ 64u;
+  pb0 = __builtin_convertvector(p0, bf16x8);
+  pb1 = __builtin_convertvector(p1, bf16x8);
+}
+
+// O^T[c][head] += V^T . P^T over this wave's column blocks.  k-step 0 of a
+// block covers tokens 0..15 in the order the S^T layout hands them to this
+// lane (rows 4h+j and 8+4h+j), k-step 1 tokens 16..31.
+template <int NSPLIT>
+__device__ __forceinline__ void pv_slot(const lds_char* buf, const bf16x8& pb0, const bf16x8& pb1,
+                                        const LaneTables& t, Acc<NSPLIT>& acc) {
+  constexpr int NCB = kCB / NSPLIT;
+  const lds_char* b0 = buf + t.vaddr[0];
+  const lds_char* b1 = buf + t.vaddr[1];
+  const lds_char* b0x = buf + (t.vaddr[0] ^ 64u);
+  const lds_char* b1x = buf + (t.vaddr[1] ^ 64u);
+  bf16x4 va[2][4];
+  auto load = [&](int cb, bf16x4(&v)[4]) {
+    const lds_char* p0 = (cb & 1) ? b0x : b0;
+    const lds_char* p1 = (cb & 1) ? b1x : b1;
+    const int step = kGroupBytes * (cb >> 1);
+    v[0] = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((LDS_AS bf16x4*)(p0 + step));
+    v[1] = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((LDS_AS bf16x4*)(p1 + step));
+    v[2] = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((LDS_AS bf16x4*)(p0 + step + 16 * 128));
+    v[3] = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((LDS_AS bf16x4*)(p1 + step + 16 * 128));
+  };
+  load(0, va[0]);
 #pragma unroll
-  for (int cbi = 0; cbi < NCB; ++cbi) {
-    const uint32_t va = (cbi & 1) ? va1 : va0;
-    const int step = 128 * (cbi >> 1);
-    bf16x4 a0 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((LDS_AS bf16x4*)(buf + va + step));
-    bf16x4 a1 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((LDS_AS bf16x4*)(buf + va + step + 8 * kRowBytes));
-    bf16x4 c0 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((LDS_AS bf16x4*)(buf + va + step + 16 * kRowBytes));
-    bf16x4 c1 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((LDS_AS bf16x4*)(buf + va + step + 24 * kRowBytes));
-    const bf16x8 v0 = __builtin_shufflevector(a0, a1, 0, 1, 2, 3, 4, 5, 6, 7);
-    const bf16x8 v1 = __builtin_shufflevector(c0, c1, 0, 1, 2, 3, 4, 5, 6, 7);
-    acc.o[cbi] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(v0, pb0, acc.o[cbi], 0, 0, 0);
-    acc.o[cbi] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(v1, pb1, acc.o[cbi], 0, 0, 0);
+  for (int cb = 0; cb < NCB; ++cb) {
+    __builtin_amdgcn_sched_barrier(0);
+    if (cb + 1 < NCB) load(cb + 1, va[(cb + 1) & 1]);
+    const bf16x4(&v)[4] = va[cb & 1];
+    const bf16x8 v0 = __builtin_shufflevector(v[0], v[1], 0, 1, 2, 3, 4, 5, 6, 7);
+    const bf16x8 v1 = __builtin_shufflevector(v[2], v[3], 0, 1, 2, 3, 4, 5, 6, 7);
+    acc.o[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(v0, pb0, acc.o[cb], 0, 0, 0);
+    acc.o[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(v1, pb1, acc.o[cb], 0, 0, 0);
   }
-  // the four V^T reads of block cbi+1 are in flight while block cbi's two
-  // MFMAs run
-  __builtin_amdgcn_sched_group_barrier(0x100, 4, 1);
-#pragma unroll
-  for (int cbi = 0; cbi < NCB - 1; ++cbi) {
-    __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
-    __builtin_amdgcn_sched_group_barrier(0x100, 2, 1);
-    __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
-    __builtin_amdgcn_sched_group_barrier(0x100, 2, 1);
-  }
-  __builtin_amdgcn_sched_group_barrier(0x008, 2, 1);
+  __builtin_amdgcn_sched_barrier(0);
 }
 
 struct SegCtx {
@@ -412,79 +520,45 @@ struct SegCtx {
   int tok0, tok1, nslots, npages;
 };
 
-// One step of the ring: wait for slot s, free the ring slot consumed in the
-// previous step and refill it with slot s+3, compute slot s.  A plain loop
-// with a run-time slot offset: the DMA is invisible to the compiler, so the
-// slots need no compile-time identity, and a loop body without early exits
-// lets the accumulators stay in fixed AGPRs.
-template <int NSPLIT>
-__device__ __forceinline__ void ring_step(int s, lds_char* ring, LDS_AS f32x4* xch, const DecodeArgs& a,
-                                          const SegCtx& sg, PageCache& pc, const bf16x8 (&qf)[kKSteps / NSPLIT],
-                                          const LaneTables<NSPLIT>& t, SoftmaxState& st, Acc<NSPLIT>& acc,
-                                          int lane, int w) {
-  const int later = min(sg.nslots - 1 - s, 2);
-  if (later == 2) wait_vm_lgkm0<2 * kDmaPerWave>();
-  else if (later == 1) wait_vm_lgkm0<kDmaPerWave>();
-  else wait_vm_lgkm0<0>();
-  barrier();
-  if (s + 3 < sg.nslots) {
-    const int ns = s + 3;
-    const int tk = sg.tok0 + ns * kTS;
-    const int page = page_of(pc, sg.bt_seg, ns >> 1, sg.npages, lane, a.num_pages);
-    const char* src = a.kv + ((size_t)page * kPage + (ns & 1) * kTS) * kRowBytes;
-    dma_slot<NSPLIT>(ring + (ns & 3) * kSlotBytes, src, min(kTS, sg.tok1 - tk), t, w);
-  }
-  compute_slot<NSPLIT>(ring + (s & 3) * kSlotBytes, xch, min(kTS, sg.tok1 - (sg.tok0 + s * kTS)), qf, t, st, acc,
-                       a.scale_log2, lane, w);
-}
-
-// Merge the nsplit pieces of sequence b for the heads of one slab:
-// LSE = log2 sum_s 2^lse_s, O = sum_s 2^(lse_s - LSE) O_s.  Piece s of the
-// sequence sits in workspace slot first + s.
-template <int HPS>
-__device__ void merge_pieces(const DecodeArgs& a, int b, int slab, int first, int nsplit) {
-  for (int idx = threadIdx.x; idx < HPS * (kDV / 4); idx += kThreads) {
-    const int head = slab * HPS + idx / (kDV / 4), c4 = idx % (kDV / 4);
-    if (head >= a.heads) break;
-    float mx = -INFINITY;
-    for (int s = 0; s < nsplit; ++s) mx = fmaxf(mx, a.ws_lse[((size_t)first + s) * a.heads + head]);
-    f32x4 acc = {};
-    float wsum = 0.0f;
-    for (int s = 0; s < nsplit; ++s) {
-      const float l = a.ws_lse[((size_t)first + s) * a.heads + head];
-      const float wgt = (l == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(l - mx);
-      const f32x4 v = *(const f32x4*)(a.ws_o + (((size_t)first + s) * a.heads + head) * kDV + 4 * c4);
-      acc += wgt * v;
-      wsum += wgt;
-    }
-    acc *= wsum > 0.0f ? 1.0f / wsum : 0.0f;
-    *(bf16x4*)((__bf16*)a.out + ((size_t)b * a.heads + head) * kDV + 4 * c4) = __builtin_convertvector(acc, bf16x4);
-    if (c4 == 0) a.lse[(size_t)b * a.heads + head] = wsum > 0.0f ? (mx + __builtin_amdgcn_logf(wsum)) * kLn2 : -INFINITY;
-  }
+// DMA job that fills ring position pos with slot s of the segment.  Slots at
+// or beyond the end are replaced by the last slot: the copy then lands in a
+// free ring position that is never read, which keeps the number of copies
+// per step, and with it every vmcnt wait, the same on every step.
+__device__ __forceinline__ DmaJob prep_slot(int s, int pos, lds_char* ring, const DecodeArgs& a, const SegCtx& sg,
+                                            PageCache& pc, const LaneTables& t, int w, int lane) {
+  s = min(s, sg.nslots - 1);
+  const int tk = sg.tok0 + s * kTS;
+  const int page = page_of(pc, sg.bt_seg, s >> 1, sg.npages, lane, a.num_pages);
+  const char* src = a.kv + ((size_t)page * kPage + (s & 1) * kTS) * kRowBytes;
+  const int nvalid = min(kTS, sg.tok1 - tk);
+  DmaJob j;
+  j.base = uniform_ptr(src);
+  j.lds0 = __builtin_amdgcn_readfirstlane(lds_addr(ring + (pos & (kRing - 1)) * kSlotBytes) + w * 1024);
+  j.off = nvalid >= kTS ? t.dma : dma_lane_off(lane, w, nvalid - 1);
+  return j;
 }
 
 // ---------------------------------------------------------------- the kernel
 
 template <int NSPLIT, bool Q_FP8>
-__global__ void __launch_bounds__(kThreads, 1) mla_decode_bf16_kernel(DecodeArgs a) {
-  __shared__ __attribute__((aligned(1024))) char ring_mem[4 * kSlotBytes];  // KV ring, 4 x 36 KB
-  __shared__ __attribute__((aligned(16))) f32x4 xbuf[kWaves * 4 * 64];  // partial S^T exchange, 16 KB
-  // the epilogue's "last piece" flag reuses the exchange buffer: it is written
-  // after a barrier that all waves reach only once their last slot is done
-  volatile int& xlast = *(int*)xbuf;
+__global__ void __launch_bounds__(kThreads, 1) __attribute__((amdgpu_waves_per_eu(1, 1)))
+mla_decode_bf16_kernel(DecodeArgs a) {
+  __shared__ __attribute__((aligned(1024))) char ring_mem[kRing * kSlotBytes];  // KV ring, 4 x 36 KB
+  __shared__ __attribute__((aligned(16))) f32x4 xbuf[kWaves * 4 * 64];         // partial S^T, 16 KB
   lds_char* const ring = (lds_char*)ring_mem;
   LDS_AS f32x4* const xch = (LDS_AS f32x4*)xbuf;
+  // redo votes reuse the exchange buffer between segments, after barriers
+  // that every wave reaches past its last exchange read
+  volatile int* const votes = (volatile int*)xbuf;
 
   constexpr int KS = kKSteps / NSPLIT;
-  constexpr int NCB = 16 / NSPLIT;
+  constexpr int NCB = kCB / NSPLIT;
   constexpr int HG = kWaves / NSPLIT;  // 32-head groups per workgroup
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int hg = w / NSPLIT, part = w % NSPLIT;
 
-  // workgroup -> (range, head slab); the slabs of a range sit 8 ids apart so
-  // they land on the same XCD.
   const int g = blockIdx.x;
   // sequences with nothing to attend: O = 0, LSE = -inf (spread over the grid)
   for (int b = g; b < a.batch; b += gridDim.x) {
@@ -492,10 +566,15 @@ __global__ void __launch_bounds__(kThreads, 1) mla_decode_bf16_kernel(DecodeArgs
       for (int i = tid; i < a.heads * (kDV / 4); i += kThreads)
         *(bf16x4*)((__bf16*)a.out + ((size_t)b * a.heads) * kDV + 4 * i) = bf16x4{};
       for (int i = tid; i < a.heads; i += kThreads) a.lse[(size_t)b * a.heads + i] = -INFINITY;
+      if (tid == 0) a.ws_seq[b] = int2{0, 0};
     }
   }
-  const int r = (g / (8 * a.slabs)) * 8 + (g % 8);
-  const int slab = (g / 8) % a.slabs;
+  // workgroups are dealt round-robin to the 8 XCDs: each XCD gets a run of
+  // consecutive ranges with all their slabs, so the slabs share KV lines in
+  // one L2 and the pieces of a sequence mostly merge from it
+  const int idx = g / 8;
+  const int r = (g % 8) * a.per_xcd + idx / a.slabs;
+  const int slab = idx % a.slabs;
   if (r >= a.ranges) return;
 
   Plan pl;
@@ -504,7 +583,7 @@ __global__ void __launch_bounds__(kThreads, 1) mla_decode_bf16_kernel(DecodeArgs
   const int head = slab * (HG * 32) + hg * 32 + (lane & 31);
   const bool head_ok = head < a.heads;
 
-  LaneTables<NSPLIT> tab;
+  LaneTables tab;
   make_tables<NSPLIT>(tab, lane, w, part);
 
   int b = pl.b0, p = pl.p0;
@@ -515,7 +594,7 @@ __global__ void __launch_bounds__(kThreads, 1) mla_decode_bf16_kernel(DecodeArgs
     if (gs < ge) {
       // ---- one segment: sequence b, units [gs - p, ge - p)
       if (!first_seg) {
-        // every wave is done with the ring and its stores before it is refilled
+        // every wave is done with the ring before it is refilled
         wait_vm_lgkm0<0>();
         barrier();
       }
@@ -529,9 +608,11 @@ __global__ void __launch_bounds__(kThreads, 1) mla_decode_bf16_kernel(DecodeArgs
       sg.bt_seg = a.block_table + (size_t)b * a.max_pages + (gs - p);
       const int first_r = p / pl.C, last_r = (p + n - 1) / pl.C;
       const int nsplit = last_r - first_r + 1;
+      const int last_valid = sg.tok1 - (sg.tok0 + (sg.nslots - 1) * kTS);
+      const int nslots = sg.nslots;
 
       // query fragments (B operand of S^T = K.Q^T): head `head`, columns
-      // 16*ks + 8*(lane/32) .. +7 for this wave's k-steps
+      // 16*(part*KS + i) + 8*(lane/32) .. +7 for this wave's k-steps
       bf16x8 qf[KS];
       if constexpr (!Q_FP8) {
         const bf16x8* qrow = (const bf16x8*)((const __bf16*)a.q + ((size_t)b * a.heads + (head_ok ? head : 0)) * kD);
@@ -550,10 +631,9 @@ __global__ void __launch_bounds__(kThreads, 1) mla_decode_bf16_kernel(DecodeArgs
       }
 
       PageCache pc;
+      // (also completes the query loads, so the ring's vmcnt accounting
+      // counts DMA only)
       page_cache_load(pc, sg.bt_seg, 0, sg.npages, lane);
-      // query and block-table loads complete before any DMA is issued, so the
-      // ring's vmcnt accounting counts DMA only
-      wait_vm_lgkm0<0>();
 
       SoftmaxState st;
       st.m_ref = -INFINITY;
@@ -566,26 +646,51 @@ __global__ void __launch_bounds__(kThreads, 1) mla_decode_bf16_kernel(DecodeArgs
         for (int c = 0; c < NCB; ++c) acc.o[c] = f32x16{};
         st.l_sum = 0.0f;
         st.m_seen = -INFINITY;
-        // prologue DMA: slots 0..2
+        // prologue: slots 0..2 in flight (slots past the end re-copy the
+        // last one), partial QK^T of slot 0
 #pragma unroll
-        for (int s = 0; s < 3; ++s) {
-          if (s < sg.nslots) {
-            const int tk = sg.tok0 + s * kTS;
-            const int page = page_of(pc, sg.bt_seg, s >> 1, sg.npages, lane, a.num_pages);
-            const char* src = a.kv + ((size_t)page * kPage + (s & 1) * kTS) * kRowBytes;
-            dma_slot<NSPLIT>(ring + s * kSlotBytes, src, min(kTS, sg.tok1 - tk), tab, w);
-          }
+        for (int s = 0; s < 3; ++s) dma_issue_all(prep_slot(s, s, ring, a, sg, pc, tab, w, lane));
+        wait_vm_lgkm0<2 * kDmaPerWave>();
+        barrier();
+        f32x16 sc = qk_partial<NSPLIT, false>(ring, qf, tab, DmaJob{});
+        bf16x8 pb0, pb1;
+        // steady state, slot s: publish its partial (computed one step
+        // earlier) and wait for slot s+1 (slot s+2 stays in flight);
+        // barrier; then the partial QK^T of slot s+1 runs beside the softmax
+        // of slot s with the copies of slot s+3 (into the ring position that
+        // slot s-1 left) between its MFMAs, then PV of slot s; a second
+        // barrier frees ring position s and the exchange buffer
+        for (int s = 0; s + 1 < nslots; ++s) {
+          put_partial(xch, sc, w, lane);
+          wait_vm_lgkm0<kDmaPerWave>();
+          barrier();
+          const f32x16 tot = total_scores<NSPLIT>(xch, sc, w, lane);
+          const DmaJob job = prep_slot(s + 3, s + 3, ring, a, sg, pc, tab, w, lane);
+          sc = qk_partial<NSPLIT, true>(ring + ((s + 1) & (kRing - 1)) * kSlotBytes, qf, tab, job);
+          softmax_slot<false>(tot, kTS, st, a.scale_log2, pb0, pb1, lane);
+          pv_slot<NSPLIT>(ring + (s & (kRing - 1)) * kSlotBytes, pb0, pb1, tab, acc);
+          wait_vm_lgkm0<63>();  // lgkmcnt(0): this wave's LDS reads are done
+          barrier();
         }
-        for (int s = 0; s < sg.nslots; ++s) ring_step<NSPLIT>(s, ring, xch, a, sg, pc, qf, tab, st, acc, lane, w);
+        {
+          // last slot (the only one that can be partial)
+          put_partial(xch, sc, w, lane);
+          wait_vm_lgkm0<0>();
+          barrier();
+          const f32x16 tot = total_scores<NSPLIT>(xch, sc, w, lane);
+          softmax_slot<true>(tot, last_valid, st, a.scale_log2, pb0, pb1, lane);
+          pv_slot<NSPLIT>(ring + ((nslots - 1) & (kRing - 1)) * kSlotBytes, pb0, pb1, tab, acc);
+        }
         // workgroup vote on a redo (every wave is past its last exchange read)
         wait_vm_lgkm0<0>();
         barrier();
         const int my_vote = __any(st.m_seen > st.m_ref + kTau) ? 1 : 0;  // all lanes vote
-        if (lane == 0) ((volatile int*)xbuf)[w] = my_vote;
+        if (lane == 0) votes[w] = my_vote;
         wait_vm_lgkm0<0>();
         barrier();
-        const int vote = ((volatile int*)xbuf)[0] | ((volatile int*)xbuf)[1] | ((volatile int*)xbuf)[2] |
-                         ((volatile int*)xbuf)[3];
+        int vote = 0;
+#pragma unroll
+        for (int i = 0; i < kWaves; ++i) vote |= votes[i];
         wait_vm_lgkm0<0>();
         barrier();  // votes read before the buffer is reused
         if (!__builtin_amdgcn_readfirstlane(vote)) break;
@@ -595,7 +700,7 @@ __global__ void __launch_bounds__(kThreads, 1) mla_decode_bf16_kernel(DecodeArgs
 
       // ---- epilogue: normalise and store this wave's columns (final output,
       // or this piece's partial in its workspace slot)
-      const float l_tot = st.l_sum + __shfl_xor(st.l_sum, 32);
+      const float l_tot = sum_halves(st.l_sum);
       const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
       const float lse2 = l_tot > 0.0f ? st.m_ref + __builtin_amdgcn_logf(l_tot) : -INFINITY;
       if (head_ok) {
@@ -619,19 +724,9 @@ __global__ void __launch_bounds__(kThreads, 1) mla_decode_bf16_kernel(DecodeArgs
           else a.ws_lse[pslot * a.heads + head] = lse2;
         }
       }
-      if (nsplit > 1) {
-        // publish this piece; the last of the nsplit pieces merges them
-        __threadfence();
-        __syncthreads();
-        int* cnt = a.ws_count + (size_t)b * a.slabs + slab;
-        if (tid == 0) xlast = atomicAdd(cnt, 1) == nsplit - 1;
-        __syncthreads();
-        if (xlast) {
-          __threadfence();
-          merge_pieces<HG * 32>(a, b, slab, b + first_r, nsplit);
-          if (tid == 0) *cnt = 0;
-        }
-      }
+      // where the pieces of b sit (every piece writes the same record); the
+      // merge kernel that follows on the stream combines split sequences
+      if (tid == 0) a.ws_seq[b] = int2{b + first_r, nsplit};
     }
     p += n;
     ++b;
@@ -639,8 +734,64 @@ __global__ void __launch_bounds__(kThreads, 1) mla_decode_bf16_kernel(DecodeArgs
   }
 }
 
+// ---------------------------------------------------------------- split-KV merge
+
+struct MergeArgs {
+  const int2* seq;   // [B] {workspace slot of piece 0, pieces}
+  const float* ws_o;
+  const float* ws_lse;
+  void* out;
+  float* lse;
+  int32_t heads;
+};
+
+constexpr int kMergeHeads = 16;  // heads per merge workgroup, 16 threads each
+
+// O = sum_s 2^(lse_s - M) O_s / sum_s 2^(lse_s - M) with M = max_s lse_s, and
+// LSE = M + log2 sum_s 2^(lse_s - M) (back to natural log), for sequences the
+// decode kernel split over several ranges; piece s sits in workspace slot
+// first + s.  A thread owns 8 float4 columns of one head and keeps all eight
+// loads of a piece in flight.
+__global__ void __launch_bounds__(kThreads) mla_merge_kernel(MergeArgs m) {
+  const int b = blockIdx.x;
+  const int2 info = m.seq[b];
+  const int first = info.x, nsplit = info.y;
+  if (nsplit <= 1) return;
+  constexpr int TPH = kThreads / kMergeHeads;
+  constexpr int U = kDV / 4 / TPH;
+  const int head = blockIdx.y * kMergeHeads + threadIdx.x / TPH, sub = threadIdx.x % TPH;
+  if (head >= m.heads) return;
+  const float* lse_col = m.ws_lse + (size_t)first * m.heads + head;
+  float mx = -INFINITY;
+  for (int s = 0; s < nsplit; ++s) mx = fmaxf(mx, lse_col[(size_t)s * m.heads]);
+  const size_t pstride = (size_t)m.heads * (kDV / 4);  // float4 per piece
+  const f32x4* src0 = (const f32x4*)(m.ws_o + ((size_t)first * m.heads + head) * kDV) + sub;
+  f32x4 acc[U];
+#pragma unroll
+  for (int u = 0; u < U; ++u) acc[u] = f32x4{};
+  float wsum = 0.0f;
+#pragma unroll 2
+  for (int s = 0; s < nsplit; ++s) {
+    const float l = lse_col[(size_t)s * m.heads];
+    const float wgt = l == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(l - mx);
+    const f32x4* ps = src0 + s * pstride;
+    f32x4 v[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) v[u] = ps[u * TPH];
+#pragma unroll
+    for (int u = 0; u < U; ++u) acc[u] += wgt * v[u];
+    wsum += wgt;
+  }
+  const float inv = wsum > 0.0f ? 1.0f / wsum : 0.0f;
+  bf16x4* dst = (bf16x4*)((__bf16*)m.out + ((size_t)b * m.heads + head) * kDV) + sub;
+#pragma unroll
+  for (int u = 0; u < U; ++u) dst[u * TPH] = __builtin_convertvector(acc[u] * inv, bf16x4);
+  if (sub == 0) m.lse[(size_t)b * m.heads + head] = wsum > 0.0f ? (mx + __builtin_amdgcn_logf(wsum)) * kLn2 : -INFINITY;
+}
+
 int nsplit_for_heads(int heads) { return heads > 32 ? 2 : 4; }
-int slabs_for_heads(int heads) { return heads > 64 ? 2 : 1; }
+int heads_per_slab(int heads) { return 32 * (kWaves / nsplit_for_heads(heads)); }
+int slabs_for_heads(int heads) { return (heads + heads_per_slab(heads) - 1) / heads_per_slab(heads); }
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
@@ -658,15 +809,19 @@ int32_t decode_ranges(int32_t cus, int32_t batch, int32_t max_pages, int32_t top
   return (int32_t)r;
 }
 
-// Workspace: [B][slabs] int counters | [(ranges + B)][H] fp32 LSE | [(ranges + B)][H][512] fp32 O.
+// Workspace: [B] int2 piece records | [(ranges + B)][H] fp32 LSE | [(ranges + B)][H][512] fp32 O.
 size_t decode_workspace_bytes(int32_t ranges, int32_t batch, int32_t heads) {
   const size_t slots = (size_t)ranges + (size_t)batch;
-  return align256(sizeof(int) * (size_t)batch * slabs_for_heads(heads)) + align256(sizeof(float) * slots * heads) +
+  return align256(sizeof(int2) * (size_t)batch) + align256(sizeof(float) * slots * heads) +
          align256(sizeof(float) * slots * heads * kDV);
 }
 
+// Every decode call rewrites all the state it reads back, so a workspace
+// needs no preparation; this clears the piece records so that a workspace
+// never holds stale ones.
 hipError_t init_decode_workspace(void* workspace, int32_t batch, int32_t heads, hipStream_t stream) {
-  const int n = batch * slabs_for_heads(heads);
+  (void)heads;
+  const int n = 2 * batch;
   hipLaunchKernelGGL(mla_zero_kernel, dim3((n + 255) / 256), dim3(256), 0, stream, (int*)workspace, n);
   return hipGetLastError();
 }
@@ -684,8 +839,8 @@ hipError_t launch_decode(const DecodeLaunch& d, hipStream_t stream) {
   a.slabs = slabs_for_heads(d.heads);
   char* ws = (char*)d.workspace;
   const size_t slots = (size_t)d.ranges + (size_t)d.batch;
-  a.ws_count = (int*)ws;
-  ws += align256(sizeof(int) * (size_t)d.batch * a.slabs);
+  a.ws_seq = (int2*)ws;
+  ws += align256(sizeof(int2) * (size_t)d.batch);
   a.ws_lse = (float*)ws;
   ws += align256(sizeof(float) * slots * d.heads);
   a.ws_o = (float*)ws;
@@ -695,13 +850,12 @@ hipError_t launch_decode(const DecodeLaunch& d, hipStream_t stream) {
   a.max_pages = d.max_pages;
   a.topk = d.topk;
   a.ranges = d.ranges;
+  a.per_xcd = (d.ranges + 7) / 8;
   a.scale_log2 = d.softmax_scale * kLog2e;
   a.q_descale = d.q_descale;
 
   if (d.kv_fp8 || d.topk > 0) return hipErrorNotSupported;
-  // the slabs of a range are 8 workgroup ids apart: round the grid up to that
-  const int groups = (d.ranges + 7) / 8;
-  const dim3 grid(groups * 8 * a.slabs), block(kThreads);
+  const dim3 grid(a.per_xcd * 8 * a.slabs), block(kThreads);
   if (nsplit_for_heads(d.heads) == 2) {
     if (d.q_fp8) hipLaunchKernelGGL((mla_decode_bf16_kernel<2, true>), grid, block, 0, stream, a);
     else hipLaunchKernelGGL((mla_decode_bf16_kernel<2, false>), grid, block, 0, stream, a);
@@ -709,6 +863,17 @@ hipError_t launch_decode(const DecodeLaunch& d, hipStream_t stream) {
     if (d.q_fp8) hipLaunchKernelGGL((mla_decode_bf16_kernel<4, true>), grid, block, 0, stream, a);
     else hipLaunchKernelGGL((mla_decode_bf16_kernel<4, false>), grid, block, 0, stream, a);
   }
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  MergeArgs m;
+  m.seq = a.ws_seq;
+  m.ws_o = a.ws_o;
+  m.ws_lse = a.ws_lse;
+  m.out = d.out;
+  m.lse = d.lse;
+  m.heads = d.heads;
+  hipLaunchKernelGGL(mla_merge_kernel, dim3(d.batch, (d.heads + kMergeHeads - 1) / kMergeHeads), dim3(kThreads), 0,
+                     stream, m);
   return hipGetLastError();
 }
 
