@@ -31,6 +31,7 @@ sys.path.insert(0, ROOT)
 
 METRIC = "MLA decode µs/step + achieved HBM GB/s (% of peak) at B=64,H=128,s_k=4096"
 HBM_PEAK_GBS = 8000.0
+CALIB_BYTES = 256 << 20  # plain copy used to scale the HBM traffic counters
 WORKLOAD = "paged_bf16_4096"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_paged_bf16_4096_traffic.json")
 KERNEL_SOURCES = [os.path.join(ROOT, "mqa_latent_kv_amd", "csrc", f) for f in ("decode.hip",)]
@@ -102,6 +103,10 @@ def main():
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--profile-run", action="store_true",
+                    help="for rocprofv3 counter runs: run the steps untimed, then a plain device copy of "
+                         f"{CALIB_BYTES >> 20} MiB (read {CALIB_BYTES >> 20} MiB, write as much) per step as the "
+                         "calibration of the FETCH_SIZE / WRITE_SIZE counters; prints no JSON")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only: --gpus {args.gpus} is not supported (the decode path is measured on "
@@ -133,6 +138,17 @@ def main():
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
+    if args.profile_run:
+        for _ in range(args.steps):
+            step()
+        src = torch.empty(CALIB_BYTES // 4, dtype=torch.int32, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        for _ in range(args.steps):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(f"profile run: {args.steps} decode steps, {args.steps} copies of {CALIB_BYTES} bytes", flush=True)
+        return
 
     # timed region: K back-to-back steps; an event pair around every launch
     # gives the kernel's own duration on its stream

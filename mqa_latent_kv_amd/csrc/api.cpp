@@ -22,8 +22,8 @@ int32_t check_decode_params(const mla_decode_params* p) {
   // 32-bit offsets inside the kernels: logical positions and pool rows
   if ((int64_t)p->max_pages_per_seq * MLA_PAGE_SIZE > INT32_MAX) return MLA_ERR_UNSUPPORTED;
   if ((int64_t)p->num_pages * MLA_PAGE_SIZE > INT32_MAX) return MLA_ERR_UNSUPPORTED;
-  // implemented variants: dense paged bf16 cache
-  if (p->kv_dtype != MLA_DTYPE_BF16 || p->topk != 0) return MLA_ERR_UNSUPPORTED;
+  // top-k entries index a [B, topk] int32 array; keep B*topk in 32 bits
+  if ((int64_t)p->batch * p->topk > INT32_MAX) return MLA_ERR_UNSUPPORTED;
   return MLA_OK;
 }
 
@@ -77,7 +77,7 @@ int32_t mla_decode_workspace_size(const mla_decode_params* p, size_t* bytes) {
   st = device_cus(&cus);
   if (st != MLA_OK) return st;
   const int32_t ranges = mla::decode_ranges(cus, p->batch, p->max_pages_per_seq, p->topk, p->heads);
-  *bytes = mla::decode_workspace_bytes(ranges, p->batch, p->heads);
+  *bytes = mla::decode_workspace_bytes(ranges, p->batch, p->heads, p->topk);
   return MLA_OK;
 }
 
@@ -106,7 +106,7 @@ int32_t mla_decode(const mla_decode_params* p, const void* q, const void* kv_cac
   st = device_cus(&cus);
   if (st != MLA_OK) return st;
   const int32_t ranges = mla::decode_ranges(cus, p->batch, p->max_pages_per_seq, p->topk, p->heads);
-  if (workspace_bytes < mla::decode_workspace_bytes(ranges, p->batch, p->heads)) return MLA_ERR_WORKSPACE;
+  if (workspace_bytes < mla::decode_workspace_bytes(ranges, p->batch, p->heads, p->topk)) return MLA_ERR_WORKSPACE;
   mla::DecodeLaunch d;
   d.q = q;
   d.kv = kv_cache;

@@ -62,6 +62,7 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 #define LDS_AS __attribute__((address_space(3)))
 typedef LDS_AS char lds_char;
@@ -72,7 +73,8 @@ constexpr int kPage = 64;
 constexpr int kRowBytes = kD * 2;            // bf16 latent row
 constexpr int kTS = 32;                      // tokens per LDS slot
 constexpr int kSlotBytes = kTS * kRowBytes;  // 36864
-constexpr int kRing = 4;                     // LDS slots
+constexpr int kRing = 4;                     // LDS slots (DMA ring)
+constexpr int kFillRing = 3;                 // positions of the register-fill ring
 constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
 constexpr int kDmaPerWave = kSlotBytes / 1024 / kWaves;  // 9 x 1 KB per wave per slot
@@ -94,6 +96,9 @@ struct DecodeArgs {
   float* ws_o;    // [(ranges + B) slots][H][512] fp32 partials
   float* ws_lse;  // [(ranges + B)][H] base-2 LSE of partials
   int2* ws_seq;   // [B] {workspace slot of piece 0, pieces}; pieces 0: nothing to attend
+  const int32_t* ws_rows;    // top-k: [B][topk] physical row per entry, -1 for a masked entry
+  const uint32_t* ws_masks;  // top-k: [B][mask_words] validity bits per 32-entry slot
+  int32_t mask_words;        // ceil(topk / 32)
   int32_t batch, heads, num_pages, max_pages, topk;
   int32_t ranges;    // KV ranges (workgroups per head slab)
   int32_t slabs;     // head slabs per range
@@ -229,26 +234,52 @@ __device__ __forceinline__ uint32_t dma_lane_off(int lane, int w, int row_cap) {
 struct LaneTables {
   uint32_t dma;       // source byte offset of this lane's chunk in a full slot (rows 8w + lane/8)
   uint32_t kaddr[4];  // QK^T A operand of this wave's k-step i: kaddr[i & 3] + 4096 * (i >> 2)
+  uint32_t kaddr_r[2];  // tiled split: the rope k-steps
   uint32_t vaddr[2];  // PV A operand (tr reads) of this wave's first column block, rows 8tt + 4h + j: [tt]
 };
 
-// Wave part `part` of a head group covers k-steps part*KS .. +KS-1 and column
-// blocks part*NCB .. +NCB-1.
+// How the QK^T reduction is cut between the NSPLIT waves of a head group.
+// Contiguous (bf16 cache): wave part p takes global k-steps p*KS .. +KS-1.
+// Tiled (FP8 cache): part p takes whole 128-column code tiles, TPP of them
+// (k-steps CS*p .. +CS-1), then RS rope k-steps 32 + RS*p ..; every code tile
+// sums into an fp32 accumulator of its own, so that the per-token tile scale
+// can be applied exactly.  Either way part p owns output columns 512p/NSPLIT
+// .. +512/NSPLIT-1, which in the tiled case are the same tiles.
 template <int NSPLIT>
+struct Tiling {
+  static constexpr int KS = kKSteps / NSPLIT;
+  static constexpr int TPP = 4 / NSPLIT;  // code tiles per part
+  static constexpr int CS = 8 * TPP;      // code k-steps per part
+  static constexpr int RS = 4 / NSPLIT;   // rope k-steps per part
+  static_assert(CS + RS == KS, "tiled split covers the 36 k-steps");
+};
+
+// global k-step of this part's local step i
+template <int NSPLIT, bool TILED>
+__device__ __forceinline__ int global_step(int part, int i) {
+  using T = Tiling<NSPLIT>;
+  if constexpr (TILED) return i < T::CS ? T::CS * part + i : 32 + T::RS * part + (i - T::CS);
+  else return T::KS * part + i;
+}
+
+// LDS address of the K fragment of global k-step g for this lane: logical
+// chunk 2g + h of row m (dims 16g + 8h .. +7), column group g / 4
+__device__ __forceinline__ uint32_t k_frag_addr(int g, int lane) {
+  const int m = lane & 31, h = lane >> 5;
+  return kGroupBytes * (g >> 2) + m * 128 + 16 * ((2 * (g & 3) + h) ^ row_swz(m));
+}
+
+// Wave part `part` of a head group covers the k-steps above and column
+// blocks part*NCB .. +NCB-1.
+template <int NSPLIT, bool TILED>
 __device__ __forceinline__ void make_tables(LaneTables& t, int lane, int w, int part) {
-  constexpr int KS = kKSteps / NSPLIT;
+  using T = Tiling<NSPLIT>;
   constexpr int NCB = kCB / NSPLIT;
   t.dma = dma_lane_off(lane, w, kTS);
-  {
-    // global k-step g reads logical chunk 2g + h of row m (dims 16g + 8h ..
-    // +7): column group g / 4, chunk (2g + h) % 8.  Steps g0 + 4q + j differ
-    // from step g0 + j by q column groups.
-    const int m = lane & 31, h = lane >> 5;
-    for (int j = 0; j < 4; ++j) {
-      const int g = part * KS + j;
-      t.kaddr[j] = kGroupBytes * (g >> 2) + m * 128 + 16 * ((2 * (g & 3) + h) ^ row_swz(m));
-    }
-  }
+  // steps g0 + 4q + j (code steps, contiguous) differ from step g0 + j by q
+  // column groups
+  for (int j = 0; j < 4; ++j) t.kaddr[j] = k_frag_addr(global_step<NSPLIT, TILED>(part, j), lane);
+  for (int k = 0; k < 2; ++k) t.kaddr_r[k] = TILED && k < T::RS ? k_frag_addr(global_step<NSPLIT, TILED>(part, T::CS + k), lane) : 0;
   {
     // ds_read_b64_tr_b16 for column block cb, k-step 0: within 16-lane group
     // G lane 4j + q supplies columns 32cb + 16*(G&1) + 4q .. +3 of token row
@@ -333,6 +364,90 @@ __device__ __forceinline__ int page_of(PageCache& pc, const int32_t* bt_seg, int
   return clamp_page(__builtin_amdgcn_readlane(pc.v, k - pc.base), num_pages);
 }
 
+// ---------------------------------------------------------------- register fill (FP8 cache, top-k)
+
+// KV layouts the kernel reads.
+constexpr int kKvBf16 = 0;        // bf16 rows [P,64,576], whole pages (LDS DMA)
+constexpr int kKvFp8 = 1;         // e4m3 rows [P,64,640] + fp32 scales [P,64,4], whole pages
+constexpr int kKvFp8TopK = 2;     // e4m3 rows, gathered top-k entries
+constexpr int kKvBf16TopK = 3;    // bf16 rows, gathered top-k entries
+constexpr bool kv_fp8(int m) { return m == kKvFp8 || m == kKvFp8TopK; }
+constexpr bool kv_topk(int m) { return m == kKvFp8TopK || m == kKvBf16TopK; }
+constexpr int kFp8RowBytes = 640;  // 512 e4m3 codes, 64 bf16 rope values
+
+// The register fill: every slot row is loaded by the eight lanes of one
+// wave that share lane % 8 (wave w: rows 8w .. 8w+7), lane / 8 = q picking
+// 128-byte pieces, so each load instruction reads 128 contiguous bytes per
+// row.  The lanes then write the row as bf16 into the same swizzled ring
+// layout the DMA produces, dequantising FP8 codes on the way as
+// bf16_rne(e4m3(code) * scale) with an exact fp32 product.
+template <int KVM>
+struct RawRow;
+
+template <>
+struct RawRow<kKvFp8> {
+  u32x4 code[4];  // codes 128k + 16q .. +15 of the row, k = 0..3 (column tile k)
+  u32x4 rope;     // rope bytes 16q .. +15
+  f32x4 scale;    // the row's four tile scales
+};
+template <>
+struct RawRow<kKvFp8TopK> : RawRow<kKvFp8> {};
+template <>
+struct RawRow<kKvBf16TopK> {
+  u32x4 v[9];  // bytes 128k + 16q .. +15 of the row, k = 0..8 (column group k)
+};
+
+template <int KVM>
+__device__ __forceinline__ void load_row(RawRow<KVM>& rr, const DecodeArgs& a, int row, int q) {
+  if constexpr (kv_fp8(KVM)) {
+    const char* base = a.kv + (size_t)row * kFp8RowBytes;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) rr.code[k] = *(const u32x4*)(base + 128 * k + 16 * q);
+    rr.rope = *(const u32x4*)(base + 512 + 16 * q);
+    rr.scale = *(const f32x4*)(a.kv_scales + (size_t)row * 4);
+  } else {
+#pragma unroll
+    for (int k = 0; k < 9; ++k) rr.v[k] = *(const u32x4*)(a.kv + (size_t)row * kRowBytes + 128 * k + 16 * q);
+  }
+}
+
+// 8 e4m3 codes (two words) as 8 bf16: every e4m3 value is exact in bf16
+// (the scaled conversion with scale 1 changes nothing)
+__device__ __forceinline__ u32x4 codes8(uint32_t w0, uint32_t w1) {
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  const bf16x2 a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, 1.0f, false);
+  const bf16x2 b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, 1.0f, true);
+  const bf16x2 c = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, 1.0f, false);
+  const bf16x2 d = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, 1.0f, true);
+  return u32x4{__builtin_bit_cast(uint32_t, a), __builtin_bit_cast(uint32_t, b), __builtin_bit_cast(uint32_t, c),
+               __builtin_bit_cast(uint32_t, d)};
+}
+
+// Write row r (this lane's q share) into the slot at `buf`; an FP8 row puts
+// its codes (unscaled) in columns 0..511 and its four tile scales into the
+// slot's scale table `stab` [tile][token].
+template <int KVM>
+__device__ __forceinline__ void fill_row(lds_char* buf, LDS_AS float* stab, const RawRow<KVM>& rr, int r, int q) {
+  const int sw = row_swz(r);
+  lds_char* rowp = buf + r * 128;
+  if constexpr (kv_fp8(KVM)) {
+    // codes 128k + 16q .. +15: column group 2k + q/4, chunks 2(q%4), 2(q%4)+1
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int c0 = 2 * (q & 3);
+      lds_char* gp = rowp + kGroupBytes * (2 * k + (q >> 2));
+      *(LDS_AS u32x4*)(gp + 16 * (c0 ^ sw)) = codes8(rr.code[k][0], rr.code[k][1]);
+      *(LDS_AS u32x4*)(gp + 16 * ((c0 + 1) ^ sw)) = codes8(rr.code[k][2], rr.code[k][3]);
+    }
+    // rope (bf16 as stored): column group 8, chunk q
+    *(LDS_AS u32x4*)(rowp + kGroupBytes * 8 + 16 * (q ^ sw)) = rr.rope;
+    if (q < 4) stab[q * kTS + r] = rr.scale[q];
+  } else {
+#pragma unroll
+    for (int k = 0; k < 9; ++k) *(LDS_AS u32x4*)(rowp + kGroupBytes * k + 16 * (q ^ sw)) = rr.v[k];
+  }
+}
+
 // ---------------------------------------------------------------- compute on one slot
 
 template <int NSPLIT>
@@ -356,40 +471,10 @@ struct SoftmaxState {
 // scheduling fences keep LDS reads and MFMAs in this order and let only
 // VALU work (the softmax of the previous slot) move between them.
 constexpr int kRA = 4;
+// What rides between the QK^T MFMAs of a step: the next slot's copies, the
+// previous slot's softmax, and (top-k) that softmax's validity mask.
+constexpr int kPipeDma = 1, kPipeSoft = 2, kPipeMask = 4;
 constexpr int kFenceValu = 0x2 | 0x400;  // sched_barrier mask: VALU and transcendental may cross
-
-template <int NSPLIT, int I, bool DMA>
-__device__ __forceinline__ void qk_steps(f32x16& s, bf16x8 (&kb)[kRA], const lds_char* buf,
-                                         const bf16x8 (&qf)[kKSteps / NSPLIT], const LaneTables& t,
-                                         const DmaJob& job) {
-  constexpr int KS = kKSteps / NSPLIT;
-  if constexpr (I < KS) {
-    __builtin_amdgcn_sched_barrier(kFenceValu);
-    s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kb[I % kRA], qf[I], s, 0, 0, 0);
-    if constexpr (I + kRA < KS)
-      kb[I % kRA] = *(const LDS_AS bf16x8*)(buf + t.kaddr[(I + kRA) & 3] + kGroupBytes * ((I + kRA) >> 2));
-    if constexpr (DMA) {
-      // the next slot's copies ride between the MFMAs, so that the wave
-      // never stalls on a full memory queue with nothing else to issue
-      constexpr int R = KS / kDmaPerWave;
-      if constexpr (I % R == R - 1) dma_issue<I / R>(job);
-    }
-    qk_steps<NSPLIT, I + 1, DMA>(s, kb, buf, qf, t, job);
-  }
-}
-
-template <int NSPLIT, bool DMA>
-__device__ __forceinline__ f32x16 qk_partial(const lds_char* buf, const bf16x8 (&qf)[kKSteps / NSPLIT],
-                                             const LaneTables& t, const DmaJob& job) {
-  static_assert((kKSteps / NSPLIT) % kDmaPerWave == 0, "copies spread evenly over the k-steps");
-  bf16x8 kb[kRA];
-#pragma unroll
-  for (int i = 0; i < kRA; ++i) kb[i] = *(const LDS_AS bf16x8*)(buf + t.kaddr[i & 3] + kGroupBytes * (i >> 2));
-  f32x16 s = {};
-  qk_steps<NSPLIT, 0, DMA>(s, kb, buf, qf, t, job);
-  __builtin_amdgcn_sched_barrier(kFenceValu);
-  return s;
-}
 
 // Publish this wave's partial: [wave][r4][lane] 16-byte rows, lane-contiguous.
 __device__ __forceinline__ void put_partial(LDS_AS f32x4* xch, const f32x16& s, int w, int lane) {
@@ -440,23 +525,187 @@ __device__ __forceinline__ float sum_halves(float v) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
+// Softmax of a full slot cut into 15 stages that ride between the QK^T
+// MFMAs of the next slot (one stage per MFMA for 18 k-steps, two for 9):
+// the exchange reads, the score sums, the max, eight pairs of exponentials
+// and the row sums.  The MFMA of each step runs on the
+// matrix core while its stage issues on the vector unit.
+struct SoftPipe {
+  uint32_t mask;    // valid tokens of the slot (top-k), bit t = token t
+  f32x16 own;       // this wave's partial S^T of the slot
+  f32x4 xr[4];      // partner's partial (two parts)
+  f32x16 x;         // full S^T
+  float mx, nref;
+  f32x8 p0, p1;
+  float lsum;
+};
+
+struct SoftCtx {
+  const LDS_AS f32x4* xch;
+  int w, lane;
+  float scale_log2;
+};
+
+// Scores of tokens whose bit in `mask` is clear become -inf.  Lane l,
+// register r holds token 8*(r/4) + 4*(l/32) + r%4.
+__device__ __forceinline__ void apply_mask(f32x16& x, uint32_t mask, int lane) {
+  const uint32_t mh = mask >> (4 * (lane >> 5));
+#pragma unroll
+  for (int r = 0; r < 16; ++r)
+    x[r] = (mh >> (8 * (r >> 2) + (r & 3))) & 1u ? x[r] : -INFINITY;
+}
+
+// p = 2^(x*scale - m_ref) with the reference's negation; while no valid token
+// has been seen (top-k slots of padding only) the reference is -inf and every
+// score is -inf too, which must give p = 0, not NaN.
+__device__ __forceinline__ float neg_ref(float m_ref) { return m_ref == -INFINITY ? 0.0f : -m_ref; }
+
+template <int NSPLIT, int ST, bool MASKED>
+__device__ __forceinline__ void soft_stage(SoftPipe& sp, SoftmaxState& st, const SoftCtx& c) {
+  if constexpr (ST == 0) {
+    if constexpr (NSPLIT == 2) {
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4) sp.xr[r4] = c.xch[((c.w ^ 1) * 4 + r4) * 64 + c.lane];
+    } else {
+      sp.x = total_scores<NSPLIT>(c.xch, sp.own, c.w, c.lane);
+    }
+  } else if constexpr (ST == 1 || ST == 2) {
+    if constexpr (NSPLIT == 2) {
+#pragma unroll
+      for (int r4 = 2 * (ST - 1); r4 < 2 * ST; ++r4)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) sp.x[4 * r4 + e] = sp.own[4 * r4 + e] + sp.xr[r4][e];
+    }
+  } else if constexpr (ST == 3) {
+    if constexpr (MASKED) apply_mask(sp.x, sp.mask, c.lane);
+    float m = sp.x[0];
+#pragma unroll
+    for (int r = 1; r < 16; ++r) m = fmaxf(m, sp.x[r]);
+    sp.mx = m;
+  } else if constexpr (ST == 4) {
+    const float mx = max_halves(sp.mx) * c.scale_log2;  // scale_log2 > 0: the max commutes with the scaling
+    st.m_ref = st.m_ref == -INFINITY ? mx : st.m_ref;
+    st.m_seen = fmaxf(st.m_seen, mx);
+    sp.nref = neg_ref(st.m_ref);
+  } else if constexpr (ST >= 5 && ST <= 12) {
+    constexpr int k = ST - 5;
+    sp.p0[k] = __builtin_amdgcn_exp2f(__builtin_fmaf(sp.x[k], c.scale_log2, sp.nref));
+    sp.p1[k] = __builtin_amdgcn_exp2f(__builtin_fmaf(sp.x[k + 8], c.scale_log2, sp.nref));
+  } else if constexpr (ST == 13) {
+    float l = 0.0f;
+#pragma unroll
+    for (int r = 0; r < 8; ++r) l += sp.p0[r];
+    sp.lsum = l;
+  } else if constexpr (ST == 14) {
+    float l = sp.lsum;
+#pragma unroll
+    for (int r = 0; r < 8; ++r) l += sp.p1[r];
+    st.l_sum += l;
+  }
+}
+
+constexpr int kSoftStages = 15;
+
+template <int NSPLIT, int ST0, int ST1, bool MASKED>
+__device__ __forceinline__ void soft_stages(SoftPipe& sp, SoftmaxState& st, const SoftCtx& c) {
+  if constexpr (ST0 < ST1 && ST0 < kSoftStages) {
+    soft_stage<NSPLIT, ST0, MASKED>(sp, st, c);
+    soft_stages<NSPLIT, ST0 + 1, ST1, MASKED>(sp, st, c);
+  }
+}
+
+template <int NSPLIT, bool TILED, int I>
+__device__ __forceinline__ uint32_t k_addr(const LaneTables& t) {
+  if constexpr (TILED && I >= Tiling<NSPLIT>::CS) return t.kaddr_r[I - Tiling<NSPLIT>::CS];
+  else return t.kaddr[I & 3] + kGroupBytes * (I >> 2);
+}
+
+// accumulators of the partial QK^T: one, or (tiled) one per code tile + rope;
+// arrays are sized for the largest case, unused entries cost nothing
+constexpr int kMaxAcc = 3;
+
+template <int NSPLIT, int I, int PIPE, bool TILED>
+__device__ __forceinline__ void qk_steps(f32x16 (&acc)[kMaxAcc], bf16x8 (&kb)[kRA],
+                                         const lds_char* buf, const bf16x8 (&qf)[kKSteps / NSPLIT],
+                                         const LaneTables& t, const DmaJob& job, SoftPipe& sp, SoftmaxState& st,
+                                         const SoftCtx& c) {
+  using T = Tiling<NSPLIT>;
+  constexpr int KS = T::KS;
+  if constexpr (I < KS) {
+    constexpr int ai = TILED ? (I < T::CS ? I / 8 : T::TPP) : 0;
+    constexpr bool first = TILED ? (I < T::CS ? I % 8 == 0 : I == T::CS) : I == 0;
+    __builtin_amdgcn_sched_barrier(0);
+    acc[ai] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kb[I % kRA], qf[I], first ? f32x16{} : acc[ai], 0, 0, 0);
+    if constexpr (I + kRA < KS) kb[I % kRA] = *(const LDS_AS bf16x8*)(buf + k_addr<NSPLIT, TILED, I + kRA>(t));
+    if constexpr ((PIPE & kPipeDma) != 0) {
+      // the next slot's copies ride between the MFMAs, so that the wave
+      // never stalls on a full memory queue with nothing else to issue
+      constexpr int R = KS / kDmaPerWave;
+      if constexpr (I % R == R - 1) dma_issue<I / R>(job);
+    }
+    if constexpr ((PIPE & kPipeSoft) != 0) {
+      // and so does the softmax of the previous slot
+      constexpr int SPS = (kSoftStages + KS - 1) / KS;  // stages per step
+      soft_stages<NSPLIT, I * SPS, (I + 1) * SPS, (PIPE & kPipeMask) != 0>(sp, st, c);
+    }
+    qk_steps<NSPLIT, I + 1, PIPE, TILED>(acc, kb, buf, qf, t, job, sp, st, c);
+  }
+}
+
+// Per-token scales of code tile `tile` for the 16 tokens this lane holds in
+// an S^T or P^T fragment (register r: token 8*(r/4) + 4*(l/32) + r%4), from a
+// slot's scale table [tile][token] in LDS.
+__device__ __forceinline__ f32x16 tile_scales(const LDS_AS float* tab, int tile, int lane) {
+  const LDS_AS f32x4* p = (const LDS_AS f32x4*)(tab + tile * kTS + 4 * (lane >> 5));
+  f32x16 s;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const f32x4 v = p[2 * k];  // tokens 8k + 4*(l/32) .. +3
+#pragma unroll
+    for (int e = 0; e < 4; ++e) s[4 * k + e] = v[e];
+  }
+  return s;
+}
+
+// Partial QK^T of one slot; with PIPE the next slot's copies and the
+// previous slot's softmax are interleaved with it.  Tiled: the tile
+// accumulators are scaled per token (scale table `stab` of the slot) and
+// added to the rope accumulator, in fp32.
+template <int NSPLIT, int PIPE, bool TILED = false>
+__device__ __forceinline__ f32x16 qk_partial(const lds_char* buf, const bf16x8 (&qf)[kKSteps / NSPLIT],
+                                             const LaneTables& t, const DmaJob& job, SoftPipe& sp, SoftmaxState& st,
+                                             const SoftCtx& c, const LDS_AS float* stab = nullptr, int part = 0) {
+  static_assert((kKSteps / NSPLIT) % kDmaPerWave == 0, "copies spread evenly over the k-steps");
+  bf16x8 kb[kRA];
+  kb[0] = *(const LDS_AS bf16x8*)(buf + k_addr<NSPLIT, TILED, 0>(t));
+  kb[1] = *(const LDS_AS bf16x8*)(buf + k_addr<NSPLIT, TILED, 1>(t));
+  kb[2] = *(const LDS_AS bf16x8*)(buf + k_addr<NSPLIT, TILED, 2>(t));
+  kb[3] = *(const LDS_AS bf16x8*)(buf + k_addr<NSPLIT, TILED, 3>(t));
+  f32x16 acc[kMaxAcc];
+  qk_steps<NSPLIT, 0, PIPE, TILED>(acc, kb, buf, qf, t, job, sp, st, c);
+  __builtin_amdgcn_sched_barrier(0);
+  if constexpr (TILED) {
+    constexpr int TPP = Tiling<NSPLIT>::TPP;
+    f32x16 s = acc[TPP];
+#pragma unroll
+    for (int j = 0; j < TPP; ++j) {
+      const f32x16 sc = tile_scales(stab, TPP * part + j, c.lane);
+#pragma unroll
+      for (int r = 0; r < 16; ++r) s[r] = __builtin_fmaf(sc[r], acc[j][r], s[r]);
+    }
+    return s;
+  } else {
+    return acc[0];
+  }
+}
+
 // Softmax numerators of one slot as bf16 P^T operands.  Lane l, register r
 // holds token 8*(r/4) + 4*(l/32) + r%4 of head l%32; tokens at and beyond
 // nvalid (only the last slot of a segment has any) get p = 0.
-template <bool MASK>
-__device__ __forceinline__ void softmax_slot(const f32x16& s, int nvalid, SoftmaxState& st, float scale_log2,
-                                             bf16x8& pb0, bf16x8& pb1, int lane) {
-  float x[16];
-  const int hi = lane >> 5;
-#pragma unroll
-  for (int r = 0; r < 16; ++r) {
-    if constexpr (MASK) {
-      const int m = 8 * (r >> 2) + 4 * hi + (r & 3);
-      x[r] = m < nvalid ? s[r] : -INFINITY;
-    } else {
-      x[r] = s[r];
-    }
-  }
+__device__ __forceinline__ void softmax_slot(const f32x16& s, uint32_t mask, SoftmaxState& st, float scale_log2,
+                                             f32x8& p0, f32x8& p1, int lane) {
+  f32x16 x = s;
+  apply_mask(x, mask, lane);
   float mx = x[0];
 #pragma unroll
   for (int r = 1; r < 16; ++r) mx = fmaxf(mx, x[r]);
@@ -465,8 +714,7 @@ __device__ __forceinline__ void softmax_slot(const f32x16& s, int nvalid, Softma
   // kTau without loss (p <= 2^kTau), beyond that the segment is redone
   st.m_ref = st.m_ref == -INFINITY ? mx : st.m_ref;
   st.m_seen = fmaxf(st.m_seen, mx);
-  const float nref = -st.m_ref;
-  f32x8 p0, p1;
+  const float nref = neg_ref(st.m_ref);
 #pragma unroll
   for (int r = 0; r < 8; ++r) {
     p0[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(x[r], scale_log2, nref));
@@ -476,17 +724,48 @@ __device__ __forceinline__ void softmax_slot(const f32x16& s, int nvalid, Softma
 #pragma unroll
   for (int r = 0; r < 8; ++r) lsum += p0[r] + p1[r];
   st.l_sum += lsum;
-  pb0 = __builtin_convertvector(p0, bf16x8);
-  pb1 = __builtin_convertvector(p1, bf16x8);
 }
+
+// P^T operands of the PV product: the numerators as bf16; tiled (FP8 cache),
+// once per code tile of this part with each token's tile scale folded in, so
+// that the codes themselves serve as V: sum_t p_t (code_t,c * s_t,tile(c)).
+template <int NSPLIT, bool TILED>
+struct POps {
+  static constexpr int N = TILED ? Tiling<NSPLIT>::TPP : 1;
+  bf16x8 b0[N], b1[N];
+};
+
+template <int NSPLIT, bool TILED>
+__device__ __forceinline__ void make_pops(POps<NSPLIT, TILED>& po, const f32x8& p0, const f32x8& p1,
+                                          const LDS_AS float* stab, int part, int lane) {
+  if constexpr (TILED) {
+#pragma unroll
+    for (int j = 0; j < POps<NSPLIT, TILED>::N; ++j) {
+      const f32x16 sc = tile_scales(stab, POps<NSPLIT, TILED>::N * part + j, lane);
+      f32x8 a, b;
+#pragma unroll
+      for (int r = 0; r < 8; ++r) {
+        a[r] = p0[r] * sc[r];
+        b[r] = p1[r] * sc[r + 8];
+      }
+      po.b0[j] = __builtin_convertvector(a, bf16x8);
+      po.b1[j] = __builtin_convertvector(b, bf16x8);
+    }
+  } else {
+    po.b0[0] = __builtin_convertvector(p0, bf16x8);
+    po.b1[0] = __builtin_convertvector(p1, bf16x8);
+  }
+}
+
 
 // O^T[c][head] += V^T . P^T over this wave's column blocks.  k-step 0 of a
 // block covers tokens 0..15 in the order the S^T layout hands them to this
 // lane (rows 4h+j and 8+4h+j), k-step 1 tokens 16..31.
-template <int NSPLIT>
-__device__ __forceinline__ void pv_slot(const lds_char* buf, const bf16x8& pb0, const bf16x8& pb1,
-                                        const LaneTables& t, Acc<NSPLIT>& acc) {
+template <int NSPLIT, bool TILED>
+__device__ __forceinline__ void pv_slot(const lds_char* buf, const POps<NSPLIT, TILED>& po, const LaneTables& t,
+                                        Acc<NSPLIT>& acc) {
   constexpr int NCB = kCB / NSPLIT;
+  constexpr int BPS = NCB / POps<NSPLIT, TILED>::N;  // column blocks per operand set
   const lds_char* b0 = buf + t.vaddr[0];
   const lds_char* b1 = buf + t.vaddr[1];
   const lds_char* b0x = buf + (t.vaddr[0] ^ 64u);
@@ -509,16 +788,21 @@ __device__ __forceinline__ void pv_slot(const lds_char* buf, const bf16x8& pb0, 
     const bf16x4(&v)[4] = va[cb & 1];
     const bf16x8 v0 = __builtin_shufflevector(v[0], v[1], 0, 1, 2, 3, 4, 5, 6, 7);
     const bf16x8 v1 = __builtin_shufflevector(v[2], v[3], 0, 1, 2, 3, 4, 5, 6, 7);
-    acc.o[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(v0, pb0, acc.o[cb], 0, 0, 0);
-    acc.o[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(v1, pb1, acc.o[cb], 0, 0, 0);
+    acc.o[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(v0, po.b0[cb / BPS], acc.o[cb], 0, 0, 0);
+    acc.o[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(v1, po.b1[cb / BPS], acc.o[cb], 0, 0, 0);
   }
   __builtin_amdgcn_sched_barrier(0);
 }
 
 struct SegCtx {
-  const int32_t* bt_seg;  // block-table entries of the segment's pages
+  const int32_t* bt_seg;     // block-table entries of the segment's pages
+  const int32_t* rows_seg;   // top-k: physical row of each entry (-1: masked) from tok0 on
+  const uint32_t* mask_seg;  // top-k: validity word of each 32-entry slot from tok0 on
   int tok0, tok1, nslots, npages;
 };
+
+// mask of the tokens [0, n) of a slot
+__device__ __forceinline__ uint32_t low_mask(int n) { return n >= 32 ? 0xffffffffu : (1u << n) - 1u; }
 
 // DMA job that fills ring position pos with slot s of the segment.  Slots at
 // or beyond the end are replaced by the last slot: the copy then lands in a
@@ -540,9 +824,9 @@ __device__ __forceinline__ DmaJob prep_slot(int s, int pos, lds_char* ring, cons
 
 // ---------------------------------------------------------------- the kernel
 
-template <int NSPLIT, bool Q_FP8>
+template <int NSPLIT, bool Q_FP8, int KVM>
 __global__ void __launch_bounds__(kThreads, 1) __attribute__((amdgpu_waves_per_eu(1, 1)))
-mla_decode_bf16_kernel(DecodeArgs a) {
+mla_decode_kernel(DecodeArgs a) {
   __shared__ __attribute__((aligned(1024))) char ring_mem[kRing * kSlotBytes];  // KV ring, 4 x 36 KB
   __shared__ __attribute__((aligned(16))) f32x4 xbuf[kWaves * 4 * 64];         // partial S^T, 16 KB
   lds_char* const ring = (lds_char*)ring_mem;
@@ -554,6 +838,7 @@ mla_decode_bf16_kernel(DecodeArgs a) {
   constexpr int KS = kKSteps / NSPLIT;
   constexpr int NCB = kCB / NSPLIT;
   constexpr int HG = kWaves / NSPLIT;  // 32-head groups per workgroup
+  constexpr bool TILED = kv_fp8(KVM);  // FP8 cache: tiled QK^T split, scales applied in fp32
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -584,7 +869,7 @@ mla_decode_bf16_kernel(DecodeArgs a) {
   const bool head_ok = head < a.heads;
 
   LaneTables tab;
-  make_tables<NSPLIT>(tab, lane, w, part);
+  make_tables<NSPLIT, TILED>(tab, lane, w, part);
 
   int b = pl.b0, p = pl.p0;
   bool first_seg = true;
@@ -599,33 +884,35 @@ mla_decode_bf16_kernel(DecodeArgs a) {
         barrier();
       }
       first_seg = false;
-      const int seqlen = min(max(a.seqlens[b], 0), a.max_pages * kPage);
+      // tokens of the sequence: positions [0, seqlen), or top-k entries [0, topk)
+      const int seglen = kv_topk(KVM) ? a.topk : min(max(a.seqlens[b], 0), a.max_pages * kPage);
       SegCtx sg;
       sg.tok0 = (gs - p) * kPage;
-      sg.tok1 = min((ge - p) * kPage, seqlen);
+      sg.tok1 = min((ge - p) * kPage, seglen);
       sg.nslots = (sg.tok1 - sg.tok0 + kTS - 1) / kTS;
       sg.npages = (sg.nslots + 1) / 2;
       sg.bt_seg = a.block_table + (size_t)b * a.max_pages + (gs - p);
+      sg.rows_seg = a.ws_rows + (size_t)b * a.topk + sg.tok0;
+      sg.mask_seg = a.ws_masks + (size_t)b * a.mask_words + sg.tok0 / kTS;
       const int first_r = p / pl.C, last_r = (p + n - 1) / pl.C;
       const int nsplit = last_r - first_r + 1;
-      const int last_valid = sg.tok1 - (sg.tok0 + (sg.nslots - 1) * kTS);
       const int nslots = sg.nslots;
 
       // query fragments (B operand of S^T = K.Q^T): head `head`, columns
-      // 16*(part*KS + i) + 8*(lane/32) .. +7 for this wave's k-steps
+      // 16g + 8*(lane/32) .. +7 for global k-step g of this wave's local step i
       bf16x8 qf[KS];
       if constexpr (!Q_FP8) {
         const bf16x8* qrow = (const bf16x8*)((const __bf16*)a.q + ((size_t)b * a.heads + (head_ok ? head : 0)) * kD);
 #pragma unroll
         for (int i = 0; i < KS; ++i) {
-          const bf16x8 v = qrow[2 * (part * KS + i) + (lane >> 5)];
+          const bf16x8 v = qrow[2 * global_step<NSPLIT, TILED>(part, i) + (lane >> 5)];
           qf[i] = head_ok ? v : bf16x8{};
         }
       } else {
         const uint2* qrow = (const uint2*)((const uint8_t*)a.q + ((size_t)b * a.heads + (head_ok ? head : 0)) * kD);
 #pragma unroll
         for (int i = 0; i < KS; ++i) {
-          const uint2 v = qrow[2 * (part * KS + i) + (lane >> 5)];
+          const uint2 v = qrow[2 * global_step<NSPLIT, TILED>(part, i) + (lane >> 5)];
           qf[i] = head_ok ? fp8x8_to_bf16(v, a.q_descale) : bf16x8{};
         }
       }
@@ -633,7 +920,29 @@ mla_decode_bf16_kernel(DecodeArgs a) {
       PageCache pc;
       // (also completes the query loads, so the ring's vmcnt accounting
       // counts DMA only)
-      page_cache_load(pc, sg.bt_seg, 0, sg.npages, lane);
+      if constexpr (!kv_topk(KVM)) page_cache_load(pc, sg.bt_seg, 0, sg.npages, lane);
+      // register fill: this lane's row of a slot and its 128-byte piece
+      const int frow = 8 * w + (lane & 7), fq = lane >> 3;
+      // physical row that this lane fills for slot t of the segment (slots
+      // past the end repeat the last one; rows past the valid count repeat
+      // the last valid row; masked top-k entries read row 0)
+      auto fill_src = [&](int t) -> int {
+        t = min(t, nslots - 1);
+        if constexpr (kv_topk(KVM)) {
+          const int e = t * kTS + frow;
+          const int rw = sg.tok0 + e < sg.tok1 ? sg.rows_seg[e] : -1;
+          return rw < 0 ? 0 : rw;
+        } else {
+          const int page = page_of(pc, sg.bt_seg, t >> 1, sg.npages, lane, a.num_pages);
+          const int nv = min(kTS, sg.tok1 - (sg.tok0 + t * kTS));
+          return page * kPage + (t & 1) * kTS + min(frow, nv - 1);
+        }
+      };
+      // validity of the tokens of slot s (dense: only the last slot is short)
+      auto slot_mask = [&](int s) -> uint32_t {
+        if constexpr (kv_topk(KVM)) return __builtin_amdgcn_readfirstlane(sg.mask_seg[s]);
+        else return low_mask(sg.tok1 - (sg.tok0 + s * kTS));
+      };
 
       SoftmaxState st;
       st.m_ref = -INFINITY;
@@ -646,40 +955,99 @@ mla_decode_bf16_kernel(DecodeArgs a) {
         for (int c = 0; c < NCB; ++c) acc.o[c] = f32x16{};
         st.l_sum = 0.0f;
         st.m_seen = -INFINITY;
-        // prologue: slots 0..2 in flight (slots past the end re-copy the
-        // last one), partial QK^T of slot 0
+        const SoftCtx sctx{xch, w, lane, a.scale_log2};
+        SoftPipe sp;
+        POps<NSPLIT, TILED> po;
+        f32x16 sc;
+        int last_pos;  // ring position of the last slot
+        if constexpr (KVM == kKvBf16) {
+          // prologue: slots 0..2 in flight (slots past the end re-copy the
+          // last one), partial QK^T of slot 0
 #pragma unroll
-        for (int s = 0; s < 3; ++s) dma_issue_all(prep_slot(s, s, ring, a, sg, pc, tab, w, lane));
-        wait_vm_lgkm0<2 * kDmaPerWave>();
-        barrier();
-        f32x16 sc = qk_partial<NSPLIT, false>(ring, qf, tab, DmaJob{});
-        bf16x8 pb0, pb1;
-        // steady state, slot s: publish its partial (computed one step
-        // earlier) and wait for slot s+1 (slot s+2 stays in flight);
-        // barrier; then the partial QK^T of slot s+1 runs beside the softmax
-        // of slot s with the copies of slot s+3 (into the ring position that
-        // slot s-1 left) between its MFMAs, then PV of slot s; a second
-        // barrier frees ring position s and the exchange buffer
-        for (int s = 0; s + 1 < nslots; ++s) {
-          put_partial(xch, sc, w, lane);
-          wait_vm_lgkm0<kDmaPerWave>();
+          for (int s = 0; s < 3; ++s) dma_issue_all(prep_slot(s, s, ring, a, sg, pc, tab, w, lane));
+          wait_vm_lgkm0<2 * kDmaPerWave>();
           barrier();
-          const f32x16 tot = total_scores<NSPLIT>(xch, sc, w, lane);
-          const DmaJob job = prep_slot(s + 3, s + 3, ring, a, sg, pc, tab, w, lane);
-          sc = qk_partial<NSPLIT, true>(ring + ((s + 1) & (kRing - 1)) * kSlotBytes, qf, tab, job);
-          softmax_slot<false>(tot, kTS, st, a.scale_log2, pb0, pb1, lane);
-          pv_slot<NSPLIT>(ring + (s & (kRing - 1)) * kSlotBytes, pb0, pb1, tab, acc);
-          wait_vm_lgkm0<63>();  // lgkmcnt(0): this wave's LDS reads are done
-          barrier();
-        }
-        {
-          // last slot (the only one that can be partial)
+          sc = qk_partial<NSPLIT, 0>(ring, qf, tab, DmaJob{}, sp, st, sctx);
+          // steady state, slot s: publish its partial (computed one step
+          // earlier) and wait for slot s+1 (slot s+2 stays in flight);
+          // barrier; then the partial QK^T of slot s+1 runs beside the
+          // softmax of slot s with the copies of slot s+3 (into the ring
+          // position that slot s-1 left) between its MFMAs, then PV of slot
+          // s; a second barrier frees ring position s and the exchange buffer
+          for (int s = 0; s + 1 < nslots; ++s) {
+            put_partial(xch, sc, w, lane);
+            wait_vm_lgkm0<kDmaPerWave>();
+            barrier();
+            const DmaJob job = prep_slot(s + 3, s + 3, ring, a, sg, pc, tab, w, lane);
+            sp.own = sc;
+            sc = qk_partial<NSPLIT, kPipeDma | kPipeSoft>(ring + ((s + 1) & (kRing - 1)) * kSlotBytes, qf, tab, job,
+                                                          sp, st, sctx);
+            make_pops<NSPLIT, TILED>(po, sp.p0, sp.p1, nullptr, part, lane);
+            pv_slot<NSPLIT, TILED>(ring + (s & (kRing - 1)) * kSlotBytes, po, tab, acc);
+            wait_vm_lgkm0<63>();  // lgkmcnt(0): this wave's LDS reads are done
+            barrier();
+          }
           put_partial(xch, sc, w, lane);
           wait_vm_lgkm0<0>();
+          last_pos = (nslots - 1) & (kRing - 1);
+        } else {
+          // register fill through a ring of three positions (slot s at
+          // position s % 3); the fourth slot region holds the FP8 scale
+          // tables, one per position.  Prologue: slots 0 and 1 written,
+          // slot 2 loaded, partial QK^T of slot 0.
+          LDS_AS float* const stabs = (LDS_AS float*)(ring + kFillRing * kSlotBytes);
+          auto pos_buf = [&](int pos) { return ring + pos * kSlotBytes; };
+          auto pos_tab = [&](int pos) { return stabs + pos * (4 * kTS); };
+          RawRow<KVM> rr;
+          load_row<KVM>(rr, a, fill_src(0), fq);
+          fill_row<KVM>(pos_buf(0), pos_tab(0), rr, frow, fq);
+          load_row<KVM>(rr, a, fill_src(1), fq);
+          fill_row<KVM>(pos_buf(1), pos_tab(1), rr, frow, fq);
+          load_row<KVM>(rr, a, fill_src(2), fq);
+          wait_vm_lgkm0<63>();
+          barrier();
+          sc = qk_partial<NSPLIT, 0, TILED>(pos_buf(0), qf, tab, DmaJob{}, sp, st, sctx, pos_tab(0), part);
+          // steady state, slot s: as above, with no copies in the QK^T; after
+          // PV of slot s the lanes write slot s+2 (loaded one step earlier)
+          // into the position that slot s-1 left and load slot s+3
+          int p0 = 0, p1 = 1, p2 = 2;  // positions of slots s, s+1, s+2
+          for (int s = 0; s + 1 < nslots; ++s) {
+            put_partial(xch, sc, w, lane);
+            wait_vm_lgkm0<63>();
+            barrier();
+            sp.own = sc;
+            if constexpr (kv_topk(KVM)) {
+              sp.mask = slot_mask(s);
+              sc = qk_partial<NSPLIT, kPipeSoft | kPipeMask, TILED>(pos_buf(p1), qf, tab, DmaJob{}, sp, st, sctx,
+                                                                   pos_tab(p1), part);
+            } else {
+              sc = qk_partial<NSPLIT, kPipeSoft, TILED>(pos_buf(p1), qf, tab, DmaJob{}, sp, st, sctx, pos_tab(p1),
+                                                        part);
+            }
+            make_pops<NSPLIT, TILED>(po, sp.p0, sp.p1, pos_tab(p0), part, lane);
+            pv_slot<NSPLIT, TILED>(pos_buf(p0), po, tab, acc);
+            fill_row<KVM>(pos_buf(p2), pos_tab(p2), rr, frow, fq);
+            load_row<KVM>(rr, a, fill_src(s + 3), fq);
+            wait_vm_lgkm0<63>();  // this wave's LDS reads and writes are done
+            barrier();
+            const int pn = p0;
+            p0 = p1;
+            p1 = p2;
+            p2 = pn;
+          }
+          put_partial(xch, sc, w, lane);
+          wait_vm_lgkm0<63>();
+          last_pos = p0;
+        }
+        {
+          // last slot (the only dense one that can be short)
           barrier();
           const f32x16 tot = total_scores<NSPLIT>(xch, sc, w, lane);
-          softmax_slot<true>(tot, last_valid, st, a.scale_log2, pb0, pb1, lane);
-          pv_slot<NSPLIT>(ring + ((nslots - 1) & (kRing - 1)) * kSlotBytes, pb0, pb1, tab, acc);
+          f32x8 q0, q1;
+          softmax_slot(tot, slot_mask(nslots - 1), st, a.scale_log2, q0, q1, lane);
+          const LDS_AS float* ltab = (const LDS_AS float*)(ring + kFillRing * kSlotBytes) + last_pos * (4 * kTS);
+          make_pops<NSPLIT, TILED>(po, q0, q1, ltab, part, lane);
+          pv_slot<NSPLIT, TILED>(ring + last_pos * kSlotBytes, po, tab, acc);
         }
         // workgroup vote on a redo (every wave is past its last exchange read)
         wait_vm_lgkm0<0>();
@@ -695,7 +1063,7 @@ mla_decode_bf16_kernel(DecodeArgs a) {
         barrier();  // votes read before the buffer is reused
         if (!__builtin_amdgcn_readfirstlane(vote)) break;
         st.m_ref = st.m_seen;
-        if (sg.npages > 64) page_cache_load(pc, sg.bt_seg, 0, sg.npages, lane);
+        if (!kv_topk(KVM) && sg.npages > 64) page_cache_load(pc, sg.bt_seg, 0, sg.npages, lane);
       }
 
       // ---- epilogue: normalise and store this wave's columns (final output,
@@ -789,6 +1157,40 @@ __global__ void __launch_bounds__(kThreads) mla_merge_kernel(MergeArgs m) {
   if (sub == 0) m.lse[(size_t)b * m.heads + head] = wsum > 0.0f ? (mx + __builtin_amdgcn_logf(wsum)) * kLn2 : -INFINITY;
 }
 
+// ---------------------------------------------------------------- top-k rows
+
+struct TopkArgs {
+  const int32_t* topk_idx;  // [B][topk] logical positions
+  const int32_t* block_table;
+  const int32_t* seqlens;
+  int32_t* rows;     // [B][topk] physical row, -1 for a masked entry
+  uint32_t* masks;   // [B][mask_words] validity bits per 32-entry slot
+  int32_t topk, mask_words, max_pages, num_pages;
+};
+
+// Translate every top-k entry of sequence blockIdx.y: logical position j is
+// valid iff 0 <= j < seqlen, and lives in row block_table[b][j / 64]*64 +
+// j % 64 (integer arithmetic, exact).  One thread per entry.
+__global__ void __launch_bounds__(kThreads) mla_topk_rows_kernel(TopkArgs t) {
+  const int b = blockIdx.y;
+  const int k = blockIdx.x * kThreads + threadIdx.x;
+  bool valid = false;
+  if (k < t.topk) {
+    const int j = t.topk_idx[(size_t)b * t.topk + k];
+    const int seqlen = min(max(t.seqlens[b], 0), t.max_pages * kPage);
+    int row = -1;
+    if (j >= 0 && j < seqlen) {
+      valid = true;
+      row = clamp_page(t.block_table[(size_t)b * t.max_pages + (j >> 6)], t.num_pages) * kPage + (j & (kPage - 1));
+    }
+    t.rows[(size_t)b * t.topk + k] = row;
+  }
+  const uint64_t bits = __ballot(valid);
+  const int word = k / kTS;
+  if ((threadIdx.x & (kTS - 1)) == 0 && word < t.mask_words)
+    t.masks[(size_t)b * t.mask_words + word] = (uint32_t)(bits >> (threadIdx.x & 32));
+}
+
 int nsplit_for_heads(int heads) { return heads > 32 ? 2 : 4; }
 int heads_per_slab(int heads) { return 32 * (kWaves / nsplit_for_heads(heads)); }
 int slabs_for_heads(int heads) { return (heads + heads_per_slab(heads) - 1) / heads_per_slab(heads); }
@@ -809,11 +1211,17 @@ int32_t decode_ranges(int32_t cus, int32_t batch, int32_t max_pages, int32_t top
   return (int32_t)r;
 }
 
-// Workspace: [B] int2 piece records | [(ranges + B)][H] fp32 LSE | [(ranges + B)][H][512] fp32 O.
-size_t decode_workspace_bytes(int32_t ranges, int32_t batch, int32_t heads) {
+int32_t mask_words_for(int32_t topk) { return (topk + kTS - 1) / kTS; }
+
+// Workspace: [B] int2 piece records | [(ranges + B)][H] fp32 LSE | [(ranges + B)][H][512] fp32 O
+// | top-k only: [B][topk] int32 rows | [B][ceil(topk / 32)] uint32 masks.
+size_t decode_workspace_bytes(int32_t ranges, int32_t batch, int32_t heads, int32_t topk) {
   const size_t slots = (size_t)ranges + (size_t)batch;
-  return align256(sizeof(int2) * (size_t)batch) + align256(sizeof(float) * slots * heads) +
-         align256(sizeof(float) * slots * heads * kDV);
+  size_t n = align256(sizeof(int2) * (size_t)batch) + align256(sizeof(float) * slots * heads) +
+             align256(sizeof(float) * slots * heads * kDV);
+  if (topk > 0)
+    n += align256(sizeof(int32_t) * (size_t)batch * topk) + align256(sizeof(uint32_t) * (size_t)batch * mask_words_for(topk));
+  return n;
 }
 
 // Every decode call rewrites all the state it reads back, so a workspace
@@ -844,6 +1252,13 @@ hipError_t launch_decode(const DecodeLaunch& d, hipStream_t stream) {
   a.ws_lse = (float*)ws;
   ws += align256(sizeof(float) * slots * d.heads);
   a.ws_o = (float*)ws;
+  ws += align256(sizeof(float) * slots * d.heads * kDV);
+  a.mask_words = mask_words_for(d.topk);
+  int32_t* ws_rows = (int32_t*)ws;
+  ws += d.topk > 0 ? align256(sizeof(int32_t) * (size_t)d.batch * d.topk) : 0;
+  uint32_t* ws_masks = (uint32_t*)ws;
+  a.ws_rows = ws_rows;
+  a.ws_masks = ws_masks;
   a.batch = d.batch;
   a.heads = d.heads;
   a.num_pages = d.num_pages;
@@ -854,15 +1269,40 @@ hipError_t launch_decode(const DecodeLaunch& d, hipStream_t stream) {
   a.scale_log2 = d.softmax_scale * kLog2e;
   a.q_descale = d.q_descale;
 
-  if (d.kv_fp8 || d.topk > 0) return hipErrorNotSupported;
-  const dim3 grid(a.per_xcd * 8 * a.slabs), block(kThreads);
-  if (nsplit_for_heads(d.heads) == 2) {
-    if (d.q_fp8) hipLaunchKernelGGL((mla_decode_bf16_kernel<2, true>), grid, block, 0, stream, a);
-    else hipLaunchKernelGGL((mla_decode_bf16_kernel<2, false>), grid, block, 0, stream, a);
-  } else {
-    if (d.q_fp8) hipLaunchKernelGGL((mla_decode_bf16_kernel<4, true>), grid, block, 0, stream, a);
-    else hipLaunchKernelGGL((mla_decode_bf16_kernel<4, false>), grid, block, 0, stream, a);
+  if (d.topk > 0) {
+    TopkArgs t;
+    t.topk_idx = d.topk_idx;
+    t.block_table = d.block_table;
+    t.seqlens = d.seqlens;
+    t.rows = ws_rows;
+    t.masks = ws_masks;
+    t.topk = d.topk;
+    t.mask_words = a.mask_words;
+    t.max_pages = d.max_pages;
+    t.num_pages = d.num_pages;
+    hipLaunchKernelGGL(mla_topk_rows_kernel, dim3((d.topk + kThreads - 1) / kThreads, d.batch), dim3(kThreads), 0,
+                       stream, t);
+    const hipError_t e0 = hipGetLastError();
+    if (e0 != hipSuccess) return e0;
   }
+  const int kvm = d.topk > 0 ? (d.kv_fp8 ? kKvFp8TopK : kKvBf16TopK) : (d.kv_fp8 ? kKvFp8 : kKvBf16);
+  const dim3 grid(a.per_xcd * 8 * a.slabs), block(kThreads);
+  const int ns = nsplit_for_heads(d.heads);
+  // one instantiation per (split, query format, cache layout)
+#define MLA_LAUNCH(NS, QF, KVM)                                                           \
+  if (ns == NS && d.q_fp8 == QF && kvm == KVM)                                           \
+    hipLaunchKernelGGL((mla_decode_kernel<NS, QF, KVM>), grid, block, 0, stream, a);
+#define MLA_LAUNCH_KV(NS, QF)  \
+  MLA_LAUNCH(NS, QF, kKvBf16)     \
+  MLA_LAUNCH(NS, QF, kKvFp8)      \
+  MLA_LAUNCH(NS, QF, kKvFp8TopK)  \
+  MLA_LAUNCH(NS, QF, kKvBf16TopK)
+  MLA_LAUNCH_KV(2, false)
+  MLA_LAUNCH_KV(2, true)
+  MLA_LAUNCH_KV(4, false)
+  MLA_LAUNCH_KV(4, true)
+#undef MLA_LAUNCH_KV
+#undef MLA_LAUNCH
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   MergeArgs m;

@@ -28,8 +28,8 @@ struct DecodeLaunch {
 // KV ranges for a device with `cus` compute units.
 int32_t decode_ranges(int32_t cus, int32_t batch, int32_t max_pages, int32_t topk, int32_t heads);
 // Workspace bytes for a decode launch with `ranges` KV ranges.
-size_t decode_workspace_bytes(int32_t ranges, int32_t batch, int32_t heads);
-// Zero the counter area that the decode kernel expects zero between calls.
+size_t decode_workspace_bytes(int32_t ranges, int32_t batch, int32_t heads, int32_t topk);
+// Clear the per-sequence piece records of a decode workspace (optional: every call rewrites them).
 hipError_t init_decode_workspace(void* workspace, int32_t batch, int32_t heads, hipStream_t stream);
 hipError_t launch_decode(const DecodeLaunch& d, hipStream_t stream);
 

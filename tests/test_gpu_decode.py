@@ -94,6 +94,21 @@ CASES = {
     "one_long_seq": dict(seed=19, batch=1, heads=128, seqlens=[20000]),
     "with_empty_seqs": dict(seed=20, batch=5, heads=64, seqlens=[0, 77, 0, 300, 0], pages_per_seq=5),
     "exact_pages": dict(seed=21, batch=3, heads=128, seqlens=[64, 128, 4096]),
+    # FP8 cache: e4m3 codes with one fp32 scale per row and 128-column tile
+    "fp8_h128_ragged": dict(seed=71, batch=3, heads=128, seqlens=[1, 300, 2100], kv_format="fp8"),
+    "fp8_h64_ragged": dict(seed=72, batch=5, heads=64, seqlen_range=(1, 1500), kv_format="fp8"),
+    "fp8_h32_ragged": dict(seed=73, batch=4, heads=32, seqlen_range=(30, 900), kv_format="fp8"),
+    "fp8_h8_fp8q": dict(seed=74, batch=6, heads=8, seqlen_range=(100, 1300), kv_format="fp8", q_format="fp8",
+                        q_descale=8.0),
+    "fp8_with_empty_seqs": dict(seed=75, batch=4, heads=64, seqlens=[0, 500, 0, 65], pages_per_seq=8,
+                                kv_format="fp8"),
+    # top-k: sorted distinct positions, trailing -1 padding
+    "topk_fp8_h128": dict(seed=81, batch=3, heads=128, seqlens=[3000, 5000, 100], kv_format="fp8", topk=512,
+                          topk_pad_max=100),
+    "topk_fp8_h64": dict(seed=82, batch=4, heads=64, seqlen_range=(200, 4000), kv_format="fp8", topk=1000),
+    "topk_fp8_h16": dict(seed=83, batch=3, heads=16, seqlen_range=(50, 3000), kv_format="fp8", topk=300),
+    "topk_bf16_h64": dict(seed=84, batch=3, heads=64, seqlen_range=(500, 3000), topk=700),
+    "topk_bf16_h128": dict(seed=85, batch=2, heads=128, seqlens=[4000, 33], topk=256, topk_pad_max=40),
 }
 
 
@@ -124,6 +139,21 @@ def test_running_max_jumps(heads):
     compare(inp, out, lse, rtol=2.0**-7, scale=abs_weighted_v(inp))
 
 
+def test_topk_masking_rules():
+    """Entries that are -1, negative, or at/after seqlen contribute nothing; a
+    sequence whose entries are all masked gets O = 0 and LSE = -inf."""
+    inp = synth.make_decode_inputs(91, batch=3, heads=64, seqlens=[700, 1200, 900], kv_format="fp8", topk=400)
+    t = inp["topk_idx"]
+    t[0, ::7] = -1
+    t[0, 1::11] = 700 + np.arange(len(t[0, 1::11]), dtype=np.int32)  # at and past seqlen
+    t[1, ::5] = -3
+    t[2, :] = -1  # nothing to attend
+    _say("[decode top-k masking]")
+    out, lse = run_gpu(inp)
+    compare(inp, out, lse)
+    assert torch.all(out[2].float() == 0) and torch.all(torch.isneginf(lse[2]))
+
+
 def test_outputs_fully_written_and_deterministic():
     inp = synth.make_decode_inputs(31, batch=7, heads=128, seqlen_range=(1, 3000))
     d = mla.to_device(inp)
@@ -138,6 +168,66 @@ def test_outputs_fully_written_and_deterministic():
         outs.append((out.clone(), lse.clone()))
     assert torch.equal(outs[0][0].view(torch.int16), outs[1][0].view(torch.int16))
     assert torch.equal(outs[0][1].view(torch.int32), outs[1][1].view(torch.int32))
+
+
+def _pow2_scales(inp, seed):
+    """Replace the FP8 scales by powers of two in {1/2, 1, 2}: code * scale is
+    then exact in bf16, so a one-hot softmax must return the row bit for bit."""
+    rng = np.random.default_rng(seed)
+    inp["kv_scales"] = (2.0 ** rng.integers(-1, 2, inp["kv_scales"].shape)).astype(np.float32)
+
+
+@pytest.mark.parametrize("heads,kv_format,topk", [(128, "fp8", 0), (64, "fp8", 0), (8, "fp8", 0),
+                                                  (128, "fp8", 600), (64, "bf16", 600)])
+def test_one_hot_gather_fp8_and_topk_bit_exact(heads, kv_format, topk):
+    """As the bf16 one-hot test, for the FP8 cache (power-of-two scales) and
+    for top-k gathers: j* is one of the listed entries, and the expected row
+    is the oracle's dequantised V[row(j*)], exact in bf16."""
+    B = 3
+    inp = synth.make_decode_inputs(141 + heads + topk, batch=B, heads=heads, seqlen_range=(700, 2500),
+                                   kv_format=kv_format, topk=topk, topk_pad_max=50)
+    if kv_format == "fp8":
+        _pow2_scales(inp, heads)
+    rng = np.random.default_rng(heads + topk)
+    q = np.empty_like(inp["q"])
+    want = np.empty((B, heads, 512), dtype=np.uint16)
+    for b in range(B):
+        n = int(inp["seqlens"][b])
+        if topk:
+            cand = inp["topk_idx"][b]
+            cand = cand[(cand >= 0) & (cand < n)]
+            js = rng.choice(cand, heads)
+            js[0] = cand[-1]
+        else:
+            js = rng.integers(0, n, heads)
+            js[0] = n - 1
+        rows = mo.physical_rows(inp["block_table"][b], js)
+        kf = mo.dequant_rows(inp["kv"], rows, inp["kv_format"], inp["kv_scales"])
+        # gain 32 (exact in bf16): every other token then trails by so many
+        # logits that its weight is 0 in fp32, also where V[row(j*)] has exact
+        # zeros (e4m3 codes 0x00 / 0x80), which a smaller gain would leave at
+        # ~1e-30 instead of 0
+        q[b] = codecs.f64_to_bf16_bits(32.0 * kf)
+        want[b] = codecs.f64_to_bf16_bits(kf[:, :512])
+        assert np.array_equal(codecs.bf16_bits_to_f64(want[b]), kf[:, :512])  # exact in bf16
+    inp["q"] = q
+    _say(f"[decode one-hot] H={heads} kv={kv_format} topk={topk}")
+    out, lse = run_gpu(inp)
+    got = out.cpu().view(torch.int16).numpy().view(np.uint16)
+    # e4m3 code 0x80 is -0: the sum p * V gives +0 for it, and the two zeros
+    # count as equal
+    g, wv = _plus_zero(got), _plus_zero(want)
+    bad = np.argwhere(g != wv)
+    for i in bad[:8]:
+        i = tuple(i)
+        gv = float(codecs.bf16_bits_to_f64(np.array([g[i]], dtype=np.uint16))[0])
+        wf = float(codecs.bf16_bits_to_f64(np.array([wv[i]], dtype=np.uint16))[0])
+        _say(f"   mismatch at {i}: gpu={gv:.6g} ({int(g[i]):#06x}) want={wf:.6g} ({int(wv[i]):#06x})")
+    np.testing.assert_array_equal(g, wv)
+
+
+def _plus_zero(bits):
+    return np.where((bits & 0x7FFF) == 0, 0, bits).astype(np.uint16)
 
 
 @pytest.mark.parametrize("heads", [128, 64, 8])
@@ -183,7 +273,7 @@ def test_page_permutation_invariance_bitwise():
     assert torch.equal(lse1.view(torch.int32), lse2.view(torch.int32))
 
 
-@pytest.mark.parametrize("name", ["paged_bf16_4096", "paged_bf16", "query_decode"])
+@pytest.mark.parametrize("name", ["paged_bf16_4096", "paged_bf16", "query_decode", "fp8_cache", "topk_sparse"])
 def test_full_size_workloads_sampled(name):
     """The full-size decode workloads, in the launch configuration the
     benchmark times, checked on a sample of sequences the oracle computes."""
