@@ -275,3 +275,21 @@ def to_device(inp: dict, device="cuda"):
     res["seqlens"] = torch.from_numpy(np.ascontiguousarray(inp["seqlens"])).to(device)
     res["topk_idx"] = None if inp.get("topk_idx") is None else torch.from_numpy(np.ascontiguousarray(inp["topk_idx"])).to(device)
     return res
+
+
+def query_to_device(inp: dict, device="cuda"):
+    """Move a seeded query-front-end input (numpy raw bits, see synth) to device
+    tensors; q_scale_inv becomes a one-element float32 device tensor."""
+    import numpy as np
+    import torch
+
+    def u16_to_bf16(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(device)
+
+    return {
+        "qkv": u16_to_bf16(inp["qkv"]),
+        "w_qa": u16_to_bf16(inp["w_qa"]),
+        "w_qb": u16_to_bf16(inp["w_qb"]),
+        "w_uk": u16_to_bf16(inp["w_uk"]),
+        "q_scale_inv": torch.tensor([inp["q_scale_inv"]], dtype=torch.float32, device=device),
+    }

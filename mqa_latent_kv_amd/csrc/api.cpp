@@ -12,6 +12,8 @@ bool valid_dtype(int32_t d) { return d == MLA_DTYPE_BF16 || d == MLA_DTYPE_FP8_E
 
 bool supported_heads(int32_t h) { return h == 8 || h == 16 || h == 32 || h == 64 || h == 128; }
 
+bool aligned16(const void* p) { return ((uintptr_t)p & 15) == 0; }
+
 int32_t check_decode_params(const mla_decode_params* p) {
   if (!p) return MLA_ERR_INVALID_ARG;
   if (p->batch < 1 || p->heads < 1 || p->num_pages < 1 || p->max_pages_per_seq < 1 || p->topk < 0)
@@ -99,6 +101,10 @@ int32_t mla_decode(const mla_decode_params* p, const void* q, const void* kv_cac
   int32_t st = check_decode_params(p);
   if (st != MLA_OK) return st;
   if (!q || !kv_cache || !block_table || !seqlens || !out || !lse) return MLA_ERR_INVALID_ARG;
+  // q rows, cache rows, scales and outputs are accessed as 8/16-byte vectors
+  if (!aligned16(q) || !aligned16(kv_cache) || !aligned16(out) || (kv_scales && !aligned16(kv_scales)) ||
+      !aligned16(workspace))
+    return MLA_ERR_INVALID_ARG;
   if ((p->topk > 0) != (topk_idx != nullptr)) return MLA_ERR_INVALID_ARG;
   if ((p->kv_dtype == MLA_DTYPE_FP8_E4M3) != (kv_scales != nullptr)) return MLA_ERR_INVALID_ARG;
   if (!workspace) return MLA_ERR_WORKSPACE;
@@ -134,6 +140,8 @@ int32_t mla_decode(const mla_decode_params* p, const void* q, const void* kv_cac
 int32_t mla_query_workspace_size(const mla_query_params* p, size_t* bytes) {
   if (!p || !bytes) return MLA_ERR_INVALID_ARG;
   if (p->batch < 1 || p->heads < 1 || p->qkv_stride < 1536 || !(p->eps >= 0.0f)) return MLA_ERR_INVALID_ARG;
+  // rows are read as 16-byte vectors
+  if (p->qkv_stride % 8 != 0) return MLA_ERR_UNSUPPORTED;
   if (p->batch > MLA_MAX_BATCH || p->heads > MLA_MAX_HEADS) return MLA_ERR_UNSUPPORTED;
   *bytes = mla::query_workspace_bytes(p->batch, p->heads);
   return MLA_OK;
@@ -146,6 +154,8 @@ int32_t mla_query(const mla_query_params* p, const void* qkv, const void* w_qa, 
   int32_t st = mla_query_workspace_size(p, &need);
   if (st != MLA_OK) return st;
   if (!qkv || !w_qa || !w_qb || !w_uk || !q_scale_inv || !out) return MLA_ERR_INVALID_ARG;
+  if (!aligned16(qkv) || !aligned16(w_qa) || !aligned16(w_qb) || !aligned16(w_uk) || !aligned16(workspace))
+    return MLA_ERR_INVALID_ARG;
   if (!workspace || workspace_bytes < need) return MLA_ERR_WORKSPACE;
   mla::QueryLaunch ql;
   ql.qkv = qkv;
