@@ -1,18 +1,29 @@
 """Benchmark of the MLA decode hot path on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+                    [--no-cpu-baseline] [--profile-run]
 
-A step is one mla_decode call over the paged bf16 workload the headline metric
-is quoted on: batch 64, 128 query heads, every sequence 4096 tokens, 64-token
-pages scattered through a 4096-page pool by a random block table, q and KV
-N(0,1) in bf16, softmax scale 192^-0.5.  The call runs the whole path on the
-GPU: work split, query tile load, block-table translation, KV streaming, QK^T,
-online softmax, PV, epilogue and the split-KV merge, in one kernel launch.
-Inputs are seeded, generated on the host and resident in HBM before timing.
+A step is one pass of the hot path over one batch of synthetic input, with
+every input resident in HBM before timing:
 
-Prints one JSON line: whole-step algorithmic HBM throughput (GB/s) as
-`value`, µs/step, tokens/s, a `roofline` object for the decode kernel (timed
-with HIP events on its stream) and a `cpu_baseline` object (the float64 CPU
+  paged_bf16_4096 (default, the headline): one mla_decode call over the paged
+      bf16 cache, batch 64, 128 query heads, every sequence 4096 tokens,
+      64-token pages scattered through a 4096-page pool by a random block
+      table, q and KV N(0,1) in bf16, softmax scale 192^-0.5.
+  paged_bf16: the same pool with seeded lengths uniform in [1024, 4096].
+  fp8_cache: batch 32, 64 heads, lengths uniform in [8192, 32768], e4m3 cache
+      (512 codes + 64 bf16 rope per row) with per-row per-tile fp32 scales.
+  topk_sparse: batch 32, 128 heads, 2048 sorted top-k positions per sequence
+      over 65536-token contexts (trailing -1 padding), e4m3 cache.
+  query_decode: mla_query (RMSNorm, Q_B, W_UK, FP8) for 64 tokens x 8 heads,
+      then mla_decode of those FP8 queries over a bf16 cache of 8192 tokens
+      per sequence.
+
+The decode call runs the work split, block-table translation (or the top-k
+prepass), KV streaming, QK^T, softmax, PV, epilogue and the split-KV merge on
+the GPU.  Prints one JSON line: algorithmic HBM throughput (GB/s) as
+`value`, µs/step, tokens/s, a `roofline` object (the step's kernels timed with
+HIP events on their stream) and a `cpu_baseline` object (the float64 CPU
 oracle on a bounded sample of the same workload).
 """
 from __future__ import annotations
@@ -31,26 +42,65 @@ sys.path.insert(0, ROOT)
 
 METRIC = "MLA decode µs/step + achieved HBM GB/s (% of peak) at B=64,H=128,s_k=4096"
 HBM_PEAK_GBS = 8000.0
+MFMA_BF16_PEAK_TFLOPS = 2500.0
 CALIB_BYTES = 256 << 20  # plain copy used to scale the HBM traffic counters
-WORKLOAD = "paged_bf16_4096"
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_paged_bf16_4096_traffic.json")
-KERNEL_SOURCES = [os.path.join(ROOT, "mqa_latent_kv_amd", "csrc", f) for f in ("decode.hip",)]
+KERNEL_SOURCES = [os.path.join(ROOT, "mqa_latent_kv_amd", "csrc", f) for f in ("decode.hip", "query.hip")]
+
+WORKLOADS = {
+    "paged_bf16_4096": "paged bf16 MLA decode: batch 64, 128 heads, seq_len 4096 each, 64-token pages, "
+                       "4096-page pool, d_qk 576, d_v 512",
+    "paged_bf16": "paged bf16 MLA decode: batch 64, 128 heads, seq_len uniform 1024..4096, 64-token pages, "
+                  "4096-page pool",
+    "fp8_cache": "FP8 (e4m3 + fp32 tile scales) MLA decode: batch 32, 64 heads, seq_len uniform 8192..32768, "
+                 "16384-page pool",
+    "topk_sparse": "top-k sparse MLA decode: batch 32, 128 heads, 2048 positions (<=256 padded) of 65536, "
+                   "e4m3 cache, 32768-page pool",
+    "query_decode": "MLA query front end (64 tokens, 8 heads: RMSNorm, Q_B 1536x1536, W_UK, FP8) then decode "
+                    "of the FP8 queries over bf16 pages, 8192 tokens each",
+}
 
 
-def algorithmic_bytes(inp) -> int:
-    """Bytes the decode must move at least once: the KV rows of every attended
-    token, the queries, the outputs (bf16 O + fp32 LSE) and the block-table
-    entries and sequence lengths it reads."""
+def traffic_file(workload: str) -> str:
+    return os.path.join(ROOT, "profiles", f"decode_{workload}_traffic.json")
+
+
+def kv_tokens(inp) -> int:
+    """KV rows the decode attends: all positions, or the valid top-k entries."""
+    if inp.get("topk_idx") is not None:
+        t, seq = inp["topk_idx"], inp["seqlens"].astype(np.int64)[:, None]
+        return int(np.sum((t >= 0) & (t < seq)))
+    return int(inp["seqlens"].astype(np.int64).sum())
+
+
+def decode_bytes(inp) -> int:
+    """Bytes the decode must move at least once: the KV rows it attends
+    (bf16 1152 B; FP8 512 codes + 128 B rope + 16 B scales), the queries, the
+    outputs (bf16 O + fp32 LSE), the block-table entries it reads, the
+    sequence lengths and the top-k lists."""
     B, H = inp["batch"], inp["heads"]
-    seq = inp["seqlens"].astype(np.int64)
     row = 576 * 2 if inp["kv_format"] == "bf16" else 512 + 128 + 16
     qb = 576 * (2 if inp["q_format"] == "bf16" else 1)
-    pages = int(np.sum((seq + 63) // 64))
-    return int(seq.sum()) * row + B * H * qb + B * H * (512 * 2 + 4) + pages * 4 + B * 4
+    if inp.get("topk_idx") is not None:
+        tables = inp["topk_idx"].size * 4 + kv_tokens(inp) * 4  # lists + one block-table entry per valid entry
+    else:
+        seq = inp["seqlens"].astype(np.int64)
+        tables = int(np.sum((seq + 63) // 64)) * 4
+    return kv_tokens(inp) * row + B * H * qb + B * H * (512 * 2 + 4) + tables + B * 4
 
 
-def algorithmic_flops(inp) -> int:
-    return int(inp["seqlens"].astype(np.int64).sum()) * 2 * inp["heads"] * (576 + 512)
+def decode_flops(inp) -> int:
+    return kv_tokens(inp) * 2 * inp["heads"] * (576 + 512)
+
+
+def query_bytes(qin) -> int:
+    """qkv rows read, the three weights, the FP8 output."""
+    B, H = qin["batch"], qin["heads"]
+    return B * 1536 * 2 + 1536 * 2 + H * 192 * 1536 * 2 + H * 128 * 512 * 2 + B * H * 576
+
+
+def query_flops(qin) -> int:
+    B, H = qin["batch"], qin["heads"]
+    return 2 * B * 1536 * H * 192 + 2 * B * H * 128 * 512
 
 
 def kernel_hash() -> str:
@@ -60,40 +110,48 @@ def kernel_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def measured_traffic():
-    """HBM bytes per launch from the committed rocprofv3 PMC summary, if it was
-    taken on the current kernel source; else None."""
+def measured_traffic(workload: str):
+    """HBM bytes per step from the committed rocprofv3 counter summary, if it
+    was taken on the current kernel sources; else None."""
     try:
-        d = json.load(open(TRAFFIC_FILE))
+        d = json.load(open(traffic_file(workload)))
     except (OSError, ValueError):
         return None
     if d.get("kernel_hash") != kernel_hash():
         return None
-    return d.get("traffic_bytes_per_launch")
+    return d.get("traffic_bytes_per_step")
 
 
-def cpu_baseline(inp, budget_s: float = 12.0):
-    """The float64 oracle (as it stands) on whole sequences of the workload,
-    until the time budget is spent; throughput in the metric's unit."""
+def cpu_threads() -> int:
     from threadpoolctl import threadpool_info
 
+    return int(max([i.get("num_threads", 1) for i in threadpool_info()
+                    if i.get("internal_api") in ("openblas", "mkl", "blis")] or [1]))
+
+
+def cpu_baseline(inp, nbytes: int, budget_s: float = 12.0, qin=None):
+    """The float64 oracle (as it stands) on whole sequences of the workload
+    until the time budget is spent, scaled to the metric's unit."""
     from oracle import mla_oracle as mo
 
-    done = 0
     t0 = time.perf_counter()
+    if qin is not None:
+        mo.mla_query(qin["qkv"], qin["w_qa"], qin["w_qb"], qin["w_uk"], qin["q_scale_inv"], eps=qin["eps"])
+    done = 0
     while done < inp["batch"] and time.perf_counter() - t0 < budget_s:
-        mo.mla_decode(inp["q"], inp["kv"], inp["block_table"], inp["seqlens"], batches=[done])
+        mo.mla_decode(inp["q"], inp["kv"], inp["block_table"], inp["seqlens"], inp.get("topk_idx"),
+                      inp.get("kv_scales"), q_format=inp["q_format"], kv_format=inp["kv_format"],
+                      q_descale=inp["q_descale"], batches=[done])
         done += 1
     dt = time.perf_counter() - t0
-    per_seq = algorithmic_bytes(inp) / inp["batch"]
-    threads = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("internal_api") in ("openblas", "mkl", "blis")] or [1])
+    frac = done / inp["batch"]
     return {
-        "value": round(per_seq * done / dt / 1e9, 4),
+        "value": round(nbytes * frac / dt / 1e9, 4),
         "unit": "GB/s",
-        "cores": int(threads),
+        "cores": cpu_threads(),
         "kind": "oracle",
-        "sample": f"{done} of {inp['batch']} sequences (all 128 heads x 4096 tokens each), {dt:.1f} s, "
-                  f"{done * 4096 / dt:.0f} KV tokens/s; host has {os.cpu_count()} logical CPUs",
+        "sample": f"{done} of {inp['batch']} sequences{' plus the whole query front end' if qin else ''}, "
+                  f"{dt:.1f} s; host has {os.cpu_count()} logical CPUs",
     }
 
 
@@ -102,6 +160,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="paged_bf16_4096", choices=list(WORKLOADS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--profile-run", action="store_true",
                     help="for rocprofv3 counter runs: run the steps untimed, then a plain device copy of "
@@ -121,19 +180,33 @@ def main():
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    inp = synth.workload_inputs(WORKLOAD)
+    name = args.workload
+    inp = synth.workload_inputs(name)
+    qin = synth.make_query_inputs(5, batch=64, heads=8) if name == "query_decode" else None
     d = mla.to_device(inp, dev)
     B, H = inp["batch"], inp["heads"]
+    topk = 0 if inp.get("topk_idx") is None else inp["topk_idx"].shape[1]
     params = mla.decode_params(batch=B, heads=H, num_pages=inp["kv"].shape[0],
-                               max_pages_per_seq=inp["block_table"].shape[1])
+                               max_pages_per_seq=inp["block_table"].shape[1], topk=topk,
+                               q_fp8=inp["q_format"] != "bf16", kv_fp8=inp["kv_format"] != "bf16",
+                               q_descale=inp["q_descale"])
     stream = torch.cuda.current_stream(dev)
     ws = mla.decode_workspace(params, dev, stream)
     out = torch.empty((B, H, 512), dtype=torch.bfloat16, device=dev)
     lse = torch.empty((B, H), dtype=torch.float32, device=dev)
+    q = d["q"]
+    if qin is not None:
+        dq = mla.query_to_device(qin, dev)
+        q = torch.empty((B, H, 576), dtype=torch.uint8, device=dev)
+        qws = torch.empty(max(mla.mla_query_workspace_size(mla.QueryParams(B, H, 1536, qin["eps"])), 1),
+                          dtype=torch.uint8, device=dev)
 
     def step():
-        mla.mla_decode(d["q"], d["kv"], d["block_table"], d["seqlens"], out=out, lse=lse, workspace=ws,
-                       stream=stream)
+        if qin is not None:
+            mla.mla_query(dq["qkv"], dq["w_qa"], dq["w_qb"], dq["w_uk"], dq["q_scale_inv"], out=q, eps=qin["eps"],
+                          workspace=qws, stream=stream)
+        mla.mla_decode(q, d["kv"], d["block_table"], d["seqlens"], d["topk_idx"], d["kv_scales"], out=out, lse=lse,
+                       q_descale=inp["q_descale"], workspace=ws, stream=stream)
 
     for _ in range(args.warmup):
         step()
@@ -147,11 +220,11 @@ def main():
         for _ in range(args.steps):
             dst.copy_(src)
         torch.cuda.synchronize()
-        print(f"profile run: {args.steps} decode steps, {args.steps} copies of {CALIB_BYTES} bytes", flush=True)
+        print(f"profile run: {name}, {args.steps} steps, {args.steps} copies of {CALIB_BYTES} bytes", flush=True)
         return
 
-    # timed region: K back-to-back steps; an event pair around every launch
-    # gives the kernel's own duration on its stream
+    # timed region: K back-to-back steps; an event pair around every step
+    # gives the duration of its kernels on their stream
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
     t_all0, t_all1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
@@ -169,7 +242,7 @@ def main():
     ms_per_step = total_ms / args.steps
 
     # cold-cache figure (secondary): a 512 MB write between steps evicts the
-    # 256 MB Infinity Cache and the L2s; only the decode launch is timed
+    # 256 MB Infinity Cache and the L2s; only the step is timed
     flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
     cold = []
     for _ in range(min(args.steps, 20)):
@@ -182,12 +255,30 @@ def main():
         cold.append(e0.elapsed_time(e1))
     del flush
 
-    nbytes = algorithmic_bytes(inp)
-    flops = algorithmic_flops(inp)
+    nbytes = decode_bytes(inp) + (query_bytes(qin) if qin else 0)
+    flops = decode_flops(inp) + (query_flops(qin) if qin else 0)
     kern_avg_s = float(kern_ms.mean()) / 1e3
     achieved = nbytes / kern_avg_s / 1e9
-    traffic = measured_traffic()
+    tflops = flops / kern_avg_s / 1e12
     value = nbytes / (ms_per_step / 1e3) / 1e9
+    kernels = {"topk_sparse": "mla_topk_rows_kernel + mla_decode_kernel<2,false,2> + mla_merge_kernel",
+               "fp8_cache": "mla_decode_kernel<2,false,1> + mla_merge_kernel",
+               "query_decode": "mla_qb_kernel + mla_ql_kernel + mla_decode_kernel<4,true,0> + mla_merge_kernel"}
+    kernel = kernels.get(name, "mla_decode_kernel<2,false,0> + mla_merge_kernel")
+    mfma_bound = name == "topk_sparse"  # 345 flop per algorithmic byte, above the bf16 ridge
+    roofline = {
+        "bound": "mfma" if mfma_bound else "hbm",
+        "kernel": kernel + " (one call, timed together)",
+        "achieved": round(tflops if mfma_bound else achieved, 1),
+        "peak": MFMA_BF16_PEAK_TFLOPS if mfma_bound else HBM_PEAK_GBS,
+        "unit": "TFLOP/s" if mfma_bound else "GB/s",
+        "frac": round((tflops / MFMA_BF16_PEAK_TFLOPS) if mfma_bound else (achieved / HBM_PEAK_GBS), 4),
+        "traffic": measured_traffic(name),
+        "kernel_us_avg": round(kern_avg_s * 1e6, 2),
+        "hbm_gbs": round(achieved, 1),
+        "mfma_tflops": round(tflops, 1),
+    }
+    seq = inp["seqlens"]
     res = {
         "metric": METRIC,
         "value": round(value, 1),
@@ -199,40 +290,27 @@ def main():
         "us_per_step": round(ms_per_step * 1e3, 2),
         "frac_of_hbm_peak": round(value / HBM_PEAK_GBS, 4),
         "tokens_per_s": round(B / (ms_per_step / 1e3), 1),
-        "kv_tokens_per_s": round(float(inp["seqlens"].sum()) / (ms_per_step / 1e3), 1),
+        "kv_tokens_per_s": round(kv_tokens(inp) / (ms_per_step / 1e3), 1),
         "cold_us_per_step_median": round(float(np.median(cold)) * 1e3, 2),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
-        "data": "synthetic (seeded N(0,1) q and KV, random permuted block table)",
+        "dtype": "bf16" if inp["kv_format"] == "bf16" else "bf16 (e4m3 cache codes)",
+        "data": "synthetic (seeded; q and KV from N(0,1), random permuted block table)",
         "config": {
-            "workload": "paged bf16 MLA decode: batch 64, 128 heads, seq_len 4096 each, 64-token pages, "
-                        "4096-page pool, d_qk 576, d_v 512",
+            "workload": WORKLOADS[name],
             "batch": B,
             "heads": H,
-            "seq_len": 4096,
+            "seq_len": int(seq.max()) if int(seq.min()) == int(seq.max()) else [int(seq.min()), int(seq.max())],
             "page_size": 64,
-            "algorithmic_bytes": nbytes,
-            "algorithmic_flops": flops,
+            "topk": topk,
+            "algorithmic_bytes": int(nbytes),
+            "algorithmic_flops": int(flops),
         },
-        "roofline": {
-            "bound": "hbm",
-            "kernel": "mla_decode_bf16_kernel<2,false>",
-            "achieved": round(achieved, 1),
-            "peak": HBM_PEAK_GBS,
-            "unit": "GB/s",
-            "frac": round(achieved / HBM_PEAK_GBS, 4),
-            "traffic": traffic,
-            "kernel_us_avg": round(kern_avg_s * 1e6, 2),
-            "mfma_tflops": round(flops / kern_avg_s / 1e12, 1),
-        },
+        "roofline": roofline,
         "wall_s_timed_region": round(wall, 4),
     }
-    if not args.no_cpu_baseline:
-        res["cpu_baseline"] = cpu_baseline(inp)
-    else:
-        res["cpu_baseline"] = None
+    res["cpu_baseline"] = None if args.no_cpu_baseline else cpu_baseline(inp, nbytes, qin=qin)
     print(json.dumps(res), flush=True)
 
 
