@@ -32,6 +32,7 @@ import argparse
 import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -104,9 +105,12 @@ def query_flops(qin) -> int:
 
 
 def kernel_hash() -> str:
+    """Hash of the kernel sources with // comments dropped and whitespace runs
+    collapsed, so a comment edit does not disown counters taken on the same code."""
     h = hashlib.sha256()
     for p in KERNEL_SOURCES:
-        h.update(open(p, "rb").read())
+        text = re.sub(r"//[^\n]*", "", open(p, encoding="utf-8").read())
+        h.update(re.sub(r"\s+", " ", text).encode())
     return h.hexdigest()[:16]
 
 

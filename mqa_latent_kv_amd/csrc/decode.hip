@@ -41,9 +41,11 @@
 //    ranges, one per workgroup and slab (a static form of the persistent
 //    scheduler the STAGE_D2 note describes under "Grid vs. Persistent Tile
 //    Scheduler").  A sequence inside one range is finished in place;
-//    otherwise each piece writes a normalised fp32 partial and its base-2 LSE
-//    and bumps a counter, and the last piece to arrive merges them (one
-//    launch, no wait on other workgroups) and resets the counter.
+//    otherwise each piece writes a normalised fp32 partial and its base-2
+//    LSE, and a second kernel (mla_merge_kernel) combines the pieces.  The
+//    merge is not done by the last piece to arrive: that would need a
+//    device-scope release fence per piece, which on gfx950 writes back the
+//    whole XCD L2.
 //  * Softmax in base 2 against a fixed reference per head: the first slot's
 //    max.  Later slots may exceed it by up to 16 (P <= 2^16, exact in fp32 and
 //    as relative bf16); if any head's scores rise further, the workgroup
