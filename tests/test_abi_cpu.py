@@ -62,12 +62,19 @@ def _params(**kw):
 FAKE = ctypes.c_void_p(0x1000)  # never dereferenced: validation fails first
 
 
-def _decode(L, p, **ptrs):
+def _decode(L, p, ws_bytes=1 << 30, **ptrs):
     args = dict(q=FAKE, kv=FAKE, bt=FAKE, sl=FAKE, topk=None, scales=None, out=FAKE, lse=FAKE, ws=FAKE)
     args.update(ptrs)
     return L.mla_decode(ctypes.byref(p) if p is not None else None, args["q"], args["kv"], args["bt"], args["sl"],
-                        args["topk"], args["scales"], args["out"], args["lse"], args["ws"], ctypes.c_size_t(1 << 30),
+                        args["topk"], args["scales"], args["out"], args["lse"], args["ws"], ctypes.c_size_t(ws_bytes),
                         None)
+
+
+def _passes_validation(code):
+    """A call that passed argument validation stops at the device query (no
+    GPU) or at the one-byte workspace (GPU): it never launches on the fake
+    pointers."""
+    return code in (-5, -3)
 
 
 @pytest.mark.parametrize(
@@ -117,12 +124,34 @@ def test_decode_optional_arguments_must_match_params(L):
     assert _decode(L, _params(), scales=FAKE) == -1
 
 
+MISALIGNED = ctypes.c_void_p(0x1008)  # 8-byte aligned only
+
+
+def test_decode_rejects_misaligned_pointers(L):
+    # the kernels move q, KV rows, outputs, scales and workspace in 16-byte units
+    for name in ("q", "kv", "out", "ws"):
+        assert _decode(L, _params(), **{name: MISALIGNED}) == -1, name
+    assert _decode(L, _params(kv_fp8=True), scales=MISALIGNED) == -1
+    # int32 tables need only their natural alignment
+    assert _passes_validation(_decode(L, _params(), ws_bytes=1, bt=ctypes.c_void_p(0x1004),
+                                      sl=ctypes.c_void_p(0x1004)))
+
+
+def test_decode_rejects_topk_lists_beyond_32_bit_offsets(L):
+    p = _params(batch=8192, topk=(1 << 31) // 8192)
+    assert _decode(L, p, topk=FAKE) == -2
+    n = ctypes.c_size_t(0)
+    assert L.mla_decode_workspace_size(ctypes.byref(p), ctypes.byref(n)) == -2
+    p = _params(batch=8192, topk=(1 << 31) // 8192 - 1)
+    assert _passes_validation(_decode(L, p, ws_bytes=1, topk=FAKE))
+
+
 def test_query_validation(L):
-    def q(p, **ptrs):
+    def q(p, ws_bytes=1 << 30, **ptrs):
         a = dict(qkv=FAKE, wqa=FAKE, wqb=FAKE, wuk=FAKE, qsi=FAKE, out=FAKE, ws=FAKE)
         a.update(ptrs)
         return L.mla_query(ctypes.byref(p) if p is not None else None, a["qkv"], a["wqa"], a["wqb"], a["wuk"],
-                           a["qsi"], a["out"], a["ws"], ctypes.c_size_t(1 << 30), None)
+                           a["qsi"], a["out"], a["ws"], ctypes.c_size_t(ws_bytes), None)
 
     good = mla.QueryParams(64, 8, 1536, 1e-6)
     assert q(None) == -1
@@ -133,6 +162,11 @@ def test_query_validation(L):
     for name in ("qkv", "wqa", "wqb", "wuk", "qsi", "out"):
         assert q(good, **{name: None}) == -1, name
     assert q(good, ws=None) == -3
+    # qkv rows are read in 16-byte vectors: the row stride must be a multiple of 8 elements
+    assert q(mla.QueryParams(64, 8, 1540, 1e-6)) == -2
+    assert q(mla.QueryParams(64, 8, 2112, 1e-6), ws_bytes=1) == -3  # valid up to the workspace size
+    for name in ("qkv", "wqa", "wqb", "wuk", "ws"):
+        assert q(good, **{name: MISALIGNED}) == -1, name
     n = ctypes.c_size_t(0)
     assert L.mla_query_workspace_size(ctypes.byref(good), ctypes.byref(n)) == 0 and n.value > 0
 
