@@ -41,11 +41,11 @@
 //    ranges, one per workgroup and slab (a static form of the persistent
 //    scheduler the STAGE_D2 note describes under "Grid vs. Persistent Tile
 //    Scheduler").  A sequence inside one range is finished in place;
-//    otherwise each piece writes a normalised fp32 partial and its base-2
-//    LSE, and a second kernel (mla_merge_kernel) combines the pieces.  The
-//    merge is not done by the last piece to arrive: that would need a
-//    device-scope release fence per piece, which on gfx950 writes back the
-//    whole XCD L2.
+//    otherwise each piece writes its normalised partial O and its base-2
+//    LSE (both fp32), and a second kernel (mla_merge_kernel) combines
+//    the pieces.  The merge is not done by the last piece to arrive: that
+//    would need a device-scope release fence per piece, which on gfx950
+//    writes back the whole XCD L2.
 //  * Softmax in base 2 against a fixed reference per head: the first slot's
 //    max.  Later slots may exceed it by up to 16 (P <= 2^16, exact in fp32 and
 //    as relative bf16); if any head's scores rise further, the workgroup
@@ -95,7 +95,7 @@ struct DecodeArgs {
   const float* kv_scales;
   void* out;
   float* lse;
-  float* ws_o;    // [(ranges + B) slots][H][512] fp32 partials
+  float* ws_o;    // [(ranges + B) slots][H][512] normalised partial O, fp32
   float* ws_lse;  // [(ranges + B)][H] base-2 LSE of partials
   int2* ws_seq;   // [B] {workspace slot of piece 0, pieces}; pieces 0: nothing to attend
   const int32_t* ws_rows;    // top-k: [B][topk] physical row per entry, -1 for a masked entry
@@ -469,10 +469,24 @@ struct SoftmaxState {
 
 // This wave's partial S^T of one slot: 32 tokens x 32 heads over its KS
 // k-steps, fp32.
-// K fragments are read kRA steps ahead of the MFMA that consumes them; the
-// scheduling fences keep LDS reads and MFMAs in this order and let only
-// VALU work (the softmax of the previous slot) move between them.
-constexpr int kRA = 4;
+// K fragments are read kRA - 1 steps ahead of the MFMA that consumes them.
+// A read must not land in the registers of an operand that an issued MFMA
+// is still reading: the wave would then wait for that MFMA to finish, and
+// everything it issues between MFMAs would serialise with the matrix core.
+// The register allocator does not know this, so every operand is kept
+// visibly alive (keep_alive) until the reads that follow its MFMA have been
+// issued; MFMA I - 1 has completed once MFMA I (which accumulates onto its
+// result) issues, so the reads may reuse its registers.  The scheduling
+// fences keep LDS reads and MFMAs in this order and let only VALU work move
+// between them.
+constexpr int kRA = 5;
+
+// An empty use that keeps a register operand live to this point; the memory
+// clobber keeps LDS reads from moving across it.
+template <typename T>
+__device__ __forceinline__ void keep_alive(const T& v) {
+  asm volatile("" ::"v"(v) : "memory");
+}
 // What rides between the QK^T MFMAs of a step: the next slot's copies, the
 // previous slot's softmax, and (top-k) that softmax's validity mask.
 constexpr int kPipeDma = 1, kPipeSoft = 2, kPipeMask = 4;
@@ -527,19 +541,23 @@ __device__ __forceinline__ float sum_halves(float v) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
-// Softmax of a full slot cut into 15 stages that ride between the QK^T
-// MFMAs of the next slot (one stage per MFMA for 18 k-steps, two for 9):
-// the exchange reads, the score sums, the max, eight pairs of exponentials
-// and the row sums.  The MFMA of each step runs on the
-// matrix core while its stage issues on the vector unit.
+// Softmax of a full slot, cut into micro-stages that ride between the QK^T
+// MFMAs of the next slot: the score sums, a tree max, the max across the two
+// token halves, the reference, eight pairs of exponentials (each also adding
+// the previous pair into two running sums) and the row sums.  The partners'
+// partial scores are read from LDS right after the barrier that publishes
+// them, together with the first K fragments, and are first used three
+// k-steps later, so the read latency hides behind MFMAs.  No stage holds a
+// dependency chain longer than one MFMA.
 struct SoftPipe {
   uint32_t mask;    // valid tokens of the slot (top-k), bit t = token t
   f32x16 own;       // this wave's partial S^T of the slot
-  f32x4 xr[4];      // partner's partial (two parts)
+  f32x4 xr[16];     // the partners' partials: [part * 4 + r4] (two parts: the partner's, [r4])
   f32x16 x;         // full S^T
+  float t[5];       // partial maxima
   float mx, nref;
   f32x8 p0, p1;
-  float lsum;
+  float la, lb;     // running sums of p0, p1
 };
 
 struct SoftCtx {
@@ -550,10 +568,11 @@ struct SoftCtx {
 
 // Scores of tokens whose bit in `mask` is clear become -inf.  Lane l,
 // register r holds token 8*(r/4) + 4*(l/32) + r%4.
+template <int R0 = 0, int R1 = 16>
 __device__ __forceinline__ void apply_mask(f32x16& x, uint32_t mask, int lane) {
   const uint32_t mh = mask >> (4 * (lane >> 5));
 #pragma unroll
-  for (int r = 0; r < 16; ++r)
+  for (int r = R0; r < R1; ++r)
     x[r] = (mh >> (8 * (r >> 2) + (r & 3))) & 1u ? x[r] : -INFINITY;
 }
 
@@ -562,51 +581,91 @@ __device__ __forceinline__ void apply_mask(f32x16& x, uint32_t mask, int lane) {
 // score is -inf too, which must give p = 0, not NaN.
 __device__ __forceinline__ float neg_ref(float m_ref) { return m_ref == -INFINITY ? 0.0f : -m_ref; }
 
-template <int NSPLIT, int ST, bool MASKED>
-__device__ __forceinline__ void soft_stage(SoftPipe& sp, SoftmaxState& st, const SoftCtx& c) {
-  if constexpr (ST == 0) {
-    if constexpr (NSPLIT == 2) {
+// The partials this wave adds: two parts, the partner's; four parts, all
+// four (the own one too, so that every wave forms the same sum).
+template <int NSPLIT>
+__device__ __forceinline__ void soft_read(SoftPipe& sp, const SoftCtx& c) {
+  if constexpr (NSPLIT == 2) {
 #pragma unroll
-      for (int r4 = 0; r4 < 4; ++r4) sp.xr[r4] = c.xch[((c.w ^ 1) * 4 + r4) * 64 + c.lane];
-    } else {
-      sp.x = total_scores<NSPLIT>(c.xch, sp.own, c.w, c.lane);
-    }
-  } else if constexpr (ST == 1 || ST == 2) {
-    if constexpr (NSPLIT == 2) {
+    for (int r4 = 0; r4 < 4; ++r4) sp.xr[r4] = c.xch[((c.w ^ 1) * 4 + r4) * 64 + c.lane];
+  } else {
+    const int g0 = c.w & ~3;
 #pragma unroll
-      for (int r4 = 2 * (ST - 1); r4 < 2 * ST; ++r4)
+    for (int q = 0; q < 4; ++q)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) sp.x[4 * r4 + e] = sp.own[4 * r4 + e] + sp.xr[r4][e];
-    }
-  } else if constexpr (ST == 3) {
-    if constexpr (MASKED) apply_mask(sp.x, sp.mask, c.lane);
-    float m = sp.x[0];
-#pragma unroll
-    for (int r = 1; r < 16; ++r) m = fmaxf(m, sp.x[r]);
-    sp.mx = m;
-  } else if constexpr (ST == 4) {
-    const float mx = max_halves(sp.mx) * c.scale_log2;  // scale_log2 > 0: the max commutes with the scaling
-    st.m_ref = st.m_ref == -INFINITY ? mx : st.m_ref;
-    st.m_seen = fmaxf(st.m_seen, mx);
-    sp.nref = neg_ref(st.m_ref);
-  } else if constexpr (ST >= 5 && ST <= 12) {
-    constexpr int k = ST - 5;
-    sp.p0[k] = __builtin_amdgcn_exp2f(__builtin_fmaf(sp.x[k], c.scale_log2, sp.nref));
-    sp.p1[k] = __builtin_amdgcn_exp2f(__builtin_fmaf(sp.x[k + 8], c.scale_log2, sp.nref));
-  } else if constexpr (ST == 13) {
-    float l = 0.0f;
-#pragma unroll
-    for (int r = 0; r < 8; ++r) l += sp.p0[r];
-    sp.lsum = l;
-  } else if constexpr (ST == 14) {
-    float l = sp.lsum;
-#pragma unroll
-    for (int r = 0; r < 8; ++r) l += sp.p1[r];
-    st.l_sum += l;
+      for (int r4 = 0; r4 < 4; ++r4) sp.xr[4 * q + r4] = c.xch[((g0 + q) * 4 + r4) * 64 + c.lane];
   }
 }
 
-constexpr int kSoftStages = 15;
+enum : int {
+  kStSum0,  // x[0..7]
+  kStSum1,  // x[8..15]
+  kStMaxA,
+  kStMaxB,
+  kStHalves,
+  kStRef,
+  kStExp0,  // .. kStExp0 + 7
+  kStLsum = kStExp0 + 8,
+  kSoftStages
+};
+template <int NSPLIT, int ST, bool MASKED>
+__device__ __forceinline__ void soft_stage(SoftPipe& sp, SoftmaxState& st, const SoftCtx& c) {
+  if constexpr (ST == kStSum0 || ST == kStSum1) {
+    constexpr int r0 = ST == kStSum0 ? 0 : 2;  // first row group of four
+#pragma unroll
+    for (int r4 = r0; r4 < r0 + 2; ++r4) {
+      f32x4 v;
+      if constexpr (NSPLIT == 2) {
+        v = f32x4{sp.own[4 * r4], sp.own[4 * r4 + 1], sp.own[4 * r4 + 2], sp.own[4 * r4 + 3]} + sp.xr[r4];
+      } else {
+        v = (sp.xr[r4] + sp.xr[4 + r4]) + (sp.xr[8 + r4] + sp.xr[12 + r4]);
+      }
+#pragma unroll
+      for (int e = 0; e < 4; ++e) sp.x[4 * r4 + e] = v[e];
+    }
+    if constexpr (MASKED) apply_mask<4 * r0, 4 * r0 + 8>(sp.x, sp.mask, c.lane);
+  } else if constexpr (ST == kStMaxA) {
+#pragma unroll
+    for (int k = 0; k < 5; ++k) sp.t[k] = fmaxf(fmaxf(sp.x[3 * k], sp.x[3 * k + 1]), sp.x[3 * k + 2]);
+  } else if constexpr (ST == kStMaxB) {
+    sp.mx = fmaxf(fmaxf(fmaxf(sp.t[0], sp.t[1]), sp.t[2]), fmaxf(fmaxf(sp.t[3], sp.t[4]), sp.x[15]));
+  } else if constexpr (ST == kStHalves) {
+    sp.mx = max_halves(sp.mx) * c.scale_log2;  // scale_log2 > 0: the max commutes with the scaling
+  } else if constexpr (ST == kStRef) {
+    st.m_ref = st.m_ref == -INFINITY ? sp.mx : st.m_ref;
+    st.m_seen = fmaxf(st.m_seen, sp.mx);
+    sp.nref = neg_ref(st.m_ref);
+  } else if constexpr (ST >= kStExp0 && ST < kStExp0 + 8) {
+    constexpr int k = ST - kStExp0;
+    sp.p0[k] = __builtin_amdgcn_exp2f(__builtin_fmaf(sp.x[k], c.scale_log2, sp.nref));
+    sp.p1[k] = __builtin_amdgcn_exp2f(__builtin_fmaf(sp.x[k + 8], c.scale_log2, sp.nref));
+    if constexpr (k == 1) {
+      sp.la = sp.p0[0];
+      sp.lb = sp.p1[0];
+    } else if constexpr (k > 1) {
+      sp.la += sp.p0[k - 1];
+      sp.lb += sp.p1[k - 1];
+    }
+  } else if constexpr (ST == kStLsum) {
+    st.l_sum += (sp.la + sp.p0[7]) + (sp.lb + sp.p1[7]);
+  }
+}
+
+// Micro-stages [stage_lo, stage_hi) run at k-step I of KS: with 18 steps one
+// per step from step 3 on (the partners' partials, read right after the
+// barrier, are first used three MFMAs later); with 9 steps, two per step from
+// step 1 on (the sums of four parts one per step).
+constexpr int stage_lo(int KS, int I) {
+  if (KS >= 18) return I < 3 ? 0 : (I - 3 < kSoftStages ? I - 3 : kSoftStages);
+  constexpr int lo9[9] = {0, 0, 1, 2, 4, 6, 8, 10, 12};
+  return lo9[I];
+}
+constexpr int stage_hi(int KS, int I) {
+  if (KS >= 18) return I < 3 ? 0 : (I - 2 < kSoftStages ? I - 2 : kSoftStages);
+  constexpr int hi9[9] = {0, 1, 2, 4, 6, 8, 10, 12, kSoftStages};
+  return hi9[I];
+}
+static_assert(stage_hi(18, 17) == kSoftStages && stage_hi(9, 8) == kSoftStages, "every stage is scheduled");
 
 template <int NSPLIT, int ST0, int ST1, bool MASKED>
 __device__ __forceinline__ void soft_stages(SoftPipe& sp, SoftmaxState& st, const SoftCtx& c) {
@@ -626,11 +685,43 @@ __device__ __forceinline__ uint32_t k_addr(const LaneTables& t) {
 // arrays are sized for the largest case, unused entries cost nothing
 constexpr int kMaxAcc = 3;
 
+// V^T operands of one PV column block: two k-steps, each two tr reads
+typedef bf16x4 VBlock[4];
+
+// ds_read_b64_tr_b16 of column block cb of this wave's PV
+__device__ __forceinline__ void pv_load(const lds_char* buf, const LaneTables& t, int cb, VBlock& v) {
+  const uint32_t x = (cb & 1) ? 64u : 0u;
+  const lds_char* p0 = buf + (t.vaddr[0] ^ x) + kGroupBytes * (cb >> 1);
+  const lds_char* p1 = buf + (t.vaddr[1] ^ x) + kGroupBytes * (cb >> 1);
+  v[0] = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((LDS_AS bf16x4*)p0);
+  v[1] = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((LDS_AS bf16x4*)p1);
+  v[2] = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((LDS_AS bf16x4*)(p0 + 16 * 128));
+  v[3] = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((LDS_AS bf16x4*)(p1 + 16 * 128));
+}
+
+// The first kRA - 1 K fragments of a slot, issued before the rest of the
+// step's work so that their latency overlaps it.
+template <int NSPLIT, bool TILED>
+__device__ __forceinline__ void qk_preload(bf16x8 (&kb)[kRA], const lds_char* buf, const LaneTables& t) {
+  static_assert(kRA == 5, "preload covers kRA - 1 fragments");
+  kb[0] = *(const LDS_AS bf16x8*)(buf + k_addr<NSPLIT, TILED, 0>(t));
+  kb[1] = *(const LDS_AS bf16x8*)(buf + k_addr<NSPLIT, TILED, 1>(t));
+  kb[2] = *(const LDS_AS bf16x8*)(buf + k_addr<NSPLIT, TILED, 2>(t));
+  kb[3] = *(const LDS_AS bf16x8*)(buf + k_addr<NSPLIT, TILED, 3>(t));
+}
+
+// What else runs during a partial QK^T: the previous slot's softmax, the
+// first V^T block of its PV, and (copy ring) the copies of a later slot.
+struct QkSide {
+  DmaJob job;
+  const lds_char* pvbuf;  // slot whose PV follows
+  VBlock* va0;            // where its first V^T block goes
+};
+
 template <int NSPLIT, int I, int PIPE, bool TILED>
-__device__ __forceinline__ void qk_steps(f32x16 (&acc)[kMaxAcc], bf16x8 (&kb)[kRA],
-                                         const lds_char* buf, const bf16x8 (&qf)[kKSteps / NSPLIT],
-                                         const LaneTables& t, const DmaJob& job, SoftPipe& sp, SoftmaxState& st,
-                                         const SoftCtx& c) {
+__device__ __forceinline__ void qk_steps(f32x16 (&acc)[kMaxAcc], bf16x8 (&kb)[kRA], const lds_char* buf,
+                                         const bf16x8 (&qf)[kKSteps / NSPLIT], const LaneTables& t,
+                                         const QkSide& side, SoftPipe& sp, SoftmaxState& st, const SoftCtx& c) {
   using T = Tiling<NSPLIT>;
   constexpr int KS = T::KS;
   if constexpr (I < KS) {
@@ -638,19 +729,21 @@ __device__ __forceinline__ void qk_steps(f32x16 (&acc)[kMaxAcc], bf16x8 (&kb)[kR
     constexpr bool first = TILED ? (I < T::CS ? I % 8 == 0 : I == T::CS) : I == 0;
     __builtin_amdgcn_sched_barrier(0);
     acc[ai] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kb[I % kRA], qf[I], first ? f32x16{} : acc[ai], 0, 0, 0);
-    if constexpr (I + kRA < KS) kb[I % kRA] = *(const LDS_AS bf16x8*)(buf + k_addr<NSPLIT, TILED, I + kRA>(t));
+    if constexpr (I + kRA - 1 < KS)
+      kb[(I + kRA - 1) % kRA] = *(const LDS_AS bf16x8*)(buf + k_addr<NSPLIT, TILED, I + kRA - 1>(t));
+    keep_alive(kb[I % kRA]);
     if constexpr ((PIPE & kPipeDma) != 0) {
       // the next slot's copies ride between the MFMAs, so that the wave
       // never stalls on a full memory queue with nothing else to issue
       constexpr int R = KS / kDmaPerWave;
-      if constexpr (I % R == R - 1) dma_issue<I / R>(job);
+      if constexpr (I % R == R - 1) dma_issue<I / R>(side.job);
     }
     if constexpr ((PIPE & kPipeSoft) != 0) {
-      // and so does the softmax of the previous slot
-      constexpr int SPS = (kSoftStages + KS - 1) / KS;  // stages per step
-      soft_stages<NSPLIT, I * SPS, (I + 1) * SPS, (PIPE & kPipeMask) != 0>(sp, st, c);
+      soft_stages<NSPLIT, stage_lo(KS, I), stage_hi(KS, I), (PIPE & kPipeMask) != 0>(sp, st, c);
+      // the PV that follows starts on data already in registers
+      if constexpr (I == KS - 3) pv_load(side.pvbuf, t, 0, *side.va0);
     }
-    qk_steps<NSPLIT, I + 1, PIPE, TILED>(acc, kb, buf, qf, t, job, sp, st, c);
+    qk_steps<NSPLIT, I + 1, PIPE, TILED>(acc, kb, buf, qf, t, side, sp, st, c);
   }
 }
 
@@ -669,29 +762,18 @@ __device__ __forceinline__ f32x16 tile_scales(const LDS_AS float* tab, int tile,
   return s;
 }
 
-// Partial QK^T of one slot; with PIPE the next slot's copies and the
-// previous slot's softmax are interleaved with it.  Tiled: the tile
-// accumulators are scaled per token (scale table `stab` of the slot) and
-// added to the rope accumulator, in fp32.
-template <int NSPLIT, int PIPE, bool TILED = false>
-__device__ __forceinline__ f32x16 qk_partial(const lds_char* buf, const bf16x8 (&qf)[kKSteps / NSPLIT],
-                                             const LaneTables& t, const DmaJob& job, SoftPipe& sp, SoftmaxState& st,
-                                             const SoftCtx& c, const LDS_AS float* stab = nullptr, int part = 0) {
-  static_assert((kKSteps / NSPLIT) % kDmaPerWave == 0, "copies spread evenly over the k-steps");
-  bf16x8 kb[kRA];
-  kb[0] = *(const LDS_AS bf16x8*)(buf + k_addr<NSPLIT, TILED, 0>(t));
-  kb[1] = *(const LDS_AS bf16x8*)(buf + k_addr<NSPLIT, TILED, 1>(t));
-  kb[2] = *(const LDS_AS bf16x8*)(buf + k_addr<NSPLIT, TILED, 2>(t));
-  kb[3] = *(const LDS_AS bf16x8*)(buf + k_addr<NSPLIT, TILED, 3>(t));
-  f32x16 acc[kMaxAcc];
-  qk_steps<NSPLIT, 0, PIPE, TILED>(acc, kb, buf, qf, t, job, sp, st, c);
-  __builtin_amdgcn_sched_barrier(0);
+// Tiled (FP8 cache) partial S^T: the code-tile accumulators scaled per
+// token (scale table `stab` of the slot) and added to the rope accumulator,
+// in fp32.
+template <int NSPLIT, bool TILED>
+__device__ __forceinline__ f32x16 qk_combine(const f32x16 (&acc)[kMaxAcc], const LDS_AS float* stab, int part,
+                                             int lane) {
   if constexpr (TILED) {
     constexpr int TPP = Tiling<NSPLIT>::TPP;
     f32x16 s = acc[TPP];
 #pragma unroll
     for (int j = 0; j < TPP; ++j) {
-      const f32x16 sc = tile_scales(stab, TPP * part + j, c.lane);
+      const f32x16 sc = tile_scales(stab, TPP * part + j, lane);
 #pragma unroll
       for (int r = 0; r < 16; ++r) s[r] = __builtin_fmaf(sc[r], acc[j][r], s[r]);
     }
@@ -699,6 +781,21 @@ __device__ __forceinline__ f32x16 qk_partial(const lds_char* buf, const bf16x8 (
   } else {
     return acc[0];
   }
+}
+
+// Partial QK^T of one slot, its first kRA - 1 fragments already loaded
+// (kb); with PIPE the previous slot's softmax, the first V^T block of its PV
+// and the copies of a later slot are interleaved with it.
+template <int NSPLIT, int PIPE, bool TILED = false>
+__device__ __forceinline__ f32x16 qk_partial(bf16x8 (&kb)[kRA], const lds_char* buf,
+                                             const bf16x8 (&qf)[kKSteps / NSPLIT], const LaneTables& t,
+                                             const QkSide& side, SoftPipe& sp, SoftmaxState& st, const SoftCtx& c,
+                                             const LDS_AS float* stab = nullptr, int part = 0) {
+  static_assert((kKSteps / NSPLIT) % kDmaPerWave == 0, "copies spread evenly over the k-steps");
+  f32x16 acc[kMaxAcc];
+  qk_steps<NSPLIT, 0, PIPE, TILED>(acc, kb, buf, qf, t, side, sp, st, c);
+  __builtin_amdgcn_sched_barrier(0);
+  return qk_combine<NSPLIT, TILED>(acc, stab, part, c.lane);
 }
 
 // Softmax numerators of one slot as bf16 P^T operands.  Lane l, register r
@@ -762,36 +859,39 @@ __device__ __forceinline__ void make_pops(POps<NSPLIT, TILED>& po, const f32x8& 
 
 // O^T[c][head] += V^T . P^T over this wave's column blocks.  k-step 0 of a
 // block covers tokens 0..15 in the order the S^T layout hands them to this
-// lane (rows 4h+j and 8+4h+j), k-step 1 tokens 16..31.
+// lane (rows 4h+j and 8+4h+j), k-step 1 tokens 16..31.  The first block's
+// V^T operands arrive loaded (va0).  Three operand buffers: the reads for
+// block cb + 1 go to the buffer of block cb - 2, whose MFMAs have left the
+// matrix core (block cb - 1's may not have).
 template <int NSPLIT, bool TILED>
-__device__ __forceinline__ void pv_slot(const lds_char* buf, const POps<NSPLIT, TILED>& po, const LaneTables& t,
-                                        Acc<NSPLIT>& acc) {
+__device__ __forceinline__ void pv_slot(const lds_char* buf, const VBlock& va0, const POps<NSPLIT, TILED>& po,
+                                        const LaneTables& t, Acc<NSPLIT>& acc) {
   constexpr int NCB = kCB / NSPLIT;
   constexpr int BPS = NCB / POps<NSPLIT, TILED>::N;  // column blocks per operand set
-  const lds_char* b0 = buf + t.vaddr[0];
-  const lds_char* b1 = buf + t.vaddr[1];
-  const lds_char* b0x = buf + (t.vaddr[0] ^ 64u);
-  const lds_char* b1x = buf + (t.vaddr[1] ^ 64u);
-  bf16x4 va[2][4];
-  auto load = [&](int cb, bf16x4(&v)[4]) {
-    const lds_char* p0 = (cb & 1) ? b0x : b0;
-    const lds_char* p1 = (cb & 1) ? b1x : b1;
-    const int step = kGroupBytes * (cb >> 1);
-    v[0] = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((LDS_AS bf16x4*)(p0 + step));
-    v[1] = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((LDS_AS bf16x4*)(p1 + step));
-    v[2] = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((LDS_AS bf16x4*)(p0 + step + 16 * 128));
-    v[3] = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((LDS_AS bf16x4*)(p1 + step + 16 * 128));
-  };
-  load(0, va[0]);
+  VBlock va[3];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) va[0][i] = va0[i];
+  bf16x8 prev0 = {}, prev1 = {};  // operands of the previous block's MFMAs
 #pragma unroll
   for (int cb = 0; cb < NCB; ++cb) {
     __builtin_amdgcn_sched_barrier(0);
-    if (cb + 1 < NCB) load(cb + 1, va[(cb + 1) & 1]);
-    const bf16x4(&v)[4] = va[cb & 1];
+    const VBlock& v = va[cb % 3];
     const bf16x8 v0 = __builtin_shufflevector(v[0], v[1], 0, 1, 2, 3, 4, 5, 6, 7);
     const bf16x8 v1 = __builtin_shufflevector(v[2], v[3], 0, 1, 2, 3, 4, 5, 6, 7);
     acc.o[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(v0, po.b0[cb / BPS], acc.o[cb], 0, 0, 0);
     acc.o[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(v1, po.b1[cb / BPS], acc.o[cb], 0, 0, 0);
+    if (cb + 1 < NCB) pv_load(buf, t, cb + 1, va[(cb + 1) % 3]);
+    // this block's operands, and the previous block's (its MFMAs are
+    // independent of these and may still be in the matrix core), stay
+    // out of the reads' way
+    keep_alive(v0);
+    keep_alive(v1);
+    if (cb > 0) {
+      keep_alive(prev0);
+      keep_alive(prev1);
+    }
+    prev0 = v0;
+    prev1 = v1;
   }
   __builtin_amdgcn_sched_barrier(0);
 }
@@ -940,10 +1040,19 @@ mla_decode_kernel(DecodeArgs a) {
           return page * kPage + (t & 1) * kTS + min(frow, nv - 1);
         }
       };
-      // validity of the tokens of slot s (dense: only the last slot is short)
+      // validity of the tokens of slot s (dense: only the last slot is
+      // short; top-k: the prepass's words, cached 64 slots at a time, one
+      // per lane, like the page numbers)
+      PageCache mc;
+      const int mwords = nslots;
+      if constexpr (kv_topk(KVM)) page_cache_load(mc, (const int32_t*)sg.mask_seg, 0, mwords, lane);
       auto slot_mask = [&](int s) -> uint32_t {
-        if constexpr (kv_topk(KVM)) return __builtin_amdgcn_readfirstlane(sg.mask_seg[s]);
-        else return low_mask(sg.tok1 - (sg.tok0 + s * kTS));
+        if constexpr (kv_topk(KVM)) {
+          if (s >= mc.base + 64) page_cache_load(mc, (const int32_t*)sg.mask_seg, s, mwords, lane);
+          return (uint32_t)__builtin_amdgcn_readlane(mc.v, s - mc.base);
+        } else {
+          return low_mask(sg.tok1 - (sg.tok0 + s * kTS));
+        }
       };
 
       SoftmaxState st;
@@ -960,6 +1069,8 @@ mla_decode_kernel(DecodeArgs a) {
         const SoftCtx sctx{xch, w, lane, a.scale_log2};
         SoftPipe sp;
         POps<NSPLIT, TILED> po;
+        bf16x8 kb[kRA];
+        VBlock va0;
         f32x16 sc;
         int last_pos;  // ring position of the last slot
         if constexpr (KVM == kKvBf16) {
@@ -969,7 +1080,8 @@ mla_decode_kernel(DecodeArgs a) {
           for (int s = 0; s < 3; ++s) dma_issue_all(prep_slot(s, s, ring, a, sg, pc, tab, w, lane));
           wait_vm_lgkm0<2 * kDmaPerWave>();
           barrier();
-          sc = qk_partial<NSPLIT, 0>(ring, qf, tab, DmaJob{}, sp, st, sctx);
+          qk_preload<NSPLIT, false>(kb, ring, tab);
+          sc = qk_partial<NSPLIT, 0>(kb, ring, qf, tab, QkSide{}, sp, st, sctx);
           // steady state, slot s: publish its partial (computed one step
           // earlier) and wait for slot s+1 (slot s+2 stays in flight);
           // barrier; then the partial QK^T of slot s+1 runs beside the
@@ -980,12 +1092,20 @@ mla_decode_kernel(DecodeArgs a) {
             put_partial(xch, sc, w, lane);
             wait_vm_lgkm0<kDmaPerWave>();
             barrier();
-            const DmaJob job = prep_slot(s + 3, s + 3, ring, a, sg, pc, tab, w, lane);
+            // LDS reads first: the next slot's first K fragments and the
+            // partners' partials of this one
+            const lds_char* const kbuf = ring + ((s + 1) & (kRing - 1)) * kSlotBytes;
+            qk_preload<NSPLIT, false>(kb, kbuf, tab);
+            soft_read<NSPLIT>(sp, sctx);
+            __builtin_amdgcn_sched_barrier(0);
+            QkSide side;
+            side.job = prep_slot(s + 3, s + 3, ring, a, sg, pc, tab, w, lane);
+            side.pvbuf = ring + (s & (kRing - 1)) * kSlotBytes;
+            side.va0 = &va0;
             sp.own = sc;
-            sc = qk_partial<NSPLIT, kPipeDma | kPipeSoft>(ring + ((s + 1) & (kRing - 1)) * kSlotBytes, qf, tab, job,
-                                                          sp, st, sctx);
+            sc = qk_partial<NSPLIT, kPipeDma | kPipeSoft>(kb, kbuf, qf, tab, side, sp, st, sctx);
             make_pops<NSPLIT, TILED>(po, sp.p0, sp.p1, nullptr, part, lane);
-            pv_slot<NSPLIT, TILED>(ring + (s & (kRing - 1)) * kSlotBytes, po, tab, acc);
+            pv_slot<NSPLIT, TILED>(side.pvbuf, va0, po, tab, acc);
             wait_vm_lgkm0<63>();  // lgkmcnt(0): this wave's LDS reads are done
             barrier();
           }
@@ -995,41 +1115,54 @@ mla_decode_kernel(DecodeArgs a) {
         } else {
           // register fill through a ring of three positions (slot s at
           // position s % 3); the fourth slot region holds the FP8 scale
-          // tables, one per position.  Prologue: slots 0 and 1 written,
-          // slot 2 loaded, partial QK^T of slot 0.
+          // tables, one per position.  A slot's rows are loaded one step
+          // before the lanes write them into the ring, and (top-k) each
+          // row's index one step before that.  Prologue: slots 0 and 1
+          // written, slot 2 loaded, partial QK^T of slot 0.
           LDS_AS float* const stabs = (LDS_AS float*)(ring + kFillRing * kSlotBytes);
           auto pos_buf = [&](int pos) { return ring + pos * kSlotBytes; };
           auto pos_tab = [&](int pos) { return stabs + pos * (4 * kTS); };
           RawRow<KVM> rr;
           load_row<KVM>(rr, a, fill_src(0), fq);
+          int next_row = fill_src(3);
           fill_row<KVM>(pos_buf(0), pos_tab(0), rr, frow, fq);
           load_row<KVM>(rr, a, fill_src(1), fq);
           fill_row<KVM>(pos_buf(1), pos_tab(1), rr, frow, fq);
           load_row<KVM>(rr, a, fill_src(2), fq);
           wait_vm_lgkm0<63>();
           barrier();
-          sc = qk_partial<NSPLIT, 0, TILED>(pos_buf(0), qf, tab, DmaJob{}, sp, st, sctx, pos_tab(0), part);
-          // steady state, slot s: as above, with no copies in the QK^T; after
-          // PV of slot s the lanes write slot s+2 (loaded one step earlier)
-          // into the position that slot s-1 left and load slot s+3
+          qk_preload<NSPLIT, TILED>(kb, pos_buf(0), tab);
+          sc = qk_partial<NSPLIT, 0, TILED>(kb, pos_buf(0), qf, tab, QkSide{}, sp, st, sctx, pos_tab(0), part);
+          // steady state, slot s: as in the copy ring, with no copies in the
+          // QK^T; after PV of slot s the lanes write slot s+2 (loaded one
+          // step earlier) into the position that slot s-1 left, and load
+          // slot s+3
           int p0 = 0, p1 = 1, p2 = 2;  // positions of slots s, s+1, s+2
           for (int s = 0; s + 1 < nslots; ++s) {
             put_partial(xch, sc, w, lane);
             wait_vm_lgkm0<63>();
             barrier();
+            qk_preload<NSPLIT, TILED>(kb, pos_buf(p1), tab);
+            soft_read<NSPLIT>(sp, sctx);
+            __builtin_amdgcn_sched_barrier(0);
+            QkSide side;
+            side.pvbuf = pos_buf(p0);
+            side.va0 = &va0;
             sp.own = sc;
             if constexpr (kv_topk(KVM)) {
               sp.mask = slot_mask(s);
-              sc = qk_partial<NSPLIT, kPipeSoft | kPipeMask, TILED>(pos_buf(p1), qf, tab, DmaJob{}, sp, st, sctx,
+              sc = qk_partial<NSPLIT, kPipeSoft | kPipeMask, TILED>(kb, pos_buf(p1), qf, tab, side, sp, st, sctx,
                                                                    pos_tab(p1), part);
             } else {
-              sc = qk_partial<NSPLIT, kPipeSoft, TILED>(pos_buf(p1), qf, tab, DmaJob{}, sp, st, sctx, pos_tab(p1),
+              sc = qk_partial<NSPLIT, kPipeSoft, TILED>(kb, pos_buf(p1), qf, tab, side, sp, st, sctx, pos_tab(p1),
                                                         part);
             }
             make_pops<NSPLIT, TILED>(po, sp.p0, sp.p1, pos_tab(p0), part, lane);
-            pv_slot<NSPLIT, TILED>(pos_buf(p0), po, tab, acc);
+            pv_slot<NSPLIT, TILED>(side.pvbuf, va0, po, tab, acc);
             fill_row<KVM>(pos_buf(p2), pos_tab(p2), rr, frow, fq);
-            load_row<KVM>(rr, a, fill_src(s + 3), fq);
+            const int row = next_row;
+            next_row = fill_src(s + 4);
+            load_row<KVM>(rr, a, row, fq);
             wait_vm_lgkm0<63>();  // this wave's LDS reads and writes are done
             barrier();
             const int pn = p0;
@@ -1048,8 +1181,9 @@ mla_decode_kernel(DecodeArgs a) {
           f32x8 q0, q1;
           softmax_slot(tot, slot_mask(nslots - 1), st, a.scale_log2, q0, q1, lane);
           const LDS_AS float* ltab = (const LDS_AS float*)(ring + kFillRing * kSlotBytes) + last_pos * (4 * kTS);
+          pv_load(ring + last_pos * kSlotBytes, tab, 0, va0);
           make_pops<NSPLIT, TILED>(po, q0, q1, ltab, part, lane);
-          pv_slot<NSPLIT, TILED>(ring + last_pos * kSlotBytes, po, tab, acc);
+          pv_slot<NSPLIT, TILED>(ring + last_pos * kSlotBytes, va0, po, tab, acc);
         }
         // workgroup vote on a redo (every wave is past its last exchange read)
         wait_vm_lgkm0<0>();
@@ -1066,6 +1200,7 @@ mla_decode_kernel(DecodeArgs a) {
         if (!__builtin_amdgcn_readfirstlane(vote)) break;
         st.m_ref = st.m_seen;
         if (!kv_topk(KVM) && sg.npages > 64) page_cache_load(pc, sg.bt_seg, 0, sg.npages, lane);
+        if (kv_topk(KVM) && nslots > 64) page_cache_load(mc, (const int32_t*)sg.mask_seg, 0, mwords, lane);
       }
 
       // ---- epilogue: normalise and store this wave's columns (final output,
@@ -1085,6 +1220,8 @@ mla_decode_kernel(DecodeArgs a) {
             const int col = 32 * cb + 8 * rg + 4 * (lane >> 5);
             f32x4 v = {acc.o[cbi][4 * rg], acc.o[cbi][4 * rg + 1], acc.o[cbi][4 * rg + 2], acc.o[cbi][4 * rg + 3]};
             v *= inv;
+            // partials stay fp32: a second bf16 rounding would double the
+            // output's rounding error where |O| is large
             if (nsplit == 1) *(bf16x4*)(orow + col) = __builtin_convertvector(v, bf16x4);
             else *(f32x4*)(prow + col) = v;
           }

@@ -71,7 +71,8 @@ def compare(inp, out, lse, batches=None, rtol=0.0, scale=None):
     excess = np.max(exc)
     if excess > O_TOL:
         i = np.unravel_index(np.argmax(exc), exc.shape)
-        _say(f"   worst at {i}: gpu={go[i]:.6g} ref={ro[i]:.6g} scale={None if scale is None else scale[sel][i]:.6g} "
+        sc_i = "none" if scale is None else f"{scale[sel][i]:.6g}"
+        _say(f"   worst at {i}: gpu={go[i]:.6g} ref={ro[i]:.6g} scale={sc_i} "
              f"lse gpu={gl[i[:2]]:.6g} ref={rl[i[:2]]:.6g}")
     _say(f"   max|dO|={err_o:.3e} (max|O|={np.max(np.abs(ro)):.3e}, max excess over rtol term={excess:.3e})"
          f"  max|dLSE|={err_l:.3e}")
