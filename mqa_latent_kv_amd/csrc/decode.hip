@@ -178,17 +178,26 @@ __device__ bool make_plan(const DecodeArgs& a, int r, int* scratch, Plan& pl) {
   const int lo = tid * per, hi = min(B, lo + per);
   int local = 0;
   for (int b = lo; b < hi; ++b) local += units_of(a, b);
-  // inclusive scan of the per-thread sums (Hillis-Steele in LDS)
-  scratch[tid] = local;
-  __syncthreads();
-  for (int off = 1; off < kThreads; off <<= 1) {
-    int v = tid >= off ? scratch[tid - off] : 0;
-    __syncthreads();
-    scratch[tid] += v;
-    __syncthreads();
+  // inclusive scan of the per-thread sums: within each wave by cross-lane
+  // reads (ds_bpermute moves data between lanes, it touches no LDS memory),
+  // then the four wave totals through LDS behind a single barrier
+  const int lane = tid & 63, wv = tid >> 6;
+  int incl = local;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int v = __builtin_amdgcn_ds_bpermute((lane - off) << 2, incl);
+    incl += lane >= off ? v : 0;
   }
-  const int incl = scratch[tid];
-  const int total = scratch[kThreads - 1];
+  if (lane == 63) scratch[wv] = incl;
+  __syncthreads();
+  int before = 0, total = 0;
+#pragma unroll
+  for (int i = 0; i < kWaves; ++i) {
+    const int t = scratch[i];
+    before += i < wv ? t : 0;
+    total += t;
+  }
+  incl += before;
   const int excl = incl - local;
   __syncthreads();
   if (total == 0) return false;
@@ -947,7 +956,16 @@ mla_decode_kernel(DecodeArgs a) {
   const int hg = w / NSPLIT, part = w % NSPLIT;
 
   const int g = blockIdx.x;
-  // sequences with nothing to attend: O = 0, LSE = -inf (spread over the grid)
+  // workgroups are dealt round-robin to the 8 XCDs: each XCD gets a run of
+  // consecutive ranges with all their slabs, so the slabs share KV lines in
+  // one L2 and the pieces of a sequence mostly merge from it
+  const int idx = g / 8;
+  const int r = (g % 8) * a.per_xcd + idx / a.slabs;
+  const int slab = idx % a.slabs;
+  Plan pl;
+  const bool has_work = r < a.ranges && make_plan(a, r, (int*)ring_mem, pl);
+  // sequences with nothing to attend: O = 0, LSE = -inf (spread over the
+  // grid; the lengths were just read by the plan)
   for (int b = g; b < a.batch; b += gridDim.x) {
     if (units_of(a, b) == 0) {
       for (int i = tid; i < a.heads * (kDV / 4); i += kThreads)
@@ -956,16 +974,7 @@ mla_decode_kernel(DecodeArgs a) {
       if (tid == 0) a.ws_seq[b] = int2{0, 0};
     }
   }
-  // workgroups are dealt round-robin to the 8 XCDs: each XCD gets a run of
-  // consecutive ranges with all their slabs, so the slabs share KV lines in
-  // one L2 and the pieces of a sequence mostly merge from it
-  const int idx = g / 8;
-  const int r = (g % 8) * a.per_xcd + idx / a.slabs;
-  const int slab = idx % a.slabs;
-  if (r >= a.ranges) return;
-
-  Plan pl;
-  if (!make_plan(a, r, (int*)ring_mem, pl)) return;
+  if (!has_work) return;
 
   const int head = slab * (HG * 32) + hg * 32 + (lane & 31);
   const bool head_ok = head < a.heads;
@@ -1122,13 +1131,20 @@ mla_decode_kernel(DecodeArgs a) {
           LDS_AS float* const stabs = (LDS_AS float*)(ring + kFillRing * kSlotBytes);
           auto pos_buf = [&](int pos) { return ring + pos * kSlotBytes; };
           auto pos_tab = [&](int pos) { return stabs + pos * (4 * kTS); };
+          // (the rows of slots 0..2, and their indices, are all requested
+          // before the first is needed: one memory latency, not three)
           RawRow<KVM> rr;
-          load_row<KVM>(rr, a, fill_src(0), fq);
-          int next_row = fill_src(3);
-          fill_row<KVM>(pos_buf(0), pos_tab(0), rr, frow, fq);
-          load_row<KVM>(rr, a, fill_src(1), fq);
-          fill_row<KVM>(pos_buf(1), pos_tab(1), rr, frow, fq);
-          load_row<KVM>(rr, a, fill_src(2), fq);
+          int next_row;
+          {
+            const int i0 = fill_src(0), i1 = fill_src(1), i2 = fill_src(2);
+            next_row = fill_src(3);
+            RawRow<KVM> r0, r1;
+            load_row<KVM>(r0, a, i0, fq);
+            load_row<KVM>(r1, a, i1, fq);
+            load_row<KVM>(rr, a, i2, fq);
+            fill_row<KVM>(pos_buf(0), pos_tab(0), r0, frow, fq);
+            fill_row<KVM>(pos_buf(1), pos_tab(1), r1, frow, fq);
+          }
           wait_vm_lgkm0<63>();
           barrier();
           qk_preload<NSPLIT, TILED>(kb, pos_buf(0), tab);
