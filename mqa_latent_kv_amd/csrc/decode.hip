@@ -1268,13 +1268,14 @@ struct MergeArgs {
   int32_t heads;
 };
 
-constexpr int kMergeHeads = 16;  // heads per merge workgroup, 16 threads each
+constexpr int kMergeHeads = 2;  // heads per merge workgroup, 128 threads each
 
 // O = sum_s 2^(lse_s - M) O_s / sum_s 2^(lse_s - M) with M = max_s lse_s, and
 // LSE = M + log2 sum_s 2^(lse_s - M) (back to natural log), for sequences the
 // decode kernel split over several ranges; piece s sits in workspace slot
-// first + s.  A thread owns 8 float4 columns of one head and keeps all eight
-// loads of a piece in flight.
+// first + s.  A thread owns one float4 column group of one head, so the grid
+// has B * H / 2 workgroups, and keeps the loads of up to eight pieces in
+// flight.
 __global__ void __launch_bounds__(kThreads) mla_merge_kernel(MergeArgs m) {
   const int b = blockIdx.x;
   const int2 info = m.seq[b];
@@ -1293,7 +1294,7 @@ __global__ void __launch_bounds__(kThreads) mla_merge_kernel(MergeArgs m) {
 #pragma unroll
   for (int u = 0; u < U; ++u) acc[u] = f32x4{};
   float wsum = 0.0f;
-#pragma unroll 2
+#pragma unroll 8
   for (int s = 0; s < nsplit; ++s) {
     const float l = lse_col[(size_t)s * m.heads];
     const float wgt = l == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(l - mx);

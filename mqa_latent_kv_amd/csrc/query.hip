@@ -1,6 +1,7 @@
 // query.hip - MLA query front end for gfx950 (MI355X).
 //
-// What is computed, per token b (FlashMLA query path, "MlaQuery" forward):
+// What is computed, per token b (the query front end of the vLLM MlaQuery
+// page, its narrow-batch `kernel` and wide-batch `tiled` forms):
 //   rr  = 1 / sqrt(sum_k x[k]^2 / 1536 + eps)      x = qkv[b, 0:1536] (q_a)
 //   xn  = bf16((x * rr) * w_qa)                    RMSNorm
 //   qb  = bf16(xn . W_qb^T)                        [H, 192]: 128 nope + 64 rope
@@ -55,37 +56,65 @@ struct QueryArgs {
   float eps;
 };
 
-// e4m3fn code of x: round to nearest even, saturate to +-448, NaN -> 0x7F.
-// Callers pass the exact product of a bf16 value and the fp32 q_scale_inv
-// (at most 8 + 24 significant bits, exact in f64), so this is the single
-// rounding of the exact value; an fp32 product would first round onto e4m3
-// midpoints (v * 0.3f lands next to one whenever v * 3/10 is one) and then
-// break the tie the wrong way.  With the exponent e of |x| (normal range e >=
-// -6) the mantissa step is 2^(e-3), so rint(|x| * 2^(3-e)) is the rounded
-// significand in units of that step (8..16, 16 carrying into the next
-// exponent); below 2^-6 the step is the subnormal 2^-9.  Scaling by powers of
-// two is exact and rint rounds to nearest even.
-__device__ __forceinline__ uint8_t e4m3_code(double x) {
-  if (x != x) return 0x7F;
-  const uint32_t sign = x < 0.0 || (x == 0.0 && __builtin_signbit(x)) ? 0x80u : 0u;
-  const double a = __builtin_fabs(x);
+// e4m3fn code of the exact product v * q (v at most 24 significant bits, q
+// fp32): round to nearest even, saturate to +-448, NaN -> 0x7F.  The
+// product is rounded once, from its exact value: an fp32 product can land
+// exactly on an e4m3 midpoint (v * 0.3f does whenever v * 3/10 is one) and
+// would then break the tie by its own rounding error.  hi = fl(v * q) and
+// lo = fma(v, q, -hi) = v * q - hi exactly; every e4m3 midpoint is an fp32
+// number, so the exact value lies on the same side of each midpoint as hi,
+// except when hi is the midpoint itself, where the sign of lo (in magnitude)
+// decides and lo = 0 is a true tie.  Normal range (|hi| >= 2^-6): the three
+// leading mantissa bits of hi are the e4m3 mantissa and the twenty below are
+// the discarded part (half = 0x80000); below 2^-6 the step is the subnormal
+// 2^-9 and |hi| * 512 (exact) is rounded to an integer 0..8.
+__host__ __device__ __forceinline__ uint8_t e4m3_of_product(float v, float q) {
+  const float hi = v * q;
+  if (hi != hi) return 0x7F;
+  const float lo = __builtin_fmaf(v, q, -hi);
+  const uint32_t hb = __builtin_bit_cast(uint32_t, hi);
+  const uint32_t sign = (hb >> 24) & 0x80u;
+  const float a = __builtin_fabsf(hi);
+  // where the exact magnitude lies relative to |hi|: above (+1), below (-1)
+  const int dir = lo == 0.0f ? 0 : ((lo > 0.0f) == (hi > 0.0f) ? 1 : -1);
   uint32_t code;
-  if (a >= 448.0) {
+  if (a >= 448.0f) {
     code = 0x7E;
-  } else if (a < 0.015625) {  // 2^-6: subnormal codes 0..7 (8 is the smallest normal)
-    code = (uint32_t)__builtin_rint(a * 512.0);
+  } else if (a < 0.015625f) {  // 2^-6: subnormal codes 0..7 (8 is the smallest normal)
+    const float t = a * 512.0f;
+    const float n = __builtin_floorf(t);
+    const float f = t - n;
+    const uint32_t ni = (uint32_t)n;
+    const bool up = f > 0.5f || (f == 0.5f && (dir > 0 || (dir == 0 && (ni & 1u))));
+    code = ni + (up ? 1u : 0u);
   } else {
-    const int e = (int)((__double_as_longlong(a) >> 52) & 0x7FF) - 1023;  // -6 .. 8
-    const uint32_t m = (uint32_t)__builtin_rint(__builtin_ldexp(a, 3 - e));  // 8 .. 16
-    code = (uint32_t)(e + 7) * 8 + (m - 8);  // m == 16 carries into the exponent field
-    code = code > 0x7E ? 0x7E : code;         // rounding up past 448 saturates
+    const uint32_t ab = __builtin_bit_cast(uint32_t, a);
+    const uint32_t e = (ab >> 23) - 120u;  // e4m3 exponent field 1..15
+    const uint32_t m3 = (ab >> 20) & 7u, rest = ab & 0xFFFFFu;
+    const bool up = rest > 0x80000u || (rest == 0x80000u && (dir > 0 || (dir == 0 && (m3 & 1u))));
+    code = ((e << 3) | m3) + (up ? 1u : 0u);  // a mantissa carry moves into the exponent field
+    code = code > 0x7Eu ? 0x7Eu : code;       // rounding up past 448 saturates
   }
   return (uint8_t)(sign | code);
 }
 
+// Sum over the 64 lanes, every lane receiving it, in registers only: two
+// quad permutations, the half-row and row mirrors (16 lanes summed), then
+// the 16- and 32-lane swaps.  (A shuffle loop would go through ds_bpermute,
+// six dependent round trips through the LDS crossbar.)
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
 __device__ __forceinline__ float wave_sum(float v) {
-  for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off);
-  return v;
+  v += dpp_f<0xB1>(v);   // quad_perm [1,0,3,2]
+  v += dpp_f<0x4E>(v);   // quad_perm [2,3,0,1]
+  v += dpp_f<0x141>(v);  // row_half_mirror: the other quad of the 8-lane half
+  v += dpp_f<0x140>(v);  // row_mirror: the other half of the 16-lane row
+  const auto r16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = __uint_as_float(r16[0]) + __uint_as_float(r16[1]);
+  const auto r32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(r32[0]) + __uint_as_float(r32[1]);
 }
 
 // ---------------------------------------------------------------- RMSNorm + Q_B
@@ -97,22 +126,49 @@ __global__ void __launch_bounds__(kThreads) mla_qb_kernel(QueryArgs a) {
   const int n0 = blockIdx.x * 32;     // first W_qb row (output column) of this workgroup
   const int m0 = blockIdx.y * kTok;   // first token
 
+  // Every load is issued before any is needed (one memory latency for the
+  // whole workgroup): this wave's W_qb fragments, w_qa and the q_a rows of
+  // the eight tokens it normalises.
+  // B fragments of this wave's 24 k-steps (reduction columns 384w ..): lane
+  // l holds W_qb row n0 + l%32, columns 16ks + 8*(l/32) .. +7
+  constexpr int KSW = kQA / 16 / 4;
+  const int nrow = n0 + (lane & 31), h8 = 8 * (lane >> 5);
+  const bool row_ok = nrow < a.heads * kQB;
+  // (loads are unconditional, from a clamped valid address, and the value is
+  // dropped afterwards: a guarded load becomes a branch around it, and the
+  // branches serialise the loads)
+  const int nrow_c = row_ok ? nrow : a.heads * kQB - 1;
+  bf16x8 bf[KSW];
+#pragma unroll
+  for (int i = 0; i < KSW; ++i) {
+    const int k = 16 * (KSW * w + i) + h8;
+    bf[i] = *(const bf16x8*)(a.w_qb + (size_t)nrow_c * kQA + k);
+  }
+#pragma unroll
+  for (int i = 0; i < KSW; ++i) bf[i] = row_ok ? bf[i] : bf16x8{};
   // RMSNorm: wave w normalises tokens m0 + 8w .. +7; lane i holds columns
   // 8i + 512k .. +7 (k = 0..2)
+  bf16x8 wq[3], xr[8][3];
+#pragma unroll
+  for (int k = 0; k < 3; ++k) wq[k] = *(const bf16x8*)(a.w_qa + 512 * k + 8 * lane);
+#pragma unroll
   for (int t = 0; t < 8; ++t) {
-    const int m = 8 * w + t, b = m0 + m;
+    const int b = min(m0 + 8 * w + t, a.batch - 1);
+#pragma unroll
+    for (int k = 0; k < 3; ++k) xr[t][k] = *(const bf16x8*)(a.qkv + (size_t)b * a.qkv_stride + 512 * k + 8 * lane);
+  }
+#pragma unroll
+  for (int t = 0; t < 8; ++t)
+#pragma unroll
+    for (int k = 0; k < 3; ++k) xr[t][k] = m0 + 8 * w + t < a.batch ? xr[t][k] : bf16x8{};
+#pragma unroll
+  for (int t = 0; t < 8; ++t) {
+    const int m = 8 * w + t;
     float x[24];
-    if (b < a.batch) {
 #pragma unroll
-      for (int k = 0; k < 3; ++k) {
-        const bf16x8 v = *(const bf16x8*)(a.qkv + (size_t)b * a.qkv_stride + 512 * k + 8 * lane);
+    for (int k = 0; k < 3; ++k)
 #pragma unroll
-        for (int e = 0; e < 8; ++e) x[8 * k + e] = (float)v[e];
-      }
-    } else {
-#pragma unroll
-      for (int e = 0; e < 24; ++e) x[e] = 0.0f;
-    }
+      for (int e = 0; e < 8; ++e) x[8 * k + e] = (float)xr[t][k][e];
     float ss = 0.0f;
 #pragma unroll
     for (int e = 0; e < 24; ++e) ss += x[e] * x[e];
@@ -120,24 +176,11 @@ __global__ void __launch_bounds__(kThreads) mla_qb_kernel(QueryArgs a) {
     const float rr = 1.0f / __builtin_sqrtf(ss / (float)kQA + a.eps);
 #pragma unroll
     for (int k = 0; k < 3; ++k) {
-      const bf16x8 wv = *(const bf16x8*)(a.w_qa + 512 * k + 8 * lane);
       bf16x8 o;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) o[e] = (__bf16)((x[8 * k + e] * rr) * (float)wv[e]);
+      for (int e = 0; e < 8; ++e) o[e] = (__bf16)((x[8 * k + e] * rr) * (float)wq[k][e]);
       *(LDS_AS bf16x8*)((lds_char*)xn_mem + m * kXnPitch + 2 * (512 * k + 8 * lane)) = o;
     }
-  }
-
-  // B fragments of this wave's 24 k-steps (reduction columns 384w ..): lane
-  // l holds W_qb row n0 + l%32, columns 16ks + 8*(l/32) .. +7
-  constexpr int KSW = kQA / 16 / 4;
-  const int nrow = n0 + (lane & 31), h8 = 8 * (lane >> 5);
-  const bool row_ok = nrow < a.heads * kQB;
-  bf16x8 bf[KSW];
-#pragma unroll
-  for (int i = 0; i < KSW; ++i) {
-    const int k = 16 * (KSW * w + i) + h8;
-    bf[i] = row_ok ? *(const bf16x8*)(a.w_qb + (size_t)nrow * kQA + k) : bf16x8{};
   }
   __syncthreads();
   f32x16 acc = {};
@@ -173,7 +216,7 @@ __global__ void __launch_bounds__(kThreads) mla_qb_kernel(QueryArgs a) {
     if (b >= a.batch) continue;
     const __bf16 v = (__bf16)acc[i];
     if (r < kNope) a.qn[((size_t)b * a.heads + head) * kNope + r] = v;
-    else a.out[((size_t)b * a.heads + head) * kOut + kDV + (r - kNope)] = e4m3_code((double)(float)v * (double)qsi);
+    else a.out[((size_t)b * a.heads + head) * kOut + kDV + (r - kNope)] = e4m3_of_product((float)v, qsi);
   }
 }
 
@@ -191,21 +234,32 @@ __global__ void __launch_bounds__(kThreads) mla_ql_kernel(QueryArgs a) {
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int head = blockIdx.x, c0 = blockIdx.y * 128, m0 = blockIdx.z * kTok;
 
-  // stage W_uk[head][0..127][c0..c0+127]: 2048 chunks of 16 bytes
-  for (int i = tid; i < 128 * 16; i += kThreads) {
-    const int p = i >> 4, ch = i & 15;  // row p, chunk ch (8 columns)
-    const u32x4 v = *(const u32x4*)(a.w_uk + ((size_t)head * kNope + p) * kDV + c0 + 8 * ch);
-    const int g = ch >> 3, x = ch & 7;
-    *(LDS_AS u32x4*)(uk + g * kUkGroup + p * 128 + 16 * (x ^ uk_swz(p))) = v;
-  }
   // A fragments: token m0 + l%32, nope columns 16ks + 8*(l/32) .. +7
+  // (unconditional loads from a clamped row; rows past the batch are zeroed)
   const int b = m0 + (lane & 31);
   const bool b_ok = b < a.batch;
+  const int b_c = b_ok ? b : a.batch - 1;
   bf16x8 af[kNope / 16];
 #pragma unroll
   for (int ks = 0; ks < kNope / 16; ++ks)
-    af[ks] = b_ok ? *(const bf16x8*)(a.qn + ((size_t)b * a.heads + head) * kNope + 16 * ks + 8 * (lane >> 5))
-                  : bf16x8{};
+    af[ks] = *(const bf16x8*)(a.qn + ((size_t)b_c * a.heads + head) * kNope + 16 * ks + 8 * (lane >> 5));
+  // stage W_uk[head][0..127][c0..c0+127]: 2048 chunks of 16 bytes, all eight
+  // of a thread loaded before any is stored
+  constexpr int kStage = 128 * 16 / kThreads;
+  u32x4 wv[kStage];
+#pragma unroll
+  for (int j = 0; j < kStage; ++j) {
+    const int i = tid + j * kThreads, p = i >> 4, ch = i & 15;  // row p, chunk ch (8 columns)
+    wv[j] = *(const u32x4*)(a.w_uk + ((size_t)head * kNope + p) * kDV + c0 + 8 * ch);
+  }
+#pragma unroll
+  for (int j = 0; j < kStage; ++j) {
+    const int i = tid + j * kThreads, p = i >> 4, ch = i & 15;
+    const int g = ch >> 3, x = ch & 7;
+    *(LDS_AS u32x4*)(uk + g * kUkGroup + p * 128 + 16 * (x ^ uk_swz(p))) = wv[j];
+  }
+#pragma unroll
+  for (int ks = 0; ks < kNope / 16; ++ks) af[ks] = b_ok ? af[ks] : bf16x8{};
   __syncthreads();
   // B operand B[k][n] = W_uk[head][16ks + k][c] by transposed reads: lane l
   // needs column n = l%32 of rows k = 8*(l/32) + i, i = 0..7, the order the A
@@ -237,7 +291,7 @@ __global__ void __launch_bounds__(kThreads) mla_ql_kernel(QueryArgs a) {
     const int bb = m0 + 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3);
     if (bb >= a.batch) continue;
     const float v = (float)(__bf16)acc[i];
-    a.out[((size_t)bb * a.heads + head) * kOut + c] = e4m3_code((double)v * (double)qsi);
+    a.out[((size_t)bb * a.heads + head) * kOut + c] = e4m3_of_product(v, qsi);
   }
 }
 
