@@ -12,7 +12,10 @@ seeded explicitly, in a fixed order, and returned as numpy arrays of raw bits:
   * fp32 scales as ``float32``, int32 tables as ``int32``.
 
 Draw order for a decode input: q, seqlens, KV pool (nope codes / bf16 rows,
-then rope, then scales), block table, top-k lists.  The per-workload recipes
+then rope, then scales; or, for the per-tensor FP8 cache, all 576 codes of each
+row, then the one k_scale_inv), block table, top-k lists.  For a KV-cache
+insert: qkv rows, w_kva, the cache's prior contents, the slots, then which
+tokens are skipped (slot -1).  The per-workload recipes
 (shapes, distributions, page pools) are in ``WORKLOADS``.
 """
 from __future__ import annotations
@@ -25,6 +28,7 @@ D_QK = 576
 D_NOPE = 512
 D_ROPE = 64
 FP8_ROW_BYTES = 640
+QKV_WIDTH = 2112  # q_a 1536 | latent KV 512 | rope key 64
 _CHUNK = 1 << 24  # elements per host draw, bounds peak memory for large pools
 
 
@@ -124,6 +128,9 @@ def make_decode_inputs(
         kv = fp8_records(codes, rope)
         del codes, rope
         kv_scales = log_uniform_scales(g, (num_pages, PAGE, D_NOPE // 128))
+    elif kv_format == "fp8_tensor":
+        kv = fp8_normal(g, (num_pages, PAGE, D_QK))
+        kv_scales = log_uniform_scales(g, (1,), -0.5, 0.5)  # k_scale_inv
     else:
         raise ValueError(kv_format)
     perm = torch.randperm(num_pages, generator=g).numpy().astype(np.int32)
@@ -172,6 +179,32 @@ def make_query_inputs(seed: int, *, batch: int, heads: int, width: int = 1536, q
     }
 
 
+def make_insert_inputs(seed: int, *, tokens: int, num_pages: int, skipped: int = 0, k_scale_inv: float = 37.0,
+                       eps: float = 1e-6) -> dict:
+    """Seeded inputs for the KV-cache insert: qkv bf16 [T, 2112] N(0,1); w_kva
+    bf16 N(1, 0.1^2) [512]; the per-tensor FP8 cache's prior contents, e4m3
+    codes of N(0,1) samples [num_pages, 64, 576]; int64 slots, T distinct slots
+    of the pool in random order, then ``skipped`` randomly chosen tokens set to
+    -1."""
+    g = _gen(seed)
+    qkv = bf16_normal(g, (tokens, QKV_WIDTH))
+    w_kva = bf16_normal(g, (D_NOPE,), mean=1.0, std=0.1)
+    cache = fp8_normal(g, (num_pages, PAGE, D_QK))
+    assert tokens <= num_pages * PAGE
+    slots = torch.randperm(num_pages * PAGE, generator=g)[:tokens].numpy().astype(np.int64)
+    if skipped:
+        slots[torch.randperm(tokens, generator=g)[:skipped].numpy()] = -1
+    return {
+        "qkv": qkv,
+        "w_kva": w_kva,
+        "cache": cache,
+        "slots": slots,
+        "k_scale_inv": float(k_scale_inv),
+        "eps": float(eps),
+        "tokens": tokens,
+    }
+
+
 # Workloads: shapes and distributions of the decode configurations this library
 # is measured and tested on.  Seed k for workload k.
 WORKLOADS = {
@@ -180,6 +213,7 @@ WORKLOADS = {
     "paged_bf16_4096": dict(seed=2, batch=64, heads=128, seqlens=[4096] * 64, num_pages=4096, pages_per_seq=64),
     "fp8_cache": dict(seed=3, batch=32, heads=64, seqlen_range=(8192, 32768), num_pages=16384, pages_per_seq=512, kv_format="fp8"),
     "topk_sparse": dict(seed=4, batch=32, heads=128, seqlens=[65536] * 32, num_pages=32768, pages_per_seq=1024, kv_format="fp8", topk=2048, topk_pad_max=256),
+    "insert_decode": dict(seed=6, batch=64, heads=128, seqlens=[4096] * 64, num_pages=4096, pages_per_seq=64, kv_format="fp8_tensor"),
     "query_decode": dict(seed=5, batch=64, heads=8, seqlens=[8192] * 64, num_pages=8192, pages_per_seq=128, q_format="fp8", q_descale=8.0),
 }
 

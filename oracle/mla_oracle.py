@@ -35,6 +35,16 @@ What is computed (sources are the three pages this library is built from):
   rope values kept in bf16; value = code * scale (the issue's per-buffer
   "dequant" K tiles).
 
+* Per-tensor FP8 cache (the layout ``MlaQuery.insert`` writes): all 576
+  columns of a row, rope included, are e4m3fn codes of value * k_scale_inv
+  with one fp32 k_scale_inv for the whole cache; value = code / k_scale_inv.
+
+* KV-cache insert (vLLM ``MlaQuery`` API page, ``insert``): for each new
+  token with slot >= 0, RMSNorm the 512 latent columns qkv[1536:2048] with
+  ``w_kva`` (mean over those 512 columns), round to bf16, then write the e4m3
+  codes of (normed * k_scale_inv) and of (qkv[2048:2112] * k_scale_inv) to row
+  offset = slot % 64 of page = slot // 64.  Slots < 0 write nothing.
+
 * Query front end (vLLM ``MlaQuery`` API page, ``kernel``): RMSNorm of the
   1536-wide q_a part of ``qkv`` with ``w_qa``; Q_B projection to 192 rows per
   head (128 nope + 64 rope); absorption of the nope part through W_UK[h]
@@ -67,10 +77,14 @@ D_NOPE = 512
 D_ROPE = 64
 D_V = 512
 FP8_ROW_BYTES = 640  # 512 e4m3 codes + 64 bf16 rope values
+FP8T_ROW_BYTES = 576  # per-tensor FP8 cache: 576 e4m3 codes
 FP8_TILE = 128  # columns per fp32 scale
 Q_A = 1536  # width of the q_a part of qkv
 QB_ROWS = 192  # Q_B rows per head: 128 nope + 64 rope
 QB_NOPE = 128
+KV_LATENT = 1536  # first qkv column of the latent KV row
+KV_ROPE = 2048  # first qkv column of the rope key
+QKV_WIDTH = 2112  # q_a 1536 | latent 512 | rope 64
 
 # ----------------------------------------------------------------------------- decode
 
@@ -134,7 +148,9 @@ def dequant_rows(kv, rows: np.ndarray, kv_format: str, kv_scales=None) -> np.nda
     bf16 cache: ``kv`` is uint16 [pages, 64, 576].
     FP8 cache: ``kv`` is uint8 [pages, 64, 640] (512 e4m3 codes, then the 64 rope
     values as little-endian bf16) and ``kv_scales`` float32 [pages, 64, 4]; column
-    d < 512 is code * scale[d // 128]."""
+    d < 512 is code * scale[d // 128].
+    Per-tensor FP8 cache (``fp8_tensor``): ``kv`` is uint8 [pages, 64, 576], all
+    e4m3 codes, and ``kv_scales`` the one fp32 k_scale_inv; value = code / k_scale_inv."""
     if kv_format == "bf16":
         flat = np.asarray(kv).reshape(-1, D_QK)
         return bf16_bits_to_f64(flat[rows])
@@ -146,6 +162,10 @@ def dequant_rows(kv, rows: np.ndarray, kv_format: str, kv_scales=None) -> np.nda
         rope = np.ascontiguousarray(flat[:, D_NOPE:]).view("<u2")
         k[:, D_NOPE:] = bf16_bits_to_f64(rope)
         return k
+    if kv_format == "fp8_tensor":
+        flat = np.asarray(kv).reshape(-1, FP8T_ROW_BYTES)[rows]
+        ksi = float(np.asarray(kv_scales, dtype=np.float32).reshape(-1)[0])
+        return e4m3_to_f64(flat) / ksi
     raise ValueError(f"unknown kv_format {kv_format!r}")
 
 
@@ -212,9 +232,10 @@ def mla_decode(
 # ----------------------------------------------------------------------------- query
 
 
-def rms_norm_q(x: np.ndarray, w: np.ndarray, eps: float):
-    """RMSNorm of the q_a rows: rr = 1 / sqrt(sum(x^2) / 1536 + eps), applied as
-    (x * rr) * w, before the bf16 rounding."""
+def rms_norm(x: np.ndarray, w: np.ndarray, eps: float):
+    """RMSNorm over the last axis (width n): rr = 1 / sqrt(sum(x^2) / n + eps),
+    applied as (x * rr) * w, before the bf16 rounding.  The q_a rows have
+    n = 1536, the latent KV rows n = 512."""
     ss = (x * x).sum(axis=-1, keepdims=True)
     rr = 1.0 / np.sqrt(ss / x.shape[-1] + eps)
     return (x * rr) * w
@@ -238,7 +259,7 @@ def mla_query(qkv, w_qa, w_qb, w_uk, q_scale_inv: float, eps: float = 1e-6, head
     wqb = bf16_bits_to_f64(w_qb)  # [H*192, 1536]
     wuk = bf16_bits_to_f64(w_uk)  # [H, 128, 512]
     H = wuk.shape[0] if heads is None else heads
-    xn_pre = rms_norm_q(x, w, eps)
+    xn_pre = rms_norm(x, w, eps)
     xn = bf16_round(xn_pre)
     qb_pre = (xn @ wqb.T).reshape(B, H, QB_ROWS)
     qb = bf16_round(qb_pre)
@@ -261,3 +282,42 @@ def mla_query(qkv, w_qa, w_qb, w_uk, q_scale_inv: float, eps: float = 1e-6, head
         "fp8_in": fp8_in,
     }
 
+
+# ----------------------------------------------------------------------------- KV-cache insert
+
+
+def slot_page_offset(slot: int, page_size: int = PAGE):
+    """Page and row offset of a cache slot (integer division, exact)."""
+    return int(slot) // page_size, int(slot) % page_size
+
+
+def kv_insert(qkv, w_kva, cache, slots, k_scale_inv: float, eps: float = 1e-6):
+    """The KV-cache insert of the new tokens' latent rows.
+
+    qkv: uint16 bf16 bits [T, >=2112] (columns 1536..2047 the latent KV row,
+    2048..2111 the rope key).  w_kva: uint16 [512].  cache: uint8 e4m3 codes
+    [pages, 64, 576] (not modified; a written copy is returned).  slots: int
+    [T], slot < 0 skips the token.  k_scale_inv: the fp32 per-tensor factor.
+
+    Returns a dict: ``cache`` (the written copy), ``normed_pre`` [T, 512] f64
+    (before the bf16 rounding), ``normed`` (after it) and ``fp8_in`` [T, 576]
+    (the values that are encoded).  Duplicate non-negative slots: the later
+    token's row wins (the GPU leaves that case unspecified).
+    """
+    qkv = np.asarray(qkv)
+    x = bf16_bits_to_f64(qkv[:, KV_LATENT:KV_ROPE])
+    rope = bf16_bits_to_f64(qkv[:, KV_ROPE:QKV_WIDTH])
+    w = bf16_bits_to_f64(w_kva)
+    normed_pre = rms_norm(x, w, eps)
+    normed = bf16_round(normed_pre)
+    ksi = float(np.float32(k_scale_inv))
+    fp8_in = np.concatenate([normed * ksi, rope * ksi], axis=-1)
+    codes = f64_to_e4m3(fp8_in)
+    out = np.array(cache, dtype=np.uint8, copy=True)
+    page_size = out.shape[1]
+    for t, slot in enumerate(np.asarray(slots).reshape(-1)):
+        if slot < 0:
+            continue
+        page, offset = slot_page_offset(slot, page_size)
+        out[page, offset, :] = codes[t]
+    return {"cache": out, "normed_pre": normed_pre, "normed": normed, "fp8_in": fp8_in, "codes": codes}

@@ -436,3 +436,140 @@ def test_query_identity_weights_closed_form():
     for r in range(128, 192):
         np.testing.assert_array_equal(res["out"][:, 0, 512 + r - 128], codecs.f64_to_e4m3(xn[:, 7 * r] * 0.125))
     assert np.all(codecs.e4m3_to_f64(res["out"][:, 0, :384]) == 0)
+
+
+# ------------------------------------------------------------------ KV-cache insert, per-tensor FP8 cache
+
+
+def _bf16_bits(values):
+    return torch.tensor(np.asarray(values, dtype=np.float32)).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+
+
+def _insert_rows(latent, rope, T=None):
+    """qkv bf16 bits [T, 2112]: q_a zeros, then the given latent and rope rows."""
+    latent = np.atleast_2d(np.asarray(latent, dtype=np.float64))
+    rope = np.atleast_2d(np.asarray(rope, dtype=np.float64))
+    T = latent.shape[0]
+    x = np.zeros((T, 2112))
+    x[:, 1536:2048] = latent
+    x[:, 2048:2112] = rope
+    return _bf16_bits(x)
+
+
+def test_insert_slot_placement_by_hand():
+    """Slots map to (page, offset) = (slot // 64, slot % 64); -1 writes nothing
+    and every other byte of the cache keeps its prior value."""
+    inp = synth.make_insert_inputs(31, tokens=5, num_pages=3)
+    slots = np.array([130, -1, 0, 191, 64], dtype=np.int64)
+    where = {0: (2, 2), 2: (0, 0), 3: (2, 63), 4: (1, 0)}  # written out by hand
+    res = mo.kv_insert(inp["qkv"], inp["w_kva"], inp["cache"], slots, inp["k_scale_inv"], inp["eps"])
+    out = res["cache"]
+    touched = np.zeros(out.shape[:2], dtype=bool)
+    for t, (pg, off) in where.items():
+        np.testing.assert_array_equal(out[pg, off], res["codes"][t])
+        touched[pg, off] = True
+    np.testing.assert_array_equal(out[~touched], inp["cache"][~touched])
+    assert not np.array_equal(res["codes"][1], out[0, 1])  # the skipped token's row landed nowhere
+
+
+def test_insert_constant_rows_closed_form():
+    """A constant latent row c has RMS |c|, so with w = 1 and eps = 0 every
+    normalised value is sign(c); the rope columns are encoded unnormalised.
+    The e4m3fn codes follow from the format's definition: 1.0 = 0x38, 4.0 =
+    0x48, 3.0 = 0x44, 0.5 = 0x30, sign bit 0x80."""
+    lat = np.array([[0.75] * 512, [-3.0] * 512, [2.0**-9] * 512])
+    rope = np.array([[1.5] * 64, [-1.5] * 64, [0.125] * 64])
+    qkv = _insert_rows(lat, rope)
+    ones = _bf16_bits(np.ones(512))
+    cache = np.zeros((1, 64, 576), dtype=np.uint8)
+    slots = np.array([0, 1, 2])
+    r1 = mo.kv_insert(qkv, ones, cache, slots, 1.0, 0.0)["cache"][0]
+    assert np.all(r1[0, :512] == 0x38) and np.all(r1[1, :512] == 0xB8) and np.all(r1[2, :512] == 0x38)
+    assert np.all(r1[0, 512:] == 0x3C) and np.all(r1[1, 512:] == 0xBC) and np.all(r1[2, 512:] == 0x20)
+    r4 = mo.kv_insert(qkv, ones, cache, slots, 4.0, 0.0)["cache"][0]
+    assert np.all(r4[0, :512] == 0x48) and np.all(r4[1, :512] == 0xC8)
+    # rope 1.5 * 4 = 6.0 = 1.5 * 2^2: exponent field 9, mantissa 100
+    assert np.all(r4[0, 512:] == 0x4C) and np.all(r4[2, 512:] == 0x30)
+    half = _bf16_bits(np.full(512, 0.5))
+    rh = mo.kv_insert(qkv, half, cache, slots, 1.0, 0.0)["cache"][0]
+    assert np.all(rh[0, :512] == 0x30) and np.all(rh[1, :512] == 0xB0)
+    # rope 1.5 * 2 = 3.0
+    assert np.all(mo.kv_insert(qkv, ones, cache, slots, 2.0, 0.0)["cache"][0][0, 512:] == 0x44)
+
+
+def test_insert_rms_invariants():
+    """With w = 1 and eps = 0 the normalised rows have mean square 1 and are
+    unchanged by scaling the input by a power of two; a huge eps reduces the
+    norm to x * w / sqrt(eps); an all-zero row gives zero codes."""
+    inp = synth.make_insert_inputs(32, tokens=6, num_pages=1)
+    ones = _bf16_bits(np.ones(512))
+    cache = np.zeros((1, 64, 576), dtype=np.uint8)
+    slots = np.arange(6)
+    r = mo.kv_insert(inp["qkv"], ones, cache, slots, 1.0, 0.0)
+    np.testing.assert_allclose((r["normed_pre"] ** 2).mean(axis=1), 1.0, rtol=1e-13)
+    x = codecs.bf16_bits_to_f64(inp["qkv"])
+    r8 = mo.kv_insert(codecs.f64_to_bf16_bits(x * 8.0), ones, cache, slots, 1.0, 0.0)
+    np.testing.assert_array_equal(r8["codes"][:, :512], r["codes"][:, :512])
+    big = mo.kv_insert(inp["qkv"], inp["w_kva"], cache, slots, 1.0, 1e12)
+    w = codecs.bf16_bits_to_f64(inp["w_kva"])
+    np.testing.assert_allclose(big["normed_pre"], x[:, 1536:2048] * w / 1e6, rtol=1e-9)
+    z = mo.kv_insert(_insert_rows(np.zeros((1, 512)), np.zeros((1, 64))), inp["w_kva"], cache, [0], 37.0, 1e-6)
+    assert np.all(z["cache"][0, 0] == 0)
+
+
+def test_insert_matches_torch_rmsnorm_and_float8_cast():
+    """The normalised latent row against torch's RMSNorm (float64), and the
+    codes against torch's float8_e4m3fn cast, with a power-of-two k_scale_inv so
+    that the product is exact in float32."""
+    inp = synth.make_insert_inputs(33, tokens=9, num_pages=2, skipped=2)
+    res = mo.kv_insert(inp["qkv"], inp["w_kva"], inp["cache"], inp["slots"], 16.0, inp["eps"])
+    x = torch.from_numpy(inp["qkv"].view(np.int16)).view(torch.bfloat16).double()
+    w = torch.from_numpy(inp["w_kva"].view(np.int16)).view(torch.bfloat16).double()
+    ref = torch.nn.functional.rms_norm(x[:, 1536:2048], (512,), w, eps=inp["eps"])
+    np.testing.assert_allclose(res["normed_pre"], ref.numpy(), rtol=1e-12, atol=1e-15)
+    normed = torch.from_numpy(res["normed"]).float()
+    lat = (normed * 16.0).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    rope = (x[:, 2048:2112].float() * 16.0).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    np.testing.assert_array_equal(res["codes"][:, :512], lat)
+    np.testing.assert_array_equal(res["codes"][:, 512:], rope)
+
+
+def test_per_tensor_dequant_matches_torch_float8():
+    inp = synth.make_decode_inputs(34, batch=1, heads=2, seqlens=[90], kv_format="fp8_tensor")
+    ksi = float(inp["kv_scales"][0])
+    rows = np.arange(0, 128, 5)
+    ours = mo.dequant_rows(inp["kv"], rows, "fp8_tensor", inp["kv_scales"])
+    codes = torch.from_numpy(inp["kv"].reshape(-1, 576)[rows]).view(torch.float8_e4m3fn).double()
+    np.testing.assert_array_equal(ours, (codes / ksi).numpy())
+
+
+def test_per_tensor_decode_equals_bf16_decode_of_its_values():
+    """With a power-of-two k_scale_inv every dequantised value is exact in bf16,
+    so decode over the per-tensor FP8 cache equals decode over a bf16 cache that
+    holds those values (decoded here by torch), dense and top-k."""
+    inp = synth.make_decode_inputs(35, batch=2, heads=4, seqlens=[130, 77], kv_format="fp8_tensor", topk=0)
+    ksi = np.array([0.25], dtype=np.float32)
+    vals = torch.from_numpy(inp["kv"]).view(torch.float8_e4m3fn).float() / 0.25
+    kv16 = vals.to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(vals.to(torch.bfloat16).float().numpy(), vals.numpy())
+    topk = np.array([[5, 129, -1, 64, 7], [76, 0, 3, 200, -1]], dtype=np.int32)
+    for tk in (None, topk):
+        a = mo.mla_decode(inp["q"], inp["kv"], inp["block_table"], inp["seqlens"], tk, ksi, kv_format="fp8_tensor")
+        b = mo.mla_decode(inp["q"], kv16, inp["block_table"], inp["seqlens"], tk)
+        np.testing.assert_array_equal(a["O"], b["O"])
+        np.testing.assert_array_equal(a["LSE"], b["LSE"])
+
+
+def test_insert_then_dequant_within_e4m3_bound():
+    """Rows written by the insert and read back through the per-tensor format
+    are the bf16 normalised (and rope) values within e4m3's rounding bound:
+    relative 2^-4 for normal codes, absolute 2^-10 / k_scale_inv below 2^-6."""
+    inp = synth.make_insert_inputs(36, tokens=12, num_pages=1, skipped=3)
+    res = mo.kv_insert(inp["qkv"], inp["w_kva"], inp["cache"], inp["slots"], inp["k_scale_inv"], inp["eps"])
+    ksi = inp["k_scale_inv"]
+    live = inp["slots"] >= 0
+    back = mo.dequant_rows(res["cache"], inp["slots"][live], "fp8_tensor", np.array([ksi], np.float32))
+    want = res["fp8_in"][live] / ksi
+    err = np.abs(back - want)
+    bound = np.maximum(np.abs(want) * 2.0**-4, 2.0**-10 / ksi)
+    assert np.all(err <= bound)
