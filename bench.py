@@ -18,6 +18,9 @@ every input resident in HBM before timing:
   query_decode: mla_query (RMSNorm, Q_B, W_UK, FP8) for 64 tokens x 8 heads,
       then mla_decode of those FP8 queries over a bf16 cache of 8192 tokens
       per sequence.
+  insert_decode: mla_kv_insert of the 64 new tokens' latent rows (RMSNorm,
+      per-tensor e4m3) at each sequence's last position, then mla_decode over
+      that all-FP8 cache: batch 64, 128 heads, 4096 tokens each, 4096-page pool.
 
 The decode call runs the work split, block-table translation (or the top-k
 prepass), KV streaming, QK^T, softmax, PV, epilogue and the split-KV merge on
@@ -58,6 +61,9 @@ WORKLOADS = {
                    "e4m3 cache, 32768-page pool",
     "query_decode": "MLA query front end (64 tokens, 8 heads: RMSNorm, Q_B 1536x1536, W_UK, FP8) then decode "
                     "of the FP8 queries over bf16 pages, 8192 tokens each",
+    "insert_decode": "KV-cache insert (64 tokens: RMSNorm of the 512-wide latent row, per-tensor e4m3 of the 576 "
+                     "columns) then decode over the all-FP8 cache: batch 64, 128 heads, seq_len 4096 each, "
+                     "4096-page pool",
 }
 
 
@@ -75,11 +81,12 @@ def kv_tokens(inp) -> int:
 
 def decode_bytes(inp) -> int:
     """Bytes the decode must move at least once: the KV rows it attends
-    (bf16 1152 B; FP8 512 codes + 128 B rope + 16 B scales), the queries, the
+    (bf16 1152 B; FP8 512 codes + 128 B rope + 16 B scales; per-tensor FP8
+    576 codes), the queries, the
     outputs (bf16 O + fp32 LSE), the block-table entries it reads, the
     sequence lengths and the top-k lists."""
     B, H = inp["batch"], inp["heads"]
-    row = 576 * 2 if inp["kv_format"] == "bf16" else 512 + 128 + 16
+    row = {"bf16": 576 * 2, "fp8": 512 + 128 + 16, "fp8_tensor": 576}[inp["kv_format"]]
     qb = 576 * (2 if inp["q_format"] == "bf16" else 1)
     if inp.get("topk_idx") is not None:
         tables = inp["topk_idx"].size * 4 + kv_tokens(inp) * 4  # lists + one block-table entry per valid entry
@@ -97,6 +104,16 @@ def query_bytes(qin) -> int:
     """qkv rows read, the three weights, the FP8 output."""
     B, H = qin["batch"], qin["heads"]
     return B * 1536 * 2 + 1536 * 2 + H * 192 * 1536 * 2 + H * 128 * 512 * 2 + B * H * 576
+
+
+def insert_bytes(tokens: int) -> int:
+    """Latent + rope bf16 read per token, its slot, the 576 codes written,
+    w_kva and the scale."""
+    return tokens * (576 * 2 + 8 + 576) + 512 * 2 + 4
+
+
+def insert_flops(tokens: int) -> int:
+    return tokens * 512 * 4  # square-accumulate, normalise, weight
 
 
 def query_flops(qin) -> int:
@@ -133,7 +150,7 @@ def cpu_threads() -> int:
                     if i.get("internal_api") in ("openblas", "mkl", "blis")] or [1]))
 
 
-def cpu_baseline(inp, nbytes: int, budget_s: float = 12.0, qin=None):
+def cpu_baseline(inp, nbytes: int, budget_s: float = 12.0, qin=None, ins=None):
     """The float64 oracle (as it stands) on whole sequences of the workload
     until the time budget is spent, scaled to the metric's unit."""
     from oracle import mla_oracle as mo
@@ -141,6 +158,8 @@ def cpu_baseline(inp, nbytes: int, budget_s: float = 12.0, qin=None):
     t0 = time.perf_counter()
     if qin is not None:
         mo.mla_query(qin["qkv"], qin["w_qa"], qin["w_qb"], qin["w_uk"], qin["q_scale_inv"], eps=qin["eps"])
+    if ins is not None:
+        mo.kv_insert(ins["qkv"], ins["w_kva"], inp["kv"], ins["slots"], float(inp["kv_scales"][0]), ins["eps"])
     done = 0
     while done < inp["batch"] and time.perf_counter() - t0 < budget_s:
         mo.mla_decode(inp["q"], inp["kv"], inp["block_table"], inp["seqlens"], inp.get("topk_idx"),
@@ -154,7 +173,8 @@ def cpu_baseline(inp, nbytes: int, budget_s: float = 12.0, qin=None):
         "unit": "GB/s",
         "cores": cpu_threads(),
         "kind": "oracle",
-        "sample": f"{done} of {inp['batch']} sequences{' plus the whole query front end' if qin else ''}, "
+        "sample": f"{done} of {inp['batch']} sequences{' plus the whole query front end' if qin else ''}"
+                  f"{' plus the whole insert' if ins else ''}, "
                   f"{dt:.1f} s; host has {os.cpu_count()} logical CPUs",
     }
 
@@ -189,10 +209,18 @@ def main():
     qin = synth.make_query_inputs(5, batch=64, heads=8) if name == "query_decode" else None
     d = mla.to_device(inp, dev)
     B, H = inp["batch"], inp["heads"]
+    ins = None
+    if name == "insert_decode":
+        # the new token of sequence b is its last position
+        bt, last = inp["block_table"], inp["seqlens"].astype(np.int64) - 1
+        ins = synth.make_insert_inputs(6, tokens=B, num_pages=1)
+        slots = bt[np.arange(B), last // 64].astype(np.int64) * 64 + last % 64
+        di = mla.insert_to_device(ins, dev)
+        di["slots"] = torch.from_numpy(slots).to(dev)
     topk = 0 if inp.get("topk_idx") is None else inp["topk_idx"].shape[1]
     params = mla.decode_params(batch=B, heads=H, num_pages=inp["kv"].shape[0],
                                max_pages_per_seq=inp["block_table"].shape[1], topk=topk,
-                               q_fp8=inp["q_format"] != "bf16", kv_fp8=inp["kv_format"] != "bf16",
+                               q_fp8=inp["q_format"] != "bf16", kv_format=inp["kv_format"],
                                q_descale=inp["q_descale"])
     stream = torch.cuda.current_stream(dev)
     ws = mla.decode_workspace(params, dev, stream)
@@ -206,6 +234,9 @@ def main():
                           dtype=torch.uint8, device=dev)
 
     def step():
+        if ins is not None:
+            mla.mla_kv_insert(di["qkv"], di["w_kva"], di["slots"], d["kv_scales"], d["kv"], eps=ins["eps"],
+                              stream=stream)
         if qin is not None:
             mla.mla_query(dq["qkv"], dq["w_qa"], dq["w_qb"], dq["w_uk"], dq["q_scale_inv"], out=q, eps=qin["eps"],
                           workspace=qws, stream=stream)
@@ -259,15 +290,16 @@ def main():
         cold.append(e0.elapsed_time(e1))
     del flush
 
-    nbytes = decode_bytes(inp) + (query_bytes(qin) if qin else 0)
-    flops = decode_flops(inp) + (query_flops(qin) if qin else 0)
+    nbytes = decode_bytes(inp) + (query_bytes(qin) if qin else 0) + (insert_bytes(B) if ins else 0)
+    flops = decode_flops(inp) + (query_flops(qin) if qin else 0) + (insert_flops(B) if ins else 0)
     kern_avg_s = float(kern_ms.mean()) / 1e3
     achieved = nbytes / kern_avg_s / 1e9
     tflops = flops / kern_avg_s / 1e12
     value = nbytes / (ms_per_step / 1e3) / 1e9
     kernels = {"topk_sparse": "mla_topk_rows_kernel + mla_decode_kernel<2,false,2> + mla_merge_kernel",
                "fp8_cache": "mla_decode_kernel<2,false,1> + mla_merge_kernel",
-               "query_decode": "mla_qb_kernel + mla_ql_kernel + mla_decode_kernel<4,true,0> + mla_merge_kernel"}
+               "query_decode": "mla_qb_kernel + mla_ql_kernel + mla_decode_kernel<4,true,0> + mla_merge_kernel",
+               "insert_decode": "mla_kv_insert_kernel + mla_decode_kernel<2,false,4> + mla_merge_kernel"}
     kernel = kernels.get(name, "mla_decode_kernel<2,false,0> + mla_merge_kernel")
     mfma_bound = name == "topk_sparse"  # 345 flop per algorithmic byte, above the bf16 ridge
     roofline = {
@@ -314,7 +346,9 @@ def main():
         "roofline": roofline,
         "wall_s_timed_region": round(wall, 4),
     }
-    res["cpu_baseline"] = None if args.no_cpu_baseline else cpu_baseline(inp, nbytes, qin=qin)
+    if ins is not None:
+        ins["slots"] = slots
+    res["cpu_baseline"] = None if args.no_cpu_baseline else cpu_baseline(inp, nbytes, qin=qin, ins=ins)
     print(json.dumps(res), flush=True)
 
 

@@ -2,7 +2,7 @@
  * mla.h - C ABI of the MI355X (gfx950) absorbed multi-head latent attention
  * (MLA) decode library.
  *
- * Two operations:
+ * Three operations:
  *
  *  mla_decode  Absorbed MLA decode for one query token per sequence.  All H
  *              query heads of a sequence attend to the same latent KV rows of
@@ -16,8 +16,9 @@
  *              are an extra block of the same QK^T product; invalid KV slots are
  *              masked when P is formed).  V is the 512 latent columns of the same
  *              row.  Variants: dense paged bf16 cache, FP8 e4m3 cache with one
- *              fp32 scale per 128 latent columns (rope kept in bf16), and top-k
- *              sparse index lists.
+ *              fp32 scale per 128 latent columns (rope kept in bf16), the
+ *              all-FP8 cache with one per-tensor scale that mla_kv_insert
+ *              writes, and top-k sparse index lists.
  *
  *  mla_query   The query front end of the vLLM MlaQuery kernel (API page of
  *              vllm.models.kimi_k3...mla.query, class MlaQuery, method
@@ -27,6 +28,14 @@
  *              encoding of [absorbed 512 | rope 64] after multiplying by
  *              q_scale_inv.  Intermediates are rounded to bf16 after RMSNorm,
  *              after Q_B and after W_UK, as on that page.
+ *
+ *  mla_kv_insert  The KV-cache insert of the same vLLM MlaQuery page (method
+ *              `insert`): RMSNorm of each new token's 512-wide latent KV row
+ *              (qkv columns 1536..2047) with w_kva, rounded to bf16, then the
+ *              e4m3 codes of (normed * k_scale_inv) and of the 64 rope values
+ *              (qkv columns 2048..2111) * k_scale_inv written to the token's
+ *              cache slot: page slot / 64, row slot % 64.  A slot < 0 writes
+ *              nothing.
  *
  * Conventions (all entry points):
  *  - Every data pointer is device memory owned by the caller.  The library
@@ -67,12 +76,19 @@ extern "C" {
 /* ---- element types ---- */
 #define MLA_DTYPE_BF16 1
 #define MLA_DTYPE_FP8_E4M3 2
+/* KV cache only: every one of the 576 columns (rope too) is an e4m3 code of
+   value * k_scale_inv, one fp32 k_scale_inv for the whole cache (the layout
+   mla_kv_insert writes). */
+#define MLA_DTYPE_FP8_E4M3_TENSOR 3
 
 /* ---- fixed geometry ---- */
 #define MLA_D_QK 576        /* latent row width: 512 nope + 64 rope */
 #define MLA_D_V 512         /* value width: the 512 nope columns */
 #define MLA_PAGE_SIZE 64    /* tokens per KV page */
 #define MLA_FP8_ROW_BYTES 640 /* FP8 cache row: 512 e4m3 codes + 64 bf16 rope */
+#define MLA_FP8T_ROW_BYTES 576 /* per-tensor FP8 cache row: 576 e4m3 codes */
+#define MLA_QKV_WIDTH 2112  /* qkv row read by mla_kv_insert: q_a 1536 | latent 512 | rope 64 */
+#define MLA_MAX_INSERT_TOKENS (1 << 24)
 #define MLA_MAX_HEADS 128
 #define MLA_MAX_BATCH 8192
 
@@ -83,7 +99,7 @@ typedef struct mla_decode_params {
   int32_t max_pages_per_seq; /* columns of block_table, >= 1 */
   int32_t topk;              /* 0: dense over [0, seqlen); > 0: entries per row of topk_idx */
   int32_t q_dtype;           /* MLA_DTYPE_BF16 or MLA_DTYPE_FP8_E4M3 */
-  int32_t kv_dtype;          /* MLA_DTYPE_BF16 or MLA_DTYPE_FP8_E4M3 */
+  int32_t kv_dtype;          /* MLA_DTYPE_BF16, MLA_DTYPE_FP8_E4M3 or MLA_DTYPE_FP8_E4M3_TENSOR */
   float softmax_scale;       /* multiplies the full 576-wide dot, e.g. 192^-0.5 */
   float q_descale;           /* FP8 queries: value = code * q_descale (= 1/q_scale_inv); ignored for bf16 */
 } mla_decode_params;
@@ -114,6 +130,7 @@ int32_t mla_decode_workspace_init(const mla_decode_params* p, void* workspace, s
  *  kv_cache    bf16 cache: [num_pages, 64, 576] bf16.
  *              FP8 cache:  [num_pages, 64, 640] bytes per row = 512 e4m3 codes
  *              of the latent columns, then the 64 rope values as bf16.
+ *              Per-tensor FP8 cache: [num_pages, 64, 576] e4m3 codes.
  *  block_table [B, max_pages_per_seq] int32: physical page of logical page j of
  *              sequence b; logical position t lives in row
  *              block_table[b, t/64]*64 + t%64 (the page/offset split of a slot
@@ -126,7 +143,9 @@ int32_t mla_decode_workspace_init(const mla_decode_params* p, void* workspace, s
  *              are masked (contribute nothing); duplicates count once per entry.
  *  kv_scales   NULL for a bf16 cache; for an FP8 cache [num_pages, 64, 4] fp32,
  *              one scale per row and 128-column tile: k[d] = code[d]*scale[d/128]
- *              for d < 512.
+ *              for d < 512.  Per-tensor FP8 cache: one fp32, the k_scale_inv
+ *              the cache was written with; k[d] = code[d] / k_scale_inv for all
+ *              576 columns.  Precondition: k_scale_inv finite and > 0.
  *  out         [B, H, 512] bf16 (round to nearest even).
  *  lse         [B, H] fp32, natural-log log-sum-exp of the scaled scores.
  *  workspace   device scratch of at least mla_decode_workspace_size bytes;
@@ -170,6 +189,38 @@ int32_t mla_query_workspace_size(const mla_query_params* p, size_t* bytes);
 int32_t mla_query(const mla_query_params* p, const void* qkv, const void* w_qa,
                   const void* w_qb, const void* w_uk, const float* q_scale_inv,
                   void* out, void* workspace, size_t workspace_bytes, void* stream);
+
+typedef struct mla_kv_insert_params {
+  int32_t tokens;      /* T new tokens, 0 <= T <= MLA_MAX_INSERT_TOKENS (0: nothing is launched) */
+  int32_t num_pages;   /* pages in the cache, >= 1, num_pages*64 <= INT32_MAX */
+  int32_t qkv_stride;  /* elements between rows of qkv, >= 2112, a multiple of 8 */
+  float eps;           /* RMSNorm epsilon, >= 0 */
+} mla_kv_insert_params;
+
+/*
+ * KV-cache insert into the per-tensor FP8 cache (vLLM MlaQuery page, method
+ * `insert`; it runs there beside the query front end).
+ *
+ *  qkv         [T, qkv_stride] bf16; columns 1536..2047 are the latent KV row,
+ *              2048..2111 the rope key.
+ *  w_kva       [512] bf16 RMSNorm weight.
+ *  slots       [T] int64: the cache slot of each token, page slot / 64 and row
+ *              slot % 64.  Negative slots are skipped.  Precondition: the
+ *              non-negative slots are distinct and < num_pages*64 (a slot past
+ *              the end is skipped, never written out of bounds; which of two
+ *              equal slots lands is unspecified).
+ *  k_scale_inv device fp32 scalar; codes are e4m3(value * k_scale_inv[0]),
+ *              rounded to nearest even from the exact product and saturated
+ *              to +-448 (never 0xFF).
+ *  kv_cache    [num_pages, 64, 576] e4m3 codes (MLA_DTYPE_FP8_E4M3_TENSOR
+ *              layout); only the rows of the given slots are written.
+ *
+ *  RMSNorm: rr = 1/sqrt(sum(x^2)/512 + eps) over the 512 latent values,
+ *  normed = bf16((x*rr)*w_kva); the rope values are encoded as they are.
+ *  No workspace.  One kernel on `stream`.
+ */
+int32_t mla_kv_insert(const mla_kv_insert_params* p, const void* qkv, const void* w_kva,
+                      const int64_t* slots, const float* k_scale_inv, void* kv_cache, void* stream);
 
 /* Static text for a status code. */
 const char* mla_status_string(int32_t status);

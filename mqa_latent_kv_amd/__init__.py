@@ -10,6 +10,7 @@ Entry points (same names as the C ABI):
     mla_decode(q, kv_cache, block_table, seqlens, topk_idx=None, kv_scales=None,
                out=None, lse=None, ...)
     mla_query(qkv, w_qa, w_qb, w_uk, q_scale_inv, out=None, ...)
+    mla_kv_insert(qkv, w_kva, slots, k_scale_inv, kv_cache, ...)
     mla_decode_workspace_size(params), mla_decode_workspace_init(params, ws),
     mla_query_workspace_size(params)
     mla_status_string(code), mla_version()
@@ -24,10 +25,14 @@ LIB_PATH = os.path.join(_HERE, "libmla.so")
 
 MLA_DTYPE_BF16 = 1
 MLA_DTYPE_FP8_E4M3 = 2
+MLA_DTYPE_FP8_E4M3_TENSOR = 3
 D_QK = 576
 D_V = 512
 PAGE_SIZE = 64
 FP8_ROW_BYTES = 640
+FP8T_ROW_BYTES = 576
+QKV_WIDTH = 2112
+KV_DTYPES = {"bf16": MLA_DTYPE_BF16, "fp8": MLA_DTYPE_FP8_E4M3, "fp8_tensor": MLA_DTYPE_FP8_E4M3_TENSOR}
 
 
 class MlaError(RuntimeError):
@@ -45,6 +50,15 @@ class DecodeParams(ctypes.Structure):
         ("kv_dtype", ctypes.c_int32),
         ("softmax_scale", ctypes.c_float),
         ("q_descale", ctypes.c_float),
+    ]
+
+
+class InsertParams(ctypes.Structure):
+    _fields_ = [
+        ("tokens", ctypes.c_int32),
+        ("num_pages", ctypes.c_int32),
+        ("qkv_stride", ctypes.c_int32),
+        ("eps", ctypes.c_float),
     ]
 
 
@@ -82,6 +96,8 @@ def lib() -> ctypes.CDLL:
         L.mla_query_workspace_size.argtypes = [ctypes.POINTER(QueryParams), ctypes.POINTER(sz)]
         L.mla_query.restype = i32
         L.mla_query.argtypes = [ctypes.POINTER(QueryParams), vp, vp, vp, vp, vp, vp, vp, sz, vp]
+        L.mla_kv_insert.restype = i32
+        L.mla_kv_insert.argtypes = [ctypes.POINTER(InsertParams), vp, vp, vp, vp, vp, vp]
         _lib = L
     return _lib
 
@@ -125,12 +141,13 @@ def _expect(t, name, dtypes, shape=None):
         raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
 
 
-def decode_params(*, batch, heads, num_pages, max_pages_per_seq, topk=0, q_fp8=False, kv_fp8=False,
+def decode_params(*, batch, heads, num_pages, max_pages_per_seq, topk=0, q_fp8=False, kv_format="bf16",
                   softmax_scale=192.0**-0.5, q_descale=1.0) -> DecodeParams:
+    """kv_format: "bf16", "fp8" (per-tile scales) or "fp8_tensor" (one per-tensor scale)."""
     return DecodeParams(
         batch, heads, num_pages, max_pages_per_seq, topk,
         MLA_DTYPE_FP8_E4M3 if q_fp8 else MLA_DTYPE_BF16,
-        MLA_DTYPE_FP8_E4M3 if kv_fp8 else MLA_DTYPE_BF16,
+        KV_DTYPES[kv_format],
         float(softmax_scale), float(q_descale),
     )
 
@@ -160,8 +177,9 @@ def mla_decode(q, kv_cache, block_table, seqlens, topk_idx=None, kv_scales=None,
     """Absorbed MLA decode (see include/mla.h).
 
     q: [B, H, 576] torch.bfloat16, or uint8 / float8_e4m3fn codes.
-    kv_cache: bf16 [P, 64, 576], or uint8 [P, 64, 640] FP8 rows (then kv_scales
-    float32 [P, 64, 4]).  block_table int32 [B, max_pages], seqlens int32 [B],
+    kv_cache: bf16 [P, 64, 576]; or uint8 [P, 64, 640] FP8 rows (then kv_scales
+    float32 [P, 64, 4]); or uint8 [P, 64, 576] per-tensor FP8 rows (then
+    kv_scales the float32 [1] k_scale_inv).  block_table int32 [B, max_pages], seqlens int32 [B],
     topk_idx int32 [B, topk] or None.  Returns (out bf16 [B, H, 512], lse fp32 [B, H]).
     """
     import torch
@@ -173,13 +191,18 @@ def mla_decode(q, kv_cache, block_table, seqlens, topk_idx=None, kv_scales=None,
     if dq != D_QK:
         raise ValueError("q must have 576 columns")
     q_fp8 = q.dtype != torch.bfloat16
-    kv_fp8 = kv_cache.dtype in (torch.uint8, torch.float8_e4m3fn)
-    if kv_fp8:
+    if kv_cache.dtype in (torch.uint8, torch.float8_e4m3fn):
         _expect(kv_cache, "kv_cache", (torch.uint8, torch.float8_e4m3fn))
-        if tuple(kv_cache.shape[1:]) != (PAGE_SIZE, FP8_ROW_BYTES):
-            raise ValueError("FP8 kv_cache must be [P, 64, 640]")
-        _expect(kv_scales, "kv_scales", (torch.float32,), (kv_cache.shape[0], PAGE_SIZE, 4))
+        if tuple(kv_cache.shape[1:]) == (PAGE_SIZE, FP8_ROW_BYTES):
+            kv_format = "fp8"
+            _expect(kv_scales, "kv_scales", (torch.float32,), (kv_cache.shape[0], PAGE_SIZE, 4))
+        elif tuple(kv_cache.shape[1:]) == (PAGE_SIZE, FP8T_ROW_BYTES):
+            kv_format = "fp8_tensor"
+            _expect(kv_scales, "kv_scales", (torch.float32,), (1,))
+        else:
+            raise ValueError("FP8 kv_cache must be [P, 64, 640] (tile scales) or [P, 64, 576] (per-tensor scale)")
     else:
+        kv_format = "bf16"
         _expect(kv_cache, "kv_cache", (torch.bfloat16,))
         if tuple(kv_cache.shape[1:]) != (PAGE_SIZE, D_QK):
             raise ValueError("bf16 kv_cache must be [P, 64, 576]")
@@ -203,7 +226,7 @@ def mla_decode(q, kv_cache, block_table, seqlens, topk_idx=None, kv_scales=None,
     _expect(out, "out", (torch.bfloat16,), (B, H, D_V))
     _expect(lse, "lse", (torch.float32,), (B, H))
     params = decode_params(batch=B, heads=H, num_pages=P, max_pages_per_seq=block_table.shape[1], topk=topk,
-                           q_fp8=q_fp8, kv_fp8=kv_fp8, softmax_scale=softmax_scale, q_descale=q_descale)
+                           q_fp8=q_fp8, kv_format=kv_format, softmax_scale=softmax_scale, q_descale=q_descale)
     if workspace is None:
         workspace = decode_workspace(params, dev, stream)
     _expect(workspace, "workspace", (torch.uint8,))
@@ -250,6 +273,47 @@ def mla_query(qkv, w_qa, w_qb, w_uk, q_scale_inv, out=None, *, eps=1e-6, workspa
     )
     _check(code, "mla_query")
     return out
+
+
+def mla_kv_insert(qkv, w_kva, slots, k_scale_inv, kv_cache, *, eps=1e-6, stream=None):
+    """KV-cache insert (see include/mla.h).  qkv bf16 [T, >=2112]; w_kva bf16
+    [512]; slots int64 [T] (negative: skipped); k_scale_inv float32 [1] on the
+    device; kv_cache uint8 / float8_e4m3fn [P, 64, 576], written in place at
+    the given slots.  Returns kv_cache."""
+    import torch
+
+    _expect(qkv, "qkv", (torch.bfloat16,))
+    if qkv.dim() != 2:
+        raise ValueError("qkv must be [T, width]")
+    T, width = qkv.shape
+    _expect(w_kva, "w_kva", (torch.bfloat16,), (D_V,))
+    _expect(slots, "slots", (torch.int64,), (T,))
+    _expect(k_scale_inv, "k_scale_inv", (torch.float32,), (1,))
+    _expect(kv_cache, "kv_cache", (torch.uint8, torch.float8_e4m3fn))
+    if kv_cache.dim() != 3 or tuple(kv_cache.shape[1:]) != (PAGE_SIZE, FP8T_ROW_BYTES):
+        raise ValueError("kv_cache must be [P, 64, 576]")
+    params = InsertParams(T, kv_cache.shape[0], width, float(eps))
+    code = lib().mla_kv_insert(
+        ctypes.byref(params), _ptr(qkv), _ptr(w_kva), _ptr(slots), _ptr(k_scale_inv), _ptr(kv_cache),
+        _stream_handle(stream, qkv.device),
+    )
+    _check(code, "mla_kv_insert")
+    return kv_cache
+
+
+def insert_to_device(inp: dict, device="cuda"):
+    """Move a seeded KV-insert input (numpy raw bits, see synth) to device
+    tensors; k_scale_inv becomes a one-element float32 device tensor."""
+    import numpy as np
+    import torch
+
+    return {
+        "qkv": torch.from_numpy(np.ascontiguousarray(inp["qkv"]).view(np.int16)).view(torch.bfloat16).to(device),
+        "w_kva": torch.from_numpy(np.ascontiguousarray(inp["w_kva"]).view(np.int16)).view(torch.bfloat16).to(device),
+        "cache": torch.from_numpy(np.ascontiguousarray(inp["cache"])).to(device),
+        "slots": torch.from_numpy(np.ascontiguousarray(inp["slots"])).to(device),
+        "k_scale_inv": torch.tensor([inp["k_scale_inv"]], dtype=torch.float32, device=device),
+    }
 
 
 def to_device(inp: dict, device="cuda"):

@@ -9,6 +9,7 @@
 namespace {
 
 bool valid_dtype(int32_t d) { return d == MLA_DTYPE_BF16 || d == MLA_DTYPE_FP8_E4M3; }
+bool valid_kv_dtype(int32_t d) { return valid_dtype(d) || d == MLA_DTYPE_FP8_E4M3_TENSOR; }
 
 bool supported_heads(int32_t h) { return h == 8 || h == 16 || h == 32 || h == 64 || h == 128; }
 
@@ -18,7 +19,7 @@ int32_t check_decode_params(const mla_decode_params* p) {
   if (!p) return MLA_ERR_INVALID_ARG;
   if (p->batch < 1 || p->heads < 1 || p->num_pages < 1 || p->max_pages_per_seq < 1 || p->topk < 0)
     return MLA_ERR_INVALID_ARG;
-  if (!valid_dtype(p->q_dtype) || !valid_dtype(p->kv_dtype)) return MLA_ERR_INVALID_ARG;
+  if (!valid_dtype(p->q_dtype) || !valid_kv_dtype(p->kv_dtype)) return MLA_ERR_INVALID_ARG;
   if (!(p->softmax_scale > 0.0f) || !(p->q_descale > 0.0f)) return MLA_ERR_INVALID_ARG;
   if (p->batch > MLA_MAX_BATCH || !supported_heads(p->heads)) return MLA_ERR_UNSUPPORTED;
   // 32-bit offsets inside the kernels: logical positions and pool rows
@@ -57,7 +58,7 @@ int32_t device_cus(int32_t* cus) {
 
 extern "C" {
 
-int32_t mla_version(void) { return 100; }
+int32_t mla_version(void) { return 200; }
 
 const char* mla_status_string(int32_t status) {
   switch (status) {
@@ -102,11 +103,13 @@ int32_t mla_decode(const mla_decode_params* p, const void* q, const void* kv_cac
   if (st != MLA_OK) return st;
   if (!q || !kv_cache || !block_table || !seqlens || !out || !lse) return MLA_ERR_INVALID_ARG;
   // q rows, cache rows, scales and outputs are accessed as 8/16-byte vectors
-  if (!aligned16(q) || !aligned16(kv_cache) || !aligned16(out) || (kv_scales && !aligned16(kv_scales)) ||
-      !aligned16(workspace))
+  // (a per-tensor scale is one float)
+  const bool tile_scales = p->kv_dtype == MLA_DTYPE_FP8_E4M3;
+  if (!aligned16(q) || !aligned16(kv_cache) || !aligned16(out) || (kv_scales && tile_scales && !aligned16(kv_scales)) ||
+      (kv_scales && ((uintptr_t)kv_scales & 3)) || !aligned16(workspace))
     return MLA_ERR_INVALID_ARG;
   if ((p->topk > 0) != (topk_idx != nullptr)) return MLA_ERR_INVALID_ARG;
-  if ((p->kv_dtype == MLA_DTYPE_FP8_E4M3) != (kv_scales != nullptr)) return MLA_ERR_INVALID_ARG;
+  if ((p->kv_dtype != MLA_DTYPE_BF16) != (kv_scales != nullptr)) return MLA_ERR_INVALID_ARG;
   if (!workspace) return MLA_ERR_WORKSPACE;
   int32_t cus = 0;
   st = device_cus(&cus);
@@ -129,7 +132,9 @@ int32_t mla_decode(const mla_decode_params* p, const void* q, const void* kv_cac
   d.max_pages = p->max_pages_per_seq;
   d.topk = p->topk;
   d.q_fp8 = p->q_dtype == MLA_DTYPE_FP8_E4M3;
-  d.kv_fp8 = p->kv_dtype == MLA_DTYPE_FP8_E4M3;
+  d.kv_format = p->kv_dtype == MLA_DTYPE_BF16       ? mla::kKvFormatBf16
+                : p->kv_dtype == MLA_DTYPE_FP8_E4M3 ? mla::kKvFormatFp8Tile
+                                                    : mla::kKvFormatFp8Tensor;
   d.softmax_scale = p->softmax_scale;
   d.q_descale = p->q_descale;
   d.ranges = ranges;
@@ -170,6 +175,34 @@ int32_t mla_query(const mla_query_params* p, const void* qkv, const void* w_qa, 
   ql.qkv_stride = p->qkv_stride;
   ql.eps = p->eps;
   if (mla::launch_query(ql, (hipStream_t)stream) != hipSuccess) return MLA_ERR_LAUNCH;
+  return MLA_OK;
+}
+
+int32_t mla_kv_insert(const mla_kv_insert_params* p, const void* qkv, const void* w_kva,
+                      const int64_t* slots, const float* k_scale_inv, void* kv_cache, void* stream) {
+  if (!p) return MLA_ERR_INVALID_ARG;
+  if (p->tokens < 0 || p->num_pages < 1 || p->qkv_stride < MLA_QKV_WIDTH || !(p->eps >= 0.0f))
+    return MLA_ERR_INVALID_ARG;
+  // rows are read as 16-byte vectors; slots and cache rows use 32-bit row numbers
+  if (p->qkv_stride % 8 != 0) return MLA_ERR_UNSUPPORTED;
+  if (p->tokens > MLA_MAX_INSERT_TOKENS || (int64_t)p->num_pages * MLA_PAGE_SIZE > INT32_MAX)
+    return MLA_ERR_UNSUPPORTED;
+  if (!qkv || !w_kva || !slots || !k_scale_inv || !kv_cache) return MLA_ERR_INVALID_ARG;
+  if (!aligned16(qkv) || !aligned16(w_kva) || ((uintptr_t)slots & 7) || ((uintptr_t)k_scale_inv & 3) ||
+      !aligned16(kv_cache))
+    return MLA_ERR_INVALID_ARG;
+  if (p->tokens == 0) return MLA_OK;
+  mla::InsertLaunch k;
+  k.qkv = qkv;
+  k.w_kva = w_kva;
+  k.slots = slots;
+  k.k_scale_inv = k_scale_inv;
+  k.cache = kv_cache;
+  k.tokens = p->tokens;
+  k.num_pages = p->num_pages;
+  k.qkv_stride = p->qkv_stride;
+  k.eps = p->eps;
+  if (mla::launch_kv_insert(k, (hipStream_t)stream) != hipSuccess) return MLA_ERR_LAUNCH;
   return MLA_OK;
 }
 

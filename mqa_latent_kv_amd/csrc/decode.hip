@@ -46,6 +46,12 @@
 //    the pieces.  The merge is not done by the last piece to arrive: that
 //    would need a device-scope release fence per piece, which on gfx950
 //    writes back the whole XCD L2.
+//  * Cache formats: bf16 rows are copied by the DMA; FP8 rows (512 codes
+//    with per-128-column scales and bf16 rope, or 576 codes with one
+//    per-tensor scale) and gathered top-k rows pass through registers, where
+//    the e4m3 codes become bf16 exactly.  Tile scales multiply the partial
+//    scores in fp32; the per-tensor 1/k_scale_inv folds into the score scale
+//    and the output normalisation.
 //  * Softmax in base 2 against a fixed reference per head: the first slot's
 //    max.  Later slots may exceed it by up to 16 (P <= 2^16, exact in fp32 and
 //    as relative bf16); if any head's scores rise further, the workgroup
@@ -382,9 +388,13 @@ constexpr int kKvBf16 = 0;        // bf16 rows [P,64,576], whole pages (LDS DMA)
 constexpr int kKvFp8 = 1;         // e4m3 rows [P,64,640] + fp32 scales [P,64,4], whole pages
 constexpr int kKvFp8TopK = 2;     // e4m3 rows, gathered top-k entries
 constexpr int kKvBf16TopK = 3;    // bf16 rows, gathered top-k entries
-constexpr bool kv_fp8(int m) { return m == kKvFp8 || m == kKvFp8TopK; }
-constexpr bool kv_topk(int m) { return m == kKvFp8TopK || m == kKvBf16TopK; }
-constexpr int kFp8RowBytes = 640;  // 512 e4m3 codes, 64 bf16 rope values
+constexpr int kKvFp8T = 4;        // e4m3 rows [P,64,576], one per-tensor k_scale_inv, whole pages
+constexpr int kKvFp8TTopK = 5;    // the same rows, gathered top-k entries
+constexpr bool kv_fp8(int m) { return m == kKvFp8 || m == kKvFp8TopK; }  // per-tile scales (tiled QK^T)
+constexpr bool kv_tensor(int m) { return m == kKvFp8T || m == kKvFp8TTopK; }
+constexpr bool kv_topk(int m) { return m == kKvFp8TopK || m == kKvBf16TopK || m == kKvFp8TTopK; }
+constexpr int kFp8RowBytes = 640;   // 512 e4m3 codes, 64 bf16 rope values
+constexpr int kFp8TRowBytes = 576;  // 576 e4m3 codes
 
 // The register fill: every slot row is loaded by the eight lanes of one
 // wave that share lane % 8 (wave w: rows 8w .. 8w+7), lane / 8 = q picking
@@ -404,6 +414,13 @@ struct RawRow<kKvFp8> {
 template <>
 struct RawRow<kKvFp8TopK> : RawRow<kKvFp8> {};
 template <>
+struct RawRow<kKvFp8T> {
+  u32x4 code[4];  // codes 128k + 16q .. +15 of the row, k = 0..3
+  uint2 rope;     // rope codes 8q .. +7
+};
+template <>
+struct RawRow<kKvFp8TTopK> : RawRow<kKvFp8T> {};
+template <>
 struct RawRow<kKvBf16TopK> {
   u32x4 v[9];  // bytes 128k + 16q .. +15 of the row, k = 0..8 (column group k)
 };
@@ -416,6 +433,11 @@ __device__ __forceinline__ void load_row(RawRow<KVM>& rr, const DecodeArgs& a, i
     for (int k = 0; k < 4; ++k) rr.code[k] = *(const u32x4*)(base + 128 * k + 16 * q);
     rr.rope = *(const u32x4*)(base + 512 + 16 * q);
     rr.scale = *(const f32x4*)(a.kv_scales + (size_t)row * 4);
+  } else if constexpr (kv_tensor(KVM)) {
+    const char* base = a.kv + (size_t)row * kFp8TRowBytes;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) rr.code[k] = *(const u32x4*)(base + 128 * k + 16 * q);
+    rr.rope = *(const uint2*)(base + 512 + 8 * q);
   } else {
 #pragma unroll
     for (int k = 0; k < 9; ++k) rr.v[k] = *(const u32x4*)(a.kv + (size_t)row * kRowBytes + 128 * k + 16 * q);
@@ -453,6 +475,16 @@ __device__ __forceinline__ void fill_row(lds_char* buf, LDS_AS float* stab, cons
     // rope (bf16 as stored): column group 8, chunk q
     *(LDS_AS u32x4*)(rowp + kGroupBytes * 8 + 16 * (q ^ sw)) = rr.rope;
     if (q < 4) stab[q * kTS + r] = rr.scale[q];
+  } else if constexpr (kv_tensor(KVM)) {
+    // codes as above; the rope codes 8q .. +7 go to chunk q of column group 8
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int c0 = 2 * (q & 3);
+      lds_char* gp = rowp + kGroupBytes * (2 * k + (q >> 2));
+      *(LDS_AS u32x4*)(gp + 16 * (c0 ^ sw)) = codes8(rr.code[k][0], rr.code[k][1]);
+      *(LDS_AS u32x4*)(gp + 16 * ((c0 + 1) ^ sw)) = codes8(rr.code[k][2], rr.code[k][3]);
+    }
+    *(LDS_AS u32x4*)(rowp + kGroupBytes * 8 + 16 * (q ^ sw)) = codes8(rr.rope.x, rr.rope.y);
   } else {
 #pragma unroll
     for (int k = 0; k < 9; ++k) *(LDS_AS u32x4*)(rowp + kGroupBytes * k + 16 * (q ^ sw)) = rr.v[k];
@@ -978,6 +1010,11 @@ mla_decode_kernel(DecodeArgs a) {
 
   const int head = slab * (HG * 32) + hg * 32 + (lane & 31);
   const bool head_ok = head < a.heads;
+  // per-tensor FP8 cache: every value is code / k_scale_inv; the factor goes
+  // into the score scale and the output normalisation, the ring holds codes
+  float kdesc = 1.0f;
+  if constexpr (kv_tensor(KVM)) kdesc = 1.0f / a.kv_scales[0];
+  const float scale_log2 = a.scale_log2 * kdesc;
 
   LaneTables tab;
   make_tables<NSPLIT, TILED>(tab, lane, w, part);
@@ -1075,7 +1112,7 @@ mla_decode_kernel(DecodeArgs a) {
         for (int c = 0; c < NCB; ++c) acc.o[c] = f32x16{};
         st.l_sum = 0.0f;
         st.m_seen = -INFINITY;
-        const SoftCtx sctx{xch, w, lane, a.scale_log2};
+        const SoftCtx sctx{xch, w, lane, scale_log2};
         SoftPipe sp;
         POps<NSPLIT, TILED> po;
         bf16x8 kb[kRA];
@@ -1195,7 +1232,7 @@ mla_decode_kernel(DecodeArgs a) {
           barrier();
           const f32x16 tot = total_scores<NSPLIT>(xch, sc, w, lane);
           f32x8 q0, q1;
-          softmax_slot(tot, slot_mask(nslots - 1), st, a.scale_log2, q0, q1, lane);
+          softmax_slot(tot, slot_mask(nslots - 1), st, scale_log2, q0, q1, lane);
           const LDS_AS float* ltab = (const LDS_AS float*)(ring + kFillRing * kSlotBytes) + last_pos * (4 * kTS);
           pv_load(ring + last_pos * kSlotBytes, tab, 0, va0);
           make_pops<NSPLIT, TILED>(po, q0, q1, ltab, part, lane);
@@ -1222,7 +1259,7 @@ mla_decode_kernel(DecodeArgs a) {
       // ---- epilogue: normalise and store this wave's columns (final output,
       // or this piece's partial in its workspace slot)
       const float l_tot = sum_halves(st.l_sum);
-      const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
+      const float inv = l_tot > 0.0f ? kdesc / l_tot : 0.0f;
       const float lse2 = l_tot > 0.0f ? st.m_ref + __builtin_amdgcn_logf(l_tot) : -INFINITY;
       if (head_ok) {
         const size_t pslot = (size_t)(b + r);
@@ -1441,18 +1478,22 @@ hipError_t launch_decode(const DecodeLaunch& d, hipStream_t stream) {
     const hipError_t e0 = hipGetLastError();
     if (e0 != hipSuccess) return e0;
   }
-  const int kvm = d.topk > 0 ? (d.kv_fp8 ? kKvFp8TopK : kKvBf16TopK) : (d.kv_fp8 ? kKvFp8 : kKvBf16);
+  const int kvm = d.kv_format == kKvFormatFp8Tile     ? (d.topk > 0 ? kKvFp8TopK : kKvFp8)
+                  : d.kv_format == kKvFormatFp8Tensor ? (d.topk > 0 ? kKvFp8TTopK : kKvFp8T)
+                                                      : (d.topk > 0 ? kKvBf16TopK : kKvBf16);
   const dim3 grid(a.per_xcd * 8 * a.slabs), block(kThreads);
   const int ns = nsplit_for_heads(d.heads);
   // one instantiation per (split, query format, cache layout)
 #define MLA_LAUNCH(NS, QF, KVM)                                                           \
   if (ns == NS && d.q_fp8 == QF && kvm == KVM)                                           \
     hipLaunchKernelGGL((mla_decode_kernel<NS, QF, KVM>), grid, block, 0, stream, a);
-#define MLA_LAUNCH_KV(NS, QF)  \
-  MLA_LAUNCH(NS, QF, kKvBf16)     \
-  MLA_LAUNCH(NS, QF, kKvFp8)      \
-  MLA_LAUNCH(NS, QF, kKvFp8TopK)  \
-  MLA_LAUNCH(NS, QF, kKvBf16TopK)
+#define MLA_LAUNCH_KV(NS, QF)      \
+  MLA_LAUNCH(NS, QF, kKvBf16)      \
+  MLA_LAUNCH(NS, QF, kKvFp8)       \
+  MLA_LAUNCH(NS, QF, kKvFp8TopK)   \
+  MLA_LAUNCH(NS, QF, kKvBf16TopK)  \
+  MLA_LAUNCH(NS, QF, kKvFp8T)      \
+  MLA_LAUNCH(NS, QF, kKvFp8TTopK)
   MLA_LAUNCH_KV(2, false)
   MLA_LAUNCH_KV(2, true)
   MLA_LAUNCH_KV(4, false)

@@ -15,15 +15,21 @@ struct DecodeLaunch {
   const int32_t* block_table;
   const int32_t* seqlens;
   const int32_t* topk_idx;  // nullptr: dense
-  const float* kv_scales;   // nullptr: bf16 cache
+  const float* kv_scales;   // nullptr: bf16 cache; per-tensor FP8: the one k_scale_inv
   void* out;
   float* lse;
   void* workspace;
   int32_t batch, heads, num_pages, max_pages, topk;
-  bool q_fp8, kv_fp8;
+  bool q_fp8;
+  int32_t kv_format;  // kKvFormat*
   float softmax_scale, q_descale;
   int32_t ranges;  // KV ranges of the split-KV decode (workgroups per head slab)
 };
+
+// Cache layouts of a decode launch.
+constexpr int32_t kKvFormatBf16 = 0;       // bf16 rows of 576
+constexpr int32_t kKvFormatFp8Tile = 1;    // 512 e4m3 codes + 64 bf16 rope, fp32 scale per 128 columns
+constexpr int32_t kKvFormatFp8Tensor = 2;  // 576 e4m3 codes, one per-tensor k_scale_inv
 
 // KV ranges for a device with `cus` compute units.
 int32_t decode_ranges(int32_t cus, int32_t batch, int32_t max_pages, int32_t topk, int32_t heads);
@@ -44,6 +50,18 @@ struct QueryLaunch {
   int32_t batch, heads, qkv_stride;
   float eps;
 };
+
+struct InsertLaunch {
+  const void* qkv;
+  const void* w_kva;
+  const int64_t* slots;
+  const float* k_scale_inv;
+  void* cache;
+  int32_t tokens, num_pages, qkv_stride;
+  float eps;
+};
+
+hipError_t launch_kv_insert(const InsertLaunch& k, hipStream_t stream);
 
 size_t query_workspace_bytes(int32_t batch, int32_t heads);
 hipError_t launch_query(const QueryLaunch& q, hipStream_t stream);

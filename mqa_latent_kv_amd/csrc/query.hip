@@ -21,6 +21,15 @@
 //    operand with ds_read_b64_tr_b16 (W_uk is stored c-contiguous, the
 //    reduction runs over p), the A operand is the bf16 nope q from the
 //    workspace.
+//
+// And the KV-cache insert of the same page (method `insert`), per new token t
+// with slot >= 0:
+//   rr   = 1 / sqrt(sum_k x[k]^2 / 512 + eps)      x = qkv[t, 1536:2048]
+//   row  = e4m3(bf16((x * rr) * w_kva) * ksi) | e4m3(qkv[t, 2048:2112] * ksi)
+//   cache[slot / 64][slot % 64][0:576] = row        ksi = k_scale_inv[0]
+//  * mla_kv_insert_kernel: one wave per token, all in registers (lane l holds
+//    latent values 8l..8l+7 and rope value l); the sum of squares is a DPP
+//    wave reduction, so the kernel has no LDS and no barrier.
 #include "mla_internal.h"
 
 namespace mla {
@@ -115,6 +124,55 @@ __device__ __forceinline__ float wave_sum(float v) {
   v = __uint_as_float(r16[0]) + __uint_as_float(r16[1]);
   const auto r32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
   return __uint_as_float(r32[0]) + __uint_as_float(r32[1]);
+}
+
+// ---------------------------------------------------------------- KV-cache insert
+
+constexpr int kQkvLatent = 1536;  // first qkv column of the latent KV row
+constexpr int kQkvRope = 2048;    // first qkv column of the rope key
+constexpr int kLatent = 512;
+constexpr int kCacheRow = 576;    // per-tensor FP8 cache row: 576 e4m3 codes
+constexpr int kCachePage = 64;
+
+struct InsertArgs {
+  const __bf16* qkv;
+  const __bf16* w_kva;
+  const int64_t* slots;
+  const float* k_scale_inv;
+  uint8_t* cache;
+  int64_t cache_rows;  // num_pages * 64
+  int32_t tokens, qkv_stride;
+  float eps;
+};
+
+__global__ void __launch_bounds__(kThreads) mla_kv_insert_kernel(InsertArgs a) {
+  const int lane = threadIdx.x & 63;
+  const int t = blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6);
+  if (t >= a.tokens) return;  // whole waves
+  const int64_t slot = a.slots[t];
+  if (slot < 0 || slot >= a.cache_rows) return;  // skipped token (uniform per wave)
+  const __bf16* row = a.qkv + (size_t)t * a.qkv_stride;
+  const bf16x8 x = *(const bf16x8*)(row + kQkvLatent + 8 * lane);
+  const bf16x8 wv = *(const bf16x8*)(a.w_kva + 8 * lane);
+  const float rope = (float)row[kQkvRope + lane];
+  const float ksi = *a.k_scale_inv;
+  float ss = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) ss = __builtin_fmaf((float)x[i], (float)x[i], ss);
+  ss = wave_sum(ss);
+  // 1/512 is a power of two: the mean is the exact quotient
+  const float rr = 1.0f / __builtin_sqrtf(ss * (1.0f / kLatent) + a.eps);
+  uint32_t lo = 0, hi = 0;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const __bf16 n = (__bf16)(((float)x[i] * rr) * (float)wv[i]);  // round to nearest even
+    const uint32_t c = e4m3_of_product((float)n, ksi);
+    if (i < 4) lo |= c << (8 * i);
+    else hi |= c << (8 * (i - 4));
+  }
+  uint8_t* dst = a.cache + (size_t)slot * kCacheRow;
+  *(uint2*)(dst + 8 * lane) = uint2{lo, hi};
+  dst[kLatent + lane] = e4m3_of_product(rope, ksi);
 }
 
 // ---------------------------------------------------------------- RMSNorm + Q_B
@@ -296,6 +354,22 @@ __global__ void __launch_bounds__(kThreads) mla_ql_kernel(QueryArgs a) {
 }
 
 }  // namespace
+
+hipError_t launch_kv_insert(const InsertLaunch& k, hipStream_t stream) {
+  InsertArgs a;
+  a.qkv = (const __bf16*)k.qkv;
+  a.w_kva = (const __bf16*)k.w_kva;
+  a.slots = k.slots;
+  a.k_scale_inv = k.k_scale_inv;
+  a.cache = (uint8_t*)k.cache;
+  a.cache_rows = (int64_t)k.num_pages * kCachePage;
+  a.tokens = k.tokens;
+  a.qkv_stride = k.qkv_stride;
+  a.eps = k.eps;
+  constexpr int per_wg = kThreads / 64;
+  hipLaunchKernelGGL(mla_kv_insert_kernel, dim3((k.tokens + per_wg - 1) / per_wg), dim3(kThreads), 0, stream, a);
+  return hipGetLastError();
+}
 
 size_t query_workspace_bytes(int32_t batch, int32_t heads) { return (size_t)batch * heads * kNope * 2 + 256; }
 

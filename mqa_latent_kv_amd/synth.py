@@ -130,7 +130,7 @@ def make_decode_inputs(
         kv_scales = log_uniform_scales(g, (num_pages, PAGE, D_NOPE // 128))
     elif kv_format == "fp8_tensor":
         kv = fp8_normal(g, (num_pages, PAGE, D_QK))
-        kv_scales = log_uniform_scales(g, (1,), -0.5, 0.5)  # k_scale_inv
+        kv_scales = log_uniform_scales(g, (1,), 0.0, 0.5)  # k_scale_inv in [1, 3.16]
     else:
         raise ValueError(kv_format)
     perm = torch.randperm(num_pages, generator=g).numpy().astype(np.int32)

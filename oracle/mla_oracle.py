@@ -302,7 +302,8 @@ def kv_insert(qkv, w_kva, cache, slots, k_scale_inv: float, eps: float = 1e-6):
     Returns a dict: ``cache`` (the written copy), ``normed_pre`` [T, 512] f64
     (before the bf16 rounding), ``normed`` (after it) and ``fp8_in`` [T, 576]
     (the values that are encoded).  Duplicate non-negative slots: the later
-    token's row wins (the GPU leaves that case unspecified).
+    token's row wins (the GPU leaves that case unspecified).  A slot at or
+    past pages * 64 names no row and, like a negative one, writes nothing.
     """
     qkv = np.asarray(qkv)
     x = bf16_bits_to_f64(qkv[:, KV_LATENT:KV_ROPE])
@@ -316,7 +317,7 @@ def kv_insert(qkv, w_kva, cache, slots, k_scale_inv: float, eps: float = 1e-6):
     out = np.array(cache, dtype=np.uint8, copy=True)
     page_size = out.shape[1]
     for t, slot in enumerate(np.asarray(slots).reshape(-1)):
-        if slot < 0:
+        if slot < 0 or slot >= out.shape[0] * page_size:
             continue
         page, offset = slot_page_offset(slot, page_size)
         out[page, offset, :] = codes[t]

@@ -30,7 +30,7 @@ def declared_functions():
 def test_header_declares_the_entry_points():
     fns = declared_functions()
     for name in ("mla_decode", "mla_decode_workspace_size", "mla_query", "mla_query_workspace_size",
-                 "mla_status_string", "mla_version"):
+                 "mla_kv_insert", "mla_status_string", "mla_version"):
         assert name in fns
 
 
@@ -51,6 +51,7 @@ def test_struct_layouts_match_header():
     # all members are 4-byte: the C structs have no padding
     assert ctypes.sizeof(mla.DecodeParams) == 9 * 4
     assert ctypes.sizeof(mla.QueryParams) == 4 * 4
+    assert ctypes.sizeof(mla.InsertParams) == 4 * 4
 
 
 def _params(**kw):
@@ -120,8 +121,20 @@ def test_decode_optional_arguments_must_match_params(L):
     assert _decode(L, _params(), topk=FAKE) == -1
     assert _decode(L, _params(topk=64)) in (-1, -2)
     # FP8 cache needs scales; a bf16 cache must not get them
-    assert _decode(L, _params(kv_fp8=True)) in (-1, -2)
+    assert _decode(L, _params(kv_format="fp8")) in (-1, -2)
+    assert _decode(L, _params(kv_format="fp8_tensor")) == -1
     assert _decode(L, _params(), scales=FAKE) == -1
+    # the per-tensor scale is one float: 4-byte alignment is enough
+    assert _passes_validation(_decode(L, _params(kv_format="fp8_tensor"), ws_bytes=1, scales=ctypes.c_void_p(0x1004)))
+    assert _decode(L, _params(kv_format="fp8_tensor"), scales=ctypes.c_void_p(0x1002)) == -1
+    assert _decode(L, _params(kv_format="fp8"), scales=ctypes.c_void_p(0x1004)) == -1
+    # the per-tensor layout is a cache format, not a query type
+    p = _params()
+    p.q_dtype = mla.MLA_DTYPE_FP8_E4M3_TENSOR
+    assert _decode(L, p) == -1
+    p = _params()
+    p.kv_dtype = 4
+    assert _decode(L, p, scales=FAKE) == -1
 
 
 MISALIGNED = ctypes.c_void_p(0x1008)  # 8-byte aligned only
@@ -131,7 +144,7 @@ def test_decode_rejects_misaligned_pointers(L):
     # the kernels move q, KV rows, outputs, scales and workspace in 16-byte units
     for name in ("q", "kv", "out", "ws"):
         assert _decode(L, _params(), **{name: MISALIGNED}) == -1, name
-    assert _decode(L, _params(kv_fp8=True), scales=MISALIGNED) == -1
+    assert _decode(L, _params(kv_format="fp8"), scales=MISALIGNED) == -1
     # int32 tables need only their natural alignment
     assert _passes_validation(_decode(L, _params(), ws_bytes=1, bt=ctypes.c_void_p(0x1004),
                                       sl=ctypes.c_void_p(0x1004)))
@@ -169,6 +182,35 @@ def test_query_validation(L):
         assert q(good, **{name: MISALIGNED}) == -1, name
     n = ctypes.c_size_t(0)
     assert L.mla_query_workspace_size(ctypes.byref(good), ctypes.byref(n)) == 0 and n.value > 0
+
+
+def test_kv_insert_validation(L):
+    """Every call here fails validation (or has no tokens), so nothing is
+    launched and the fake pointers are never used."""
+    def ins(p, **ptrs):
+        a = dict(qkv=FAKE, w=FAKE, slots=FAKE, ksi=FAKE, cache=FAKE)
+        a.update(ptrs)
+        return L.mla_kv_insert(ctypes.byref(p) if p is not None else None, a["qkv"], a["w"], a["slots"], a["ksi"],
+                               a["cache"], None)
+
+    P = mla.InsertParams
+    assert ins(None) == -1
+    assert ins(P(-1, 8, 2112, 1e-6)) == -1
+    assert ins(P(4, 0, 2112, 1e-6)) == -1
+    assert ins(P(4, 8, 2111, 1e-6)) == -1  # the rope key ends at column 2112
+    assert ins(P(4, 8, 2112, -1.0)) == -1
+    assert ins(P(4, 8, 2116, 1e-6)) == -2  # rows are read in 16-byte vectors
+    assert ins(P((1 << 24) + 1, 8, 2112, 1e-6)) == -2
+    assert ins(P(4, (1 << 25), 2112, 1e-6)) == -2  # slot rows must fit in 32 bits
+    for name in ("qkv", "w", "slots", "ksi", "cache"):
+        assert ins(P(4, 8, 2112, 1e-6), **{name: None}) == -1, name
+    for name in ("qkv", "w", "cache"):
+        assert ins(P(4, 8, 2112, 1e-6), **{name: MISALIGNED}) == -1, name
+    assert ins(P(4, 8, 2112, 1e-6), slots=ctypes.c_void_p(0x1004)) == -1  # int64 slots
+    assert ins(P(4, 8, 2112, 1e-6), ksi=ctypes.c_void_p(0x1002)) == -1
+    # no tokens: a valid call with nothing to launch
+    assert ins(P(0, 8, 2112, 1e-6)) == 0
+    assert ins(P(0, 8, 2112, 1e-6), slots=ctypes.c_void_p(0x1008), ksi=ctypes.c_void_p(0x1004)) == 0
 
 
 def test_workspace_size_needs_a_device(L):

@@ -110,6 +110,17 @@ CASES = {
     "topk_fp8_h16": dict(seed=83, batch=3, heads=16, seqlen_range=(50, 3000), kv_format="fp8", topk=300),
     "topk_bf16_h64": dict(seed=84, batch=3, heads=64, seqlen_range=(500, 3000), topk=700),
     "topk_bf16_h128": dict(seed=85, batch=2, heads=128, seqlens=[4000, 33], topk=256, topk_pad_max=40),
+    # per-tensor FP8 cache (the layout mla_kv_insert writes): 576 e4m3 codes per row, one k_scale_inv
+    "fp8t_h128_ragged": dict(seed=101, batch=3, heads=128, seqlens=[1, 300, 2100], kv_format="fp8_tensor"),
+    "fp8t_h64_ragged": dict(seed=102, batch=5, heads=64, seqlen_range=(1, 1500), kv_format="fp8_tensor"),
+    "fp8t_h16_fp8q": dict(seed=103, batch=4, heads=16, seqlen_range=(30, 900), kv_format="fp8_tensor",
+                          q_format="fp8", q_descale=8.0),
+    "fp8t_h8": dict(seed=104, batch=6, heads=8, seqlen_range=(1, 1300), kv_format="fp8_tensor"),
+    "fp8t_with_empty_seqs": dict(seed=105, batch=4, heads=32, seqlens=[0, 500, 0, 65], pages_per_seq=8,
+                                 kv_format="fp8_tensor"),
+    "topk_fp8t_h128": dict(seed=106, batch=3, heads=128, seqlens=[3000, 5000, 100], kv_format="fp8_tensor",
+                           topk=512, topk_pad_max=100),
+    "topk_fp8t_h64": dict(seed=107, batch=4, heads=64, seqlen_range=(200, 4000), kv_format="fp8_tensor", topk=1000),
 }
 
 
@@ -179,9 +190,11 @@ def _pow2_scales(inp, seed):
 
 
 @pytest.mark.parametrize("heads,kv_format,topk", [(128, "fp8", 0), (64, "fp8", 0), (8, "fp8", 0),
-                                                  (128, "fp8", 600), (64, "bf16", 600)])
+                                                  (128, "fp8", 600), (64, "bf16", 600),
+                                                  (128, "fp8_tensor", 0), (8, "fp8_tensor", 0),
+                                                  (64, "fp8_tensor", 600)])
 def test_one_hot_gather_fp8_and_topk_bit_exact(heads, kv_format, topk):
-    """As the bf16 one-hot test, for the FP8 cache (power-of-two scales) and
+    """As the bf16 one-hot test, for the FP8 caches (power-of-two scales) and
     for top-k gathers: j* is one of the listed entries, and the expected row
     is the oracle's dequantised V[row(j*)], exact in bf16."""
     B = 3
@@ -189,6 +202,8 @@ def test_one_hot_gather_fp8_and_topk_bit_exact(heads, kv_format, topk):
                                    kv_format=kv_format, topk=topk, topk_pad_max=50)
     if kv_format == "fp8":
         _pow2_scales(inp, heads)
+    if kv_format == "fp8_tensor":
+        inp["kv_scales"] = np.array([2.0], dtype=np.float32)  # code / 2 is exact in bf16
     rng = np.random.default_rng(heads + topk)
     q = np.empty_like(inp["q"])
     want = np.empty((B, heads, 512), dtype=np.uint16)
@@ -274,7 +289,8 @@ def test_page_permutation_invariance_bitwise():
     assert torch.equal(lse1.view(torch.int32), lse2.view(torch.int32))
 
 
-@pytest.mark.parametrize("name", ["paged_bf16_4096", "paged_bf16", "query_decode", "fp8_cache", "topk_sparse"])
+@pytest.mark.parametrize("name", ["paged_bf16_4096", "paged_bf16", "query_decode", "fp8_cache", "topk_sparse",
+                                  "insert_decode"])
 def test_full_size_workloads_sampled(name):
     """The full-size decode workloads, in the launch configuration the
     benchmark times, checked on a sample of sequences the oracle computes."""

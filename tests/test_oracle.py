@@ -462,6 +462,9 @@ def test_insert_slot_placement_by_hand():
     inp = synth.make_insert_inputs(31, tokens=5, num_pages=3)
     slots = np.array([130, -1, 0, 191, 64], dtype=np.int64)
     where = {0: (2, 2), 2: (0, 0), 3: (2, 63), 4: (1, 0)}  # written out by hand
+    # a slot past the pool (3 pages: 192 rows) writes nothing either
+    past = mo.kv_insert(inp["qkv"][:1], inp["w_kva"], inp["cache"], [192], inp["k_scale_inv"], inp["eps"])
+    np.testing.assert_array_equal(past["cache"], inp["cache"])
     res = mo.kv_insert(inp["qkv"], inp["w_kva"], inp["cache"], slots, inp["k_scale_inv"], inp["eps"])
     out = res["cache"]
     touched = np.zeros(out.shape[:2], dtype=bool)
