@@ -301,7 +301,9 @@ def main():
                "query_decode": "mla_qb_kernel + mla_ql_kernel + mla_decode_kernel<4,true,0> + mla_merge_kernel",
                "insert_decode": "mla_kv_insert_kernel + mla_decode_kernel<2,false,4> + mla_merge_kernel"}
     kernel = kernels.get(name, "mla_decode_kernel<2,false,0> + mla_merge_kernel")
-    mfma_bound = name == "topk_sparse"  # 345 flop per algorithmic byte, above the bf16 ridge
+    # above the ridge (2.5 PFLOP/s over 8 TB/s = 312.5 flop/B) the step is bound by the bf16 MFMA rate:
+    # top-k (345 flop/B) and the per-tensor FP8 cache at 128 heads (432 flop/B)
+    mfma_bound = flops / nbytes > MFMA_BF16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9)
     roofline = {
         "bound": "mfma" if mfma_bound else "hbm",
         "kernel": kernel + " (one call, timed together)",
