@@ -92,6 +92,7 @@ def make_decode_inputs(
     topk: int = 0,
     topk_pad_max: int = 256,
     q_descale: float = 1.0,
+    tokens_per_seq: int = 1,
 ) -> dict:
     """Seeded inputs for one decode call.
 
@@ -99,15 +100,18 @@ def make_decode_inputs(
     pages_per_seq: block-table width (default: pages of the longest sequence).
     num_pages: pool size (default: batch * pages_per_seq); the block table is the
     first batch*pages_per_seq entries of a random permutation of the pool.
-    topk > 0: per sequence, ``topk`` distinct positions drawn uniformly from
-    [0, seqlen), sorted, then the last U{0..topk_pad_max} slots set to -1.
+    topk > 0: per sequence (and query token), ``topk`` distinct positions drawn
+    uniformly from [0, seqlen), sorted, then the last U{0..topk_pad_max} slots
+    set to -1.
+    tokens_per_seq = T > 1: q is [B, T, H, 576] and the top-k lists [B, T, topk].
     """
     g = _gen(seed)
-    B, H = batch, heads
+    B, H, T = batch, heads, tokens_per_seq
+    qshape = (B, H, D_QK) if T == 1 else (B, T, H, D_QK)
     if q_format == "bf16":
-        q = bf16_normal(g, (B, H, D_QK))
+        q = bf16_normal(g, qshape)
     elif q_format == "fp8":
-        q = fp8_normal(g, (B, H, D_QK))
+        q = fp8_normal(g, qshape)
     else:
         raise ValueError(q_format)
     if seqlens is None:
@@ -137,15 +141,16 @@ def make_decode_inputs(
     block_table = np.ascontiguousarray(perm[: B * pages_per_seq].reshape(B, pages_per_seq))
     topk_idx = None
     if topk:
-        topk_idx = np.full((B, topk), -1, dtype=np.int32)
-        for b in range(B):
-            n = int(seqlens[b])
+        topk_idx = np.full((B * T, topk), -1, dtype=np.int32)
+        for bt in range(B * T):
+            n = int(seqlens[bt // T])
             k = min(topk, n)
             sel = torch.randperm(n, generator=g)[:k].sort().values.numpy().astype(np.int32)
             pad = int(torch.randint(0, topk_pad_max + 1, (1,), generator=g).item())
-            topk_idx[b, :k] = sel
+            topk_idx[bt, :k] = sel
             if pad:
-                topk_idx[b, topk - pad :] = -1
+                topk_idx[bt, topk - pad :] = -1
+        topk_idx = topk_idx.reshape((B, topk) if T == 1 else (B, T, topk))
     return {
         "q": q,
         "kv": kv,
@@ -159,6 +164,7 @@ def make_decode_inputs(
         "softmax_scale": 192.0**-0.5,
         "heads": H,
         "batch": B,
+        "tokens_per_seq": T,
     }
 
 

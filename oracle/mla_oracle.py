@@ -31,6 +31,14 @@ What is computed (sources are the three pages this library is built from):
   positions outside [0, seqlen) are masked (FlashMLA issue: invalid slots are
   masked when P is formed).
 
+* Several new query tokens per sequence (T > 1: multi-token prediction or
+  speculative decode).  The STAGE_D2 note packs the T*H query rows of a
+  sequence into one tile over the same KV rows.  The pages do not state the
+  mask; the reading taken is causal: the KV cache already holds the T new
+  tokens, and query token t (0-based) sees positions [0, seqlen - T + 1 + t),
+  itself included and its successors excluded.  Sparse lists are per query
+  token and are cut at the same limit.
+
 * FP8 cache: 512 e4m3fn codes with one fp32 scale per 128-column tile, the 64
   rope values kept in bf16; value = code * scale (the issue's per-buffer
   "dequant" K tiles).
@@ -180,6 +188,12 @@ def query_rows(q, b: int, q_format: str, q_descale: float) -> np.ndarray:
     raise ValueError(f"unknown q_format {q_format!r}")
 
 
+def causal_limit(seqlen: int, T: int, t: int) -> int:
+    """Positions visible to query token t of T new tokens: [0, seqlen - T + 1 + t)
+    (none when that is empty)."""
+    return max(int(seqlen) - int(T) + 1 + int(t), 0)
+
+
 def mla_decode(
     q,
     kv,
@@ -194,33 +208,40 @@ def mla_decode(
     softmax_scale: float = 192.0**-0.5,
     batches=None,
 ):
-    """Absorbed MLA decode, one query token per sequence.
+    """Absorbed MLA decode of T new query tokens per sequence.
 
-    q: [B, H, 576] (uint16 bf16 bits or uint8 e4m3 codes; a [B, 1, H, 576] array
-       is accepted).  kv / kv_scales: see ``dequant_rows``.  block_table: int32
-       [B, max_pages].  seqlens: int32 [B].  topk_idx: None (dense) or int32
-       [B, topk] / [B, 1, topk] logical positions with -1 padding.
+    q: [B, H, 576] (one token) or [B, T, H, 576] (uint16 bf16 bits or uint8 e4m3
+       codes).  kv / kv_scales: see ``dequant_rows``.  block_table: int32
+       [B, max_pages].  seqlens: int32 [B], the cache length including the T
+       new tokens.  topk_idx: None (dense) or int32 [B, topk] / [B, T, topk]
+       logical positions with -1 padding, one list per query token.
+    Query token t sees positions below ``causal_limit(seqlen, T, t)``.
     ``batches`` restricts the work to a subset of batch entries (for sampled
     checks of large configurations); other rows of the result stay NaN.
 
-    Returns a dict with f64 ``O`` [B, H, 512] and ``LSE`` [B, H] (natural log),
-    plus the stored forms ``out_bf16`` (uint16 bits, RNE) and ``lse_f32``.
+    Returns a dict with f64 ``O`` [B, H, 512] and ``LSE`` [B, H] (natural log)
+    when T = 1, [B, T, H, 512] and [B, T, H] when T > 1, plus the stored forms
+    ``out_bf16`` (uint16 bits, RNE) and ``lse_f32``.
     """
     q = np.asarray(q)
-    if q.ndim == 4:
-        q = q[:, 0]
-    B, H = q.shape[0], q.shape[1]
+    if q.ndim == 3:
+        q = q[:, None]
+    B, T, H = q.shape[0], q.shape[1], q.shape[2]
     seqlens = np.asarray(seqlens).reshape(-1)
     if topk_idx is not None:
-        topk_idx = np.asarray(topk_idx).reshape(B, -1)
-    O = np.full((B, H, D_V), np.nan)
-    LSE = np.full((B, H), np.nan)
+        topk_idx = np.asarray(topk_idx).reshape(B, T, -1)
+    O = np.full((B, T, H, D_V), np.nan)
+    LSE = np.full((B, T, H), np.nan)
     for b in range(B) if batches is None else batches:
-        pos = valid_positions(seqlens[b], None if topk_idx is None else topk_idx[b])
-        rows = physical_rows(np.asarray(block_table)[b], pos)
-        kf = dequant_rows(kv, rows, kv_format, kv_scales)
-        qf = query_rows(q, b, q_format, q_descale)
-        O[b], LSE[b], _ = attend(qf, kf, softmax_scale)
+        for t in range(T):
+            lim = causal_limit(seqlens[b], T, t)
+            pos = valid_positions(lim, None if topk_idx is None else topk_idx[b, t])
+            rows = physical_rows(np.asarray(block_table)[b], pos)
+            kf = dequant_rows(kv, rows, kv_format, kv_scales)
+            qf = query_rows(q[:, t], b, q_format, q_descale)
+            O[b, t], LSE[b, t], _ = attend(qf, kf, softmax_scale)
+    if T == 1:
+        O, LSE = O[:, 0], LSE[:, 0]
     return {
         "O": O,
         "LSE": LSE,

@@ -576,3 +576,64 @@ def test_insert_then_dequant_within_e4m3_bound():
     err = np.abs(back - want)
     bound = np.maximum(np.abs(want) * 2.0**-4, 2.0**-10 / ksi)
     assert np.all(err <= bound)
+
+
+# ------------------------------------------------------------------ several query tokens per sequence (causal)
+
+
+def test_multi_token_causal_mask_by_hand_against_sdpa():
+    """seqlen 5, T = 3: token 0 sees positions 0..2, token 1 sees 0..3, token 2
+    sees 0..4 (the mask below is written out by hand), checked against torch's
+    SDPA in float64 with that boolean mask."""
+    inp = synth.make_decode_inputs(37, batch=1, heads=2, seqlens=[5], num_pages=1, tokens_per_seq=3)
+    res = mo.mla_decode(inp["q"], inp["kv"], inp["block_table"], inp["seqlens"])
+    assert res["O"].shape == (1, 3, 2, 512) and res["LSE"].shape == (1, 3, 2)
+    visible = np.array([[1, 1, 1, 0, 0], [1, 1, 1, 1, 0], [1, 1, 1, 1, 1]], dtype=bool)
+    k, _ = _dense_kq(inp, 0)
+    q = torch.from_numpy(codecs.bf16_bits_to_f64(inp["q"][0]))  # [T, H, 576]
+    kt = torch.from_numpy(k)
+    for h in range(2):
+        o = torch.nn.functional.scaled_dot_product_attention(
+            q[:, h][None], kt[None], kt[:, :512][None], attn_mask=torch.from_numpy(visible)[None], scale=SCALE)[0]
+        np.testing.assert_allclose(res["O"][0, :, h], o.numpy(), rtol=1e-12, atol=1e-14)
+        s = (q[:, h] @ kt.T).numpy() * SCALE
+        lse = [np.log(np.exp(s[t, visible[t]]).sum()) for t in range(3)]
+        np.testing.assert_allclose(res["LSE"][0, :, h], lse, rtol=1e-13)
+
+
+def test_multi_token_reduces_to_single_token_at_each_position():
+    """Token t of a T-token decode equals a one-token decode of the same
+    sequence cut to its causal length, dense and sparse (the one-token path is
+    pinned against SDPA above)."""
+    T = 4
+    for topk in (0, 40):
+        inp = synth.make_decode_inputs(38 + topk, batch=3, heads=4, seqlens=[70, 3, 129], tokens_per_seq=T,
+                                       topk=topk, topk_pad_max=5)
+        res = mo.mla_decode(inp["q"], inp["kv"], inp["block_table"], inp["seqlens"], inp["topk_idx"])
+        for t in range(T):
+            cut = np.maximum(inp["seqlens"] - T + 1 + t, 0).astype(np.int32)
+            one = mo.mla_decode(inp["q"][:, t], inp["kv"], inp["block_table"], cut,
+                                None if topk == 0 else inp["topk_idx"][:, t])
+            np.testing.assert_array_equal(res["O"][:, t], one["O"])
+            np.testing.assert_array_equal(res["LSE"][:, t], one["LSE"])
+
+
+def test_multi_token_nothing_visible_and_sparse_cut():
+    """seqlen 2 with T = 4: tokens 0 and 1 see nothing (O = 0, LSE = -inf),
+    token 2 sees position 0 only, token 3 positions 0 and 1.  A sparse list
+    entry at or past the token's own position is masked."""
+    inp = synth.make_decode_inputs(39, batch=1, heads=2, seqlens=[2], num_pages=1, tokens_per_seq=4)
+    res = mo.mla_decode(inp["q"], inp["kv"], inp["block_table"], inp["seqlens"])
+    assert np.all(res["O"][0, :2] == 0) and np.all(np.isneginf(res["LSE"][0, :2]))
+    k, _ = _dense_kq(inp, 0)
+    np.testing.assert_allclose(res["O"][0, 2], np.broadcast_to(k[0, :512], (2, 512)), rtol=0, atol=1e-15)
+    # sparse: seqlen 10, T = 2; lists [9, 8, 1] for both tokens -> token 0 drops 9
+    inp = synth.make_decode_inputs(40, batch=1, heads=2, seqlens=[10], num_pages=1, tokens_per_seq=2)
+    lists = np.array([[[9, 8, 1], [9, 8, 1]]], dtype=np.int32)
+    res = mo.mla_decode(inp["q"], inp["kv"], inp["block_table"], inp["seqlens"], lists)
+    k, _ = _dense_kq(inp, 0)
+    qf = codecs.bf16_bits_to_f64(inp["q"][0])
+    o0, l0, _ = mo.attend(qf[0], k[[8, 1]], SCALE)
+    o1, l1, _ = mo.attend(qf[1], k[[9, 8, 1]], SCALE)
+    np.testing.assert_array_equal(res["O"][0, 0], o0)
+    np.testing.assert_array_equal(res["O"][0, 1], o1)
