@@ -21,6 +21,9 @@ every input resident in HBM before timing:
   insert_decode: mla_kv_insert of the 64 new tokens' latent rows (RMSNorm,
       per-tensor e4m3) at each sequence's last position, then mla_decode over
       that all-FP8 cache: batch 64, 128 heads, 4096 tokens each, 4096-page pool.
+  mtp_bf16: two new query tokens per sequence (causal), batch 64, 128 heads,
+      4096 tokens each, over the headline's bf16 pool: 256 query rows read
+      every KV row once.
 
 The decode call runs the work split, block-table translation (or the top-k
 prepass), KV streaming, QK^T, softmax, PV, epilogue and the split-KV merge on
@@ -64,6 +67,8 @@ WORKLOADS = {
     "insert_decode": "KV-cache insert (64 tokens: RMSNorm of the 512-wide latent row, per-tensor e4m3 of the 576 "
                      "columns) then decode over the all-FP8 cache: batch 64, 128 heads, seq_len 4096 each, "
                      "4096-page pool",
+    "mtp_bf16": "paged bf16 MLA decode of 2 new query tokens per sequence (causal): batch 64, 128 heads, "
+                "seq_len 4096 each, 4096-page pool",
 }
 
 
@@ -71,12 +76,28 @@ def traffic_file(workload: str) -> str:
     return os.path.join(ROOT, "profiles", f"decode_{workload}_traffic.json")
 
 
+def causal_limits(inp) -> np.ndarray:
+    """[B, T] positions visible to each query token: seqlen - T + 1 + t."""
+    T = inp.get("tokens_per_seq", 1)
+    seq = inp["seqlens"].astype(np.int64)[:, None]
+    return np.maximum(seq - T + 1 + np.arange(T)[None, :], 0)
+
+
 def kv_tokens(inp) -> int:
-    """KV rows the decode attends: all positions, or the valid top-k entries."""
+    """KV rows the decode must read: every position once for all query tokens
+    (dense), or the valid entries of every top-k list."""
     if inp.get("topk_idx") is not None:
-        t, seq = inp["topk_idx"], inp["seqlens"].astype(np.int64)[:, None]
-        return int(np.sum((t >= 0) & (t < seq)))
+        B, T = inp["batch"], inp.get("tokens_per_seq", 1)
+        t = inp["topk_idx"].reshape(B, T, -1)
+        return int(np.sum((t >= 0) & (t < causal_limits(inp)[:, :, None])))
     return int(inp["seqlens"].astype(np.int64).sum())
+
+
+def attended_pairs(inp) -> int:
+    """(query token, KV row) pairs the scores are computed for."""
+    if inp.get("topk_idx") is not None:
+        return kv_tokens(inp)
+    return int(causal_limits(inp).sum())
 
 
 def decode_bytes(inp) -> int:
@@ -85,7 +106,7 @@ def decode_bytes(inp) -> int:
     576 codes), the queries, the
     outputs (bf16 O + fp32 LSE), the block-table entries it reads, the
     sequence lengths and the top-k lists."""
-    B, H = inp["batch"], inp["heads"]
+    B, H = inp["batch"], inp["heads"] * inp.get("tokens_per_seq", 1)  # query rows per sequence
     row = {"bf16": 576 * 2, "fp8": 512 + 128 + 16, "fp8_tensor": 576}[inp["kv_format"]]
     qb = 576 * (2 if inp["q_format"] == "bf16" else 1)
     if inp.get("topk_idx") is not None:
@@ -97,7 +118,7 @@ def decode_bytes(inp) -> int:
 
 
 def decode_flops(inp) -> int:
-    return kv_tokens(inp) * 2 * inp["heads"] * (576 + 512)
+    return attended_pairs(inp) * 2 * inp["heads"] * (576 + 512)
 
 
 def query_bytes(qin) -> int:
@@ -217,15 +238,17 @@ def main():
         slots = bt[np.arange(B), last // 64].astype(np.int64) * 64 + last % 64
         di = mla.insert_to_device(ins, dev)
         di["slots"] = torch.from_numpy(slots).to(dev)
-    topk = 0 if inp.get("topk_idx") is None else inp["topk_idx"].shape[1]
+    T = inp.get("tokens_per_seq", 1)
+    topk = 0 if inp.get("topk_idx") is None else inp["topk_idx"].shape[-1]
     params = mla.decode_params(batch=B, heads=H, num_pages=inp["kv"].shape[0],
                                max_pages_per_seq=inp["block_table"].shape[1], topk=topk,
                                q_fp8=inp["q_format"] != "bf16", kv_format=inp["kv_format"],
-                               q_descale=inp["q_descale"])
+                               q_descale=inp["q_descale"], tokens_per_seq=T)
     stream = torch.cuda.current_stream(dev)
     ws = mla.decode_workspace(params, dev, stream)
-    out = torch.empty((B, H, 512), dtype=torch.bfloat16, device=dev)
-    lse = torch.empty((B, H), dtype=torch.float32, device=dev)
+    rows = (B, H) if T == 1 else (B, T, H)
+    out = torch.empty(rows + (512,), dtype=torch.bfloat16, device=dev)
+    lse = torch.empty(rows, dtype=torch.float32, device=dev)
     q = d["q"]
     if qin is not None:
         dq = mla.query_to_device(qin, dev)
@@ -299,7 +322,8 @@ def main():
     kernels = {"topk_sparse": "mla_topk_rows_kernel + mla_decode_kernel<2,false,2> + mla_merge_kernel",
                "fp8_cache": "mla_decode_kernel<2,false,1> + mla_merge_kernel",
                "query_decode": "mla_qb_kernel + mla_ql_kernel + mla_decode_kernel<4,true,0> + mla_merge_kernel",
-               "insert_decode": "mla_kv_insert_kernel + mla_decode_kernel<2,false,4> + mla_merge_kernel"}
+               "insert_decode": "mla_kv_insert_kernel + mla_decode_kernel<2,false,4> + mla_merge_kernel",
+               "mtp_bf16": "mla_decode_kernel<2,false,0,true> + mla_merge_kernel"}
     kernel = kernels.get(name, "mla_decode_kernel<2,false,0> + mla_merge_kernel")
     # above the ridge (2.5 PFLOP/s over 8 TB/s = 312.5 flop/B) the step is bound by the bf16 MFMA rate:
     # top-k (345 flop/B) and the per-tensor FP8 cache at 128 heads (432 flop/B)
@@ -327,7 +351,7 @@ def main():
         "ms_per_step": round(ms_per_step, 5),
         "us_per_step": round(ms_per_step * 1e3, 2),
         "frac_of_hbm_peak": round(value / HBM_PEAK_GBS, 4),
-        "tokens_per_s": round(B / (ms_per_step / 1e3), 1),
+        "tokens_per_s": round(B * T / (ms_per_step / 1e3), 1),
         "kv_tokens_per_s": round(kv_tokens(inp) / (ms_per_step / 1e3), 1),
         "cold_us_per_step_median": round(float(np.median(cold)) * 1e3, 2),
         "higher_is_better": True,
@@ -350,6 +374,8 @@ def main():
     }
     if ins is not None:
         ins["slots"] = slots
+    if T > 1:
+        res["config"]["tokens_per_seq"] = T
     res["cpu_baseline"] = None if args.no_cpu_baseline else cpu_baseline(inp, nbytes, qin=qin, ins=ins)
     print(json.dumps(res), flush=True)
 

@@ -89,6 +89,7 @@ extern "C" {
 #define MLA_FP8T_ROW_BYTES 576 /* per-tensor FP8 cache row: 576 e4m3 codes */
 #define MLA_QKV_WIDTH 2112  /* qkv row read by mla_kv_insert: q_a 1536 | latent 512 | rope 64 */
 #define MLA_MAX_INSERT_TOKENS (1 << 24)
+#define MLA_MAX_TOKENS_PER_SEQ 16
 #define MLA_MAX_HEADS 128
 #define MLA_MAX_BATCH 8192
 
@@ -102,6 +103,7 @@ typedef struct mla_decode_params {
   int32_t kv_dtype;          /* MLA_DTYPE_BF16, MLA_DTYPE_FP8_E4M3 or MLA_DTYPE_FP8_E4M3_TENSOR */
   float softmax_scale;       /* multiplies the full 576-wide dot, e.g. 192^-0.5 */
   float q_descale;           /* FP8 queries: value = code * q_descale (= 1/q_scale_inv); ignored for bf16 */
+  int32_t tokens_per_seq;    /* T new query tokens per sequence, 1 <= T <= MLA_MAX_TOKENS_PER_SEQ */
 } mla_decode_params;
 
 /*
@@ -122,9 +124,14 @@ int32_t mla_decode_workspace_init(const mla_decode_params* p, void* workspace, s
                                   void* stream);
 
 /*
- * Absorbed MLA decode, one query token per sequence.
+ * Absorbed MLA decode of T = tokens_per_seq new query tokens per sequence.
+ * With T > 1 (multi-token prediction, speculative decode) the mask is causal:
+ * the cache already holds the T new tokens, and query token t (0-based) sees
+ * positions [0, seqlens[b] - T + 1 + t).  The STAGE_D2 note packs the T*H
+ * query rows of a sequence into one tile; here a dense decode reads each KV
+ * row once for all T*H rows.
  *
- *  q           [B, H, 576] bf16, or e4m3 codes when q_dtype is FP8 (the
+ *  q           [B, T, H, 576] bf16, or e4m3 codes when q_dtype is FP8 (the
  *              MlaQuery output layout: cols 0..511 absorbed latent q, 512..575
  *              rope q).  Row stride 576 elements.
  *  kv_cache    bf16 cache: [num_pages, 64, 576] bf16.
@@ -135,19 +142,20 @@ int32_t mla_decode_workspace_init(const mla_decode_params* p, void* workspace, s
  *              sequence b; logical position t lives in row
  *              block_table[b, t/64]*64 + t%64 (the page/offset split of a slot
  *              in MlaQuery.insert).  Precondition: entries in [0, num_pages).
- *  seqlens     [B] int32: tokens of each sequence.  Precondition:
- *              0 <= seqlens[b] <= 64*max_pages_per_seq.  A sequence with nothing
- *              to attend gets O = 0 and LSE = -inf.
- *  topk_idx    NULL when topk == 0; else [B, topk] int32 logical positions
- *              (sparse decode).  Entries that are -1 or outside [0, seqlens[b])
- *              are masked (contribute nothing); duplicates count once per entry.
+ *  seqlens     [B] int32: tokens of each sequence (the T new ones included).
+ *              Precondition: 0 <= seqlens[b] <= 64*max_pages_per_seq.  A query
+ *              token with nothing to attend gets O = 0 and LSE = -inf.
+ *  topk_idx    NULL when topk == 0; else [B, T, topk] int32 logical positions
+ *              (sparse decode), one list per query token.  Entries that are -1
+ *              or outside [0, seqlens[b] - T + 1 + t) are masked (contribute
+ *              nothing); duplicates count once per entry.
  *  kv_scales   NULL for a bf16 cache; for an FP8 cache [num_pages, 64, 4] fp32,
  *              one scale per row and 128-column tile: k[d] = code[d]*scale[d/128]
  *              for d < 512.  Per-tensor FP8 cache: one fp32, the k_scale_inv
  *              the cache was written with; k[d] = code[d] / k_scale_inv for all
  *              576 columns.  Precondition: k_scale_inv finite and > 0.
- *  out         [B, H, 512] bf16 (round to nearest even).
- *  lse         [B, H] fp32, natural-log log-sum-exp of the scaled scores.
+ *  out         [B, T, H, 512] bf16 (round to nearest even).
+ *  lse         [B, T, H] fp32, natural-log log-sum-exp of the scaled scores.
  *  workspace   device scratch of at least mla_decode_workspace_size bytes;
  *              its contents are clobbered.  Calls that share a workspace must
  *              be ordered (one stream).

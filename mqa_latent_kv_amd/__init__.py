@@ -50,6 +50,7 @@ class DecodeParams(ctypes.Structure):
         ("kv_dtype", ctypes.c_int32),
         ("softmax_scale", ctypes.c_float),
         ("q_descale", ctypes.c_float),
+        ("tokens_per_seq", ctypes.c_int32),
     ]
 
 
@@ -142,13 +143,13 @@ def _expect(t, name, dtypes, shape=None):
 
 
 def decode_params(*, batch, heads, num_pages, max_pages_per_seq, topk=0, q_fp8=False, kv_format="bf16",
-                  softmax_scale=192.0**-0.5, q_descale=1.0) -> DecodeParams:
+                  softmax_scale=192.0**-0.5, q_descale=1.0, tokens_per_seq=1) -> DecodeParams:
     """kv_format: "bf16", "fp8" (per-tile scales) or "fp8_tensor" (one per-tensor scale)."""
     return DecodeParams(
         batch, heads, num_pages, max_pages_per_seq, topk,
         MLA_DTYPE_FP8_E4M3 if q_fp8 else MLA_DTYPE_BF16,
         KV_DTYPES[kv_format],
-        float(softmax_scale), float(q_descale),
+        float(softmax_scale), float(q_descale), int(tokens_per_seq),
     )
 
 
@@ -176,18 +177,26 @@ def mla_decode(q, kv_cache, block_table, seqlens, topk_idx=None, kv_scales=None,
                softmax_scale=192.0**-0.5, q_descale=1.0, workspace=None, stream=None):
     """Absorbed MLA decode (see include/mla.h).
 
-    q: [B, H, 576] torch.bfloat16, or uint8 / float8_e4m3fn codes.
+    q: [B, H, 576] (one query token per sequence) or [B, T, H, 576] (T new
+    tokens, causal), torch.bfloat16, or uint8 / float8_e4m3fn codes.
     kv_cache: bf16 [P, 64, 576]; or uint8 [P, 64, 640] FP8 rows (then kv_scales
     float32 [P, 64, 4]); or uint8 [P, 64, 576] per-tensor FP8 rows (then
     kv_scales the float32 [1] k_scale_inv).  block_table int32 [B, max_pages], seqlens int32 [B],
-    topk_idx int32 [B, topk] or None.  Returns (out bf16 [B, H, 512], lse fp32 [B, H]).
+    topk_idx int32 [B, topk] ([B, T, topk] for T tokens) or None.  Returns (out bf16 [B, H, 512], lse
+    fp32 [B, H]), or [B, T, H, 512] and [B, T, H] for a 4-D q.
     """
     import torch
 
-    if q.dim() == 4:
-        q = q.reshape(q.shape[0], q.shape[2], q.shape[3]) if q.shape[1] == 1 else q
     _expect(q, "q", (torch.bfloat16, torch.uint8, torch.float8_e4m3fn))
-    B, H, dq = q.shape
+    if q.dim() == 3:
+        B, H, dq = q.shape
+        T = 1
+        oshape, lshape = (B, H, D_V), (B, H)
+    elif q.dim() == 4:
+        B, T, H, dq = q.shape
+        oshape, lshape = (B, T, H, D_V), (B, T, H)
+    else:
+        raise ValueError("q must be [B, H, 576] or [B, T, H, 576]")
     if dq != D_QK:
         raise ValueError("q must have 576 columns")
     q_fp8 = q.dtype != torch.bfloat16
@@ -215,18 +224,20 @@ def mla_decode(q, kv_cache, block_table, seqlens, topk_idx=None, kv_scales=None,
     _expect(seqlens, "seqlens", (torch.int32,), (B,))
     topk = 0
     if topk_idx is not None:
-        topk_idx = topk_idx.reshape(B, -1)
         _expect(topk_idx, "topk_idx", (torch.int32,))
-        topk = topk_idx.shape[1]
+        if topk_idx.numel() % (B * T) != 0:
+            raise ValueError("topk_idx must be [B, topk] or [B, T, topk]")
+        topk = topk_idx.numel() // (B * T)
     dev = q.device
     if out is None:
-        out = torch.empty((B, H, D_V), dtype=torch.bfloat16, device=dev)
+        out = torch.empty(oshape, dtype=torch.bfloat16, device=dev)
     if lse is None:
-        lse = torch.empty((B, H), dtype=torch.float32, device=dev)
-    _expect(out, "out", (torch.bfloat16,), (B, H, D_V))
-    _expect(lse, "lse", (torch.float32,), (B, H))
+        lse = torch.empty(lshape, dtype=torch.float32, device=dev)
+    _expect(out, "out", (torch.bfloat16,), oshape)
+    _expect(lse, "lse", (torch.float32,), lshape)
     params = decode_params(batch=B, heads=H, num_pages=P, max_pages_per_seq=block_table.shape[1], topk=topk,
-                           q_fp8=q_fp8, kv_format=kv_format, softmax_scale=softmax_scale, q_descale=q_descale)
+                           q_fp8=q_fp8, kv_format=kv_format, softmax_scale=softmax_scale, q_descale=q_descale,
+                           tokens_per_seq=T)
     if workspace is None:
         workspace = decode_workspace(params, dev, stream)
     _expect(workspace, "workspace", (torch.uint8,))

@@ -21,12 +21,14 @@ int32_t check_decode_params(const mla_decode_params* p) {
     return MLA_ERR_INVALID_ARG;
   if (!valid_dtype(p->q_dtype) || !valid_kv_dtype(p->kv_dtype)) return MLA_ERR_INVALID_ARG;
   if (!(p->softmax_scale > 0.0f) || !(p->q_descale > 0.0f)) return MLA_ERR_INVALID_ARG;
-  if (p->batch > MLA_MAX_BATCH || !supported_heads(p->heads)) return MLA_ERR_UNSUPPORTED;
+  if (p->tokens_per_seq < 1) return MLA_ERR_INVALID_ARG;
+  if (p->batch > MLA_MAX_BATCH || !supported_heads(p->heads) || p->tokens_per_seq > MLA_MAX_TOKENS_PER_SEQ)
+    return MLA_ERR_UNSUPPORTED;
   // 32-bit offsets inside the kernels: logical positions and pool rows
   if ((int64_t)p->max_pages_per_seq * MLA_PAGE_SIZE > INT32_MAX) return MLA_ERR_UNSUPPORTED;
   if ((int64_t)p->num_pages * MLA_PAGE_SIZE > INT32_MAX) return MLA_ERR_UNSUPPORTED;
-  // top-k entries index a [B, topk] int32 array; keep B*topk in 32 bits
-  if ((int64_t)p->batch * p->topk > INT32_MAX) return MLA_ERR_UNSUPPORTED;
+  // top-k entries index a [B*T, topk] int32 array; keep B*T*topk in 32 bits
+  if ((int64_t)p->batch * p->tokens_per_seq * p->topk > INT32_MAX) return MLA_ERR_UNSUPPORTED;
   return MLA_OK;
 }
 
@@ -58,7 +60,7 @@ int32_t device_cus(int32_t* cus) {
 
 extern "C" {
 
-int32_t mla_version(void) { return 200; }
+int32_t mla_version(void) { return 300; }
 
 const char* mla_status_string(int32_t status) {
   switch (status) {
@@ -79,8 +81,10 @@ int32_t mla_decode_workspace_size(const mla_decode_params* p, size_t* bytes) {
   int32_t cus = 0;
   st = device_cus(&cus);
   if (st != MLA_OK) return st;
-  const int32_t ranges = mla::decode_ranges(cus, p->batch, p->max_pages_per_seq, p->topk, p->heads);
-  *bytes = mla::decode_workspace_bytes(ranges, p->batch, p->heads, p->topk);
+  int32_t eb = 0, eh = 0;
+  mla::effective_dims(p->batch, p->heads, p->topk, p->tokens_per_seq, &eb, &eh);
+  const int32_t ranges = mla::decode_ranges(cus, eb, p->max_pages_per_seq, p->topk, eh);
+  *bytes = mla::decode_workspace_bytes(ranges, eb, eh, p->topk);
   return MLA_OK;
 }
 
@@ -90,7 +94,9 @@ int32_t mla_decode_workspace_init(const mla_decode_params* p, void* workspace, s
   int32_t st = mla_decode_workspace_size(p, &need);
   if (st != MLA_OK) return st;
   if (!workspace || workspace_bytes < need) return MLA_ERR_WORKSPACE;
-  if (mla::init_decode_workspace(workspace, p->batch, p->heads, (hipStream_t)stream) != hipSuccess)
+  int32_t eb = 0, eh = 0;
+  mla::effective_dims(p->batch, p->heads, p->topk, p->tokens_per_seq, &eb, &eh);
+  if (mla::init_decode_workspace(workspace, eb, eh, (hipStream_t)stream) != hipSuccess)
     return MLA_ERR_LAUNCH;
   return MLA_OK;
 }
@@ -114,8 +120,10 @@ int32_t mla_decode(const mla_decode_params* p, const void* q, const void* kv_cac
   int32_t cus = 0;
   st = device_cus(&cus);
   if (st != MLA_OK) return st;
-  const int32_t ranges = mla::decode_ranges(cus, p->batch, p->max_pages_per_seq, p->topk, p->heads);
-  if (workspace_bytes < mla::decode_workspace_bytes(ranges, p->batch, p->heads, p->topk)) return MLA_ERR_WORKSPACE;
+  int32_t eb = 0, eh = 0;
+  mla::effective_dims(p->batch, p->heads, p->topk, p->tokens_per_seq, &eb, &eh);
+  const int32_t ranges = mla::decode_ranges(cus, eb, p->max_pages_per_seq, p->topk, eh);
+  if (workspace_bytes < mla::decode_workspace_bytes(ranges, eb, eh, p->topk)) return MLA_ERR_WORKSPACE;
   mla::DecodeLaunch d;
   d.q = q;
   d.kv = kv_cache;
@@ -131,6 +139,7 @@ int32_t mla_decode(const mla_decode_params* p, const void* q, const void* kv_cac
   d.num_pages = p->num_pages;
   d.max_pages = p->max_pages_per_seq;
   d.topk = p->topk;
+  d.tq = p->tokens_per_seq;
   d.q_fp8 = p->q_dtype == MLA_DTYPE_FP8_E4M3;
   d.kv_format = p->kv_dtype == MLA_DTYPE_BF16       ? mla::kKvFormatBf16
                 : p->kv_dtype == MLA_DTYPE_FP8_E4M3 ? mla::kKvFormatFp8Tile

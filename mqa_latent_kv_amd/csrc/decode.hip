@@ -108,6 +108,8 @@ struct DecodeArgs {
   const uint32_t* ws_masks;  // top-k: [B][mask_words] validity bits per 32-entry slot
   int32_t mask_words;        // ceil(topk / 32)
   int32_t batch, heads, num_pages, max_pages, topk;
+  int32_t tq;         // dense, several query tokens: T (rows of a sequence = T x heads_tok), else 1
+  int32_t heads_tok;  // query heads per token
   int32_t ranges;    // KV ranges (workgroups per head slab)
   int32_t slabs;     // head slabs per range
   int32_t per_xcd;   // ranges per XCD in the block -> (range, slab) mapping
@@ -967,7 +969,7 @@ __device__ __forceinline__ DmaJob prep_slot(int s, int pos, lds_char* ring, cons
 
 // ---------------------------------------------------------------- the kernel
 
-template <int NSPLIT, bool Q_FP8, int KVM>
+template <int NSPLIT, bool Q_FP8, int KVM, bool CAUSAL>
 __global__ void __launch_bounds__(kThreads, 1) __attribute__((amdgpu_waves_per_eu(1, 1)))
 mla_decode_kernel(DecodeArgs a) {
   __shared__ __attribute__((aligned(1024))) char ring_mem[kRing * kSlotBytes];  // KV ring, 4 x 36 KB
@@ -1015,6 +1017,11 @@ mla_decode_kernel(DecodeArgs a) {
   float kdesc = 1.0f;
   if constexpr (kv_tensor(KVM)) kdesc = 1.0f / a.kv_scales[0];
   const float scale_log2 = a.scale_log2 * kdesc;
+  // T query tokens per sequence (causal): row `head` is head head % heads_tok
+  // of query token t = head / heads_tok, which sees the positions below
+  // seqlen - lag with lag = T - 1 - t
+  int lag = 0;
+  if constexpr (CAUSAL) lag = a.tq - 1 - min(head, a.heads - 1) / a.heads_tok;
 
   LaneTables tab;
   make_tables<NSPLIT, TILED>(tab, lane, w, part);
@@ -1045,6 +1052,18 @@ mla_decode_kernel(DecodeArgs a) {
       const int first_r = p / pl.C, last_r = (p + n - 1) / pl.C;
       const int nsplit = last_r - first_r + 1;
       const int nslots = sg.nslots;
+      // causal: this lane's row sees the segment's tokens below lim; slots
+      // from causal_from on hide a token from some row (at most the last two)
+      int lim = sg.tok1, causal_from = nslots;
+      if constexpr (CAUSAL) {
+        lim = min(sg.tok1, seglen - lag);
+        const int lim0 = seglen - (a.tq - 1);
+        causal_from = lim0 >= sg.tok1 ? nslots : max(0, (lim0 - sg.tok0) / kTS);
+      }
+      auto causal_mask = [&](int s) -> uint32_t {
+        const int nv = lim - (sg.tok0 + s * kTS);
+        return nv <= 0 ? 0u : low_mask(nv);
+      };
 
       // query fragments (B operand of S^T = K.Q^T): head `head`, columns
       // 16g + 8*(lane/32) .. +7 for global k-step g of this wave's local step i
@@ -1149,7 +1168,16 @@ mla_decode_kernel(DecodeArgs a) {
             side.pvbuf = ring + (s & (kRing - 1)) * kSlotBytes;
             side.va0 = &va0;
             sp.own = sc;
-            sc = qk_partial<NSPLIT, kPipeDma | kPipeSoft>(kb, kbuf, qf, tab, side, sp, st, sctx);
+            if constexpr (CAUSAL) {
+              if (s >= causal_from) {
+                sp.mask = causal_mask(s);
+                sc = qk_partial<NSPLIT, kPipeDma | kPipeSoft | kPipeMask>(kb, kbuf, qf, tab, side, sp, st, sctx);
+              } else {
+                sc = qk_partial<NSPLIT, kPipeDma | kPipeSoft>(kb, kbuf, qf, tab, side, sp, st, sctx);
+              }
+            } else {
+              sc = qk_partial<NSPLIT, kPipeDma | kPipeSoft>(kb, kbuf, qf, tab, side, sp, st, sctx);
+            }
             make_pops<NSPLIT, TILED>(po, sp.p0, sp.p1, nullptr, part, lane);
             pv_slot<NSPLIT, TILED>(side.pvbuf, va0, po, tab, acc);
             wait_vm_lgkm0<63>();  // lgkmcnt(0): this wave's LDS reads are done
@@ -1206,6 +1234,10 @@ mla_decode_kernel(DecodeArgs a) {
               sp.mask = slot_mask(s);
               sc = qk_partial<NSPLIT, kPipeSoft | kPipeMask, TILED>(kb, pos_buf(p1), qf, tab, side, sp, st, sctx,
                                                                    pos_tab(p1), part);
+            } else if (CAUSAL && s >= causal_from) {
+              sp.mask = causal_mask(s);
+              sc = qk_partial<NSPLIT, kPipeSoft | kPipeMask, TILED>(kb, pos_buf(p1), qf, tab, side, sp, st, sctx,
+                                                                   pos_tab(p1), part);
             } else {
               sc = qk_partial<NSPLIT, kPipeSoft, TILED>(kb, pos_buf(p1), qf, tab, side, sp, st, sctx, pos_tab(p1),
                                                         part);
@@ -1232,7 +1264,7 @@ mla_decode_kernel(DecodeArgs a) {
           barrier();
           const f32x16 tot = total_scores<NSPLIT>(xch, sc, w, lane);
           f32x8 q0, q1;
-          softmax_slot(tot, slot_mask(nslots - 1), st, scale_log2, q0, q1, lane);
+          softmax_slot(tot, CAUSAL ? causal_mask(nslots - 1) : slot_mask(nslots - 1), st, scale_log2, q0, q1, lane);
           const LDS_AS float* ltab = (const LDS_AS float*)(ring + kFillRing * kSlotBytes) + last_pos * (4 * kTS);
           pv_load(ring + last_pos * kSlotBytes, tab, 0, va0);
           make_pops<NSPLIT, TILED>(po, q0, q1, ltab, part, lane);
@@ -1353,35 +1385,39 @@ __global__ void __launch_bounds__(kThreads) mla_merge_kernel(MergeArgs m) {
 // ---------------------------------------------------------------- top-k rows
 
 struct TopkArgs {
-  const int32_t* topk_idx;  // [B][topk] logical positions
+  const int32_t* topk_idx;  // [B*T][topk] logical positions, one list per query token
   const int32_t* block_table;
   const int32_t* seqlens;
-  int32_t* rows;     // [B][topk] physical row, -1 for a masked entry
-  uint32_t* masks;   // [B][mask_words] validity bits per 32-entry slot
+  int32_t* rows;     // [B*T][topk] physical row, -1 for a masked entry
+  uint32_t* masks;   // [B*T][mask_words] validity bits per 32-entry slot
   int32_t topk, mask_words, max_pages, num_pages;
+  int32_t tq;        // query tokens per sequence (T)
 };
 
-// Translate every top-k entry of sequence blockIdx.y: logical position j is
-// valid iff 0 <= j < seqlen, and lives in row block_table[b][j / 64]*64 +
-// j % 64 (integer arithmetic, exact).  One thread per entry.
+// Translate every top-k entry of list blockIdx.y = b*T + t (query token t of
+// sequence b): logical position j is valid iff 0 <= j < seqlen - T + 1 + t
+// (its causal limit; seqlen when T = 1), and lives in row
+// block_table[b][j / 64]*64 + j % 64 (integer arithmetic, exact).  One thread
+// per entry.
 __global__ void __launch_bounds__(kThreads) mla_topk_rows_kernel(TopkArgs t) {
-  const int b = blockIdx.y;
+  const int bt = blockIdx.y;
+  const int b = bt / t.tq;
   const int k = blockIdx.x * kThreads + threadIdx.x;
   bool valid = false;
   if (k < t.topk) {
-    const int j = t.topk_idx[(size_t)b * t.topk + k];
-    const int seqlen = min(max(t.seqlens[b], 0), t.max_pages * kPage);
+    const int j = t.topk_idx[(size_t)bt * t.topk + k];
+    const int seqlen = min(max(t.seqlens[b], 0), t.max_pages * kPage) - (t.tq - 1 - bt % t.tq);
     int row = -1;
     if (j >= 0 && j < seqlen) {
       valid = true;
       row = clamp_page(t.block_table[(size_t)b * t.max_pages + (j >> 6)], t.num_pages) * kPage + (j & (kPage - 1));
     }
-    t.rows[(size_t)b * t.topk + k] = row;
+    t.rows[(size_t)bt * t.topk + k] = row;
   }
   const uint64_t bits = __ballot(valid);
   const int word = k / kTS;
   if ((threadIdx.x & (kTS - 1)) == 0 && word < t.mask_words)
-    t.masks[(size_t)b * t.mask_words + word] = (uint32_t)(bits >> (threadIdx.x & 32));
+    t.masks[(size_t)bt * t.mask_words + word] = (uint32_t)(bits >> (threadIdx.x & 32));
 }
 
 int nsplit_for_heads(int heads) { return heads > 32 ? 2 : 4; }
@@ -1395,6 +1431,15 @@ __global__ void mla_zero_kernel(int* p, int n) {
 }
 
 }  // namespace
+
+// Sequences and query rows per sequence that the kernels see: T query tokens
+// of a dense decode are T*H rows over one sequence's KV (the KV is read once
+// for all of them); top-k lists are per query token, so each token is its own
+// sequence of H rows.
+void effective_dims(int32_t batch, int32_t heads, int32_t topk, int32_t tq, int32_t* eb, int32_t* eh) {
+  *eb = topk > 0 ? batch * tq : batch;
+  *eh = topk > 0 ? heads : heads * tq;
+}
 
 int32_t decode_ranges(int32_t cus, int32_t batch, int32_t max_pages, int32_t topk, int32_t heads) {
   const int64_t units = (int64_t)batch * (topk > 0 ? (topk + kPage - 1) / kPage : max_pages);
@@ -1427,7 +1472,11 @@ hipError_t init_decode_workspace(void* workspace, int32_t batch, int32_t heads, 
   return hipGetLastError();
 }
 
-hipError_t launch_decode(const DecodeLaunch& d, hipStream_t stream) {
+hipError_t launch_decode(const DecodeLaunch& din, hipStream_t stream) {
+  // the kernels see the effective batch and rows (d.heads: rows per sequence)
+  DecodeLaunch d = din;
+  effective_dims(din.batch, din.heads, din.topk, din.tq, &d.batch, &d.heads);
+  const bool causal = din.tq > 1 && din.topk == 0;
   DecodeArgs a;
   a.q = d.q;
   a.kv = (const char*)d.kv;
@@ -1457,6 +1506,8 @@ hipError_t launch_decode(const DecodeLaunch& d, hipStream_t stream) {
   a.num_pages = d.num_pages;
   a.max_pages = d.max_pages;
   a.topk = d.topk;
+  a.tq = causal ? din.tq : 1;
+  a.heads_tok = din.heads;
   a.ranges = d.ranges;
   a.per_xcd = (d.ranges + 7) / 8;
   a.scale_log2 = d.softmax_scale * kLog2e;
@@ -1473,6 +1524,7 @@ hipError_t launch_decode(const DecodeLaunch& d, hipStream_t stream) {
     t.mask_words = a.mask_words;
     t.max_pages = d.max_pages;
     t.num_pages = d.num_pages;
+    t.tq = din.tq;
     hipLaunchKernelGGL(mla_topk_rows_kernel, dim3((d.topk + kThreads - 1) / kThreads, d.batch), dim3(kThreads), 0,
                        stream, t);
     const hipError_t e0 = hipGetLastError();
@@ -1484,16 +1536,19 @@ hipError_t launch_decode(const DecodeLaunch& d, hipStream_t stream) {
   const dim3 grid(a.per_xcd * 8 * a.slabs), block(kThreads);
   const int ns = nsplit_for_heads(d.heads);
   // one instantiation per (split, query format, cache layout)
-#define MLA_LAUNCH(NS, QF, KVM)                                                           \
-  if (ns == NS && d.q_fp8 == QF && kvm == KVM)                                           \
-    hipLaunchKernelGGL((mla_decode_kernel<NS, QF, KVM>), grid, block, 0, stream, a);
-#define MLA_LAUNCH_KV(NS, QF)      \
-  MLA_LAUNCH(NS, QF, kKvBf16)      \
-  MLA_LAUNCH(NS, QF, kKvFp8)       \
-  MLA_LAUNCH(NS, QF, kKvFp8TopK)   \
-  MLA_LAUNCH(NS, QF, kKvBf16TopK)  \
-  MLA_LAUNCH(NS, QF, kKvFp8T)      \
-  MLA_LAUNCH(NS, QF, kKvFp8TTopK)
+#define MLA_LAUNCH(NS, QF, KVM, C)                                                           \
+  if (ns == NS && d.q_fp8 == QF && kvm == KVM && causal == C)                               \
+    hipLaunchKernelGGL((mla_decode_kernel<NS, QF, KVM, C>), grid, block, 0, stream, a);
+#define MLA_LAUNCH_KV(NS, QF)            \
+  MLA_LAUNCH(NS, QF, kKvBf16, false)     \
+  MLA_LAUNCH(NS, QF, kKvFp8, false)      \
+  MLA_LAUNCH(NS, QF, kKvFp8TopK, false)  \
+  MLA_LAUNCH(NS, QF, kKvBf16TopK, false) \
+  MLA_LAUNCH(NS, QF, kKvFp8T, false)     \
+  MLA_LAUNCH(NS, QF, kKvFp8TTopK, false) \
+  MLA_LAUNCH(NS, QF, kKvBf16, true)      \
+  MLA_LAUNCH(NS, QF, kKvFp8, true)       \
+  MLA_LAUNCH(NS, QF, kKvFp8T, true)
   MLA_LAUNCH_KV(2, false)
   MLA_LAUNCH_KV(2, true)
   MLA_LAUNCH_KV(4, false)

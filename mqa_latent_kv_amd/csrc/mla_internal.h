@@ -20,6 +20,7 @@ struct DecodeLaunch {
   float* lse;
   void* workspace;
   int32_t batch, heads, num_pages, max_pages, topk;
+  int32_t tq;  // query tokens per sequence (T >= 1); batch and heads are per the C ABI (B, H)
   bool q_fp8;
   int32_t kv_format;  // kKvFormat*
   float softmax_scale, q_descale;
@@ -31,6 +32,9 @@ constexpr int32_t kKvFormatBf16 = 0;       // bf16 rows of 576
 constexpr int32_t kKvFormatFp8Tile = 1;    // 512 e4m3 codes + 64 bf16 rope, fp32 scale per 128 columns
 constexpr int32_t kKvFormatFp8Tensor = 2;  // 576 e4m3 codes, one per-tensor k_scale_inv
 
+// Sequences and rows per sequence the kernels see for B sequences of T query
+// tokens of H heads (the ranges and the workspace are sized on these).
+void effective_dims(int32_t batch, int32_t heads, int32_t topk, int32_t tq, int32_t* eb, int32_t* eh);
 // KV ranges for a device with `cus` compute units.
 int32_t decode_ranges(int32_t cus, int32_t batch, int32_t max_pages, int32_t topk, int32_t heads);
 // Workspace bytes for a decode launch with `ranges` KV ranges.

@@ -220,6 +220,7 @@ WORKLOADS = {
     "fp8_cache": dict(seed=3, batch=32, heads=64, seqlen_range=(8192, 32768), num_pages=16384, pages_per_seq=512, kv_format="fp8"),
     "topk_sparse": dict(seed=4, batch=32, heads=128, seqlens=[65536] * 32, num_pages=32768, pages_per_seq=1024, kv_format="fp8", topk=2048, topk_pad_max=256),
     "insert_decode": dict(seed=6, batch=64, heads=128, seqlens=[4096] * 64, num_pages=4096, pages_per_seq=64, kv_format="fp8_tensor"),
+    "mtp_bf16": dict(seed=7, batch=64, heads=128, seqlens=[4096] * 64, num_pages=4096, pages_per_seq=64, tokens_per_seq=2),
     "query_decode": dict(seed=5, batch=64, heads=8, seqlens=[8192] * 64, num_pages=8192, pages_per_seq=128, q_format="fp8", q_descale=8.0),
 }
 

@@ -49,7 +49,7 @@ def test_version_and_status_strings(L):
 
 def test_struct_layouts_match_header():
     # all members are 4-byte: the C structs have no padding
-    assert ctypes.sizeof(mla.DecodeParams) == 9 * 4
+    assert ctypes.sizeof(mla.DecodeParams) == 10 * 4
     assert ctypes.sizeof(mla.QueryParams) == 4 * 4
     assert ctypes.sizeof(mla.InsertParams) == 4 * 4
 
@@ -148,6 +148,17 @@ def test_decode_rejects_misaligned_pointers(L):
     # int32 tables need only their natural alignment
     assert _passes_validation(_decode(L, _params(), ws_bytes=1, bt=ctypes.c_void_p(0x1004),
                                       sl=ctypes.c_void_p(0x1004)))
+
+
+def test_decode_tokens_per_seq_bounds(L):
+    assert _decode(L, _params(tokens_per_seq=0)) == -1
+    assert _decode(L, _params(tokens_per_seq=17)) == -2
+    assert _passes_validation(_decode(L, _params(tokens_per_seq=16), ws_bytes=1))
+    # B * T * topk entries must stay within 32-bit offsets
+    p = _params(batch=4096, topk=(1 << 31) // 8192, tokens_per_seq=2)
+    assert _decode(L, p, topk=FAKE) == -2
+    p = _params(batch=4096, topk=(1 << 31) // 8192 - 1, tokens_per_seq=2)
+    assert _passes_validation(_decode(L, p, ws_bytes=1, topk=FAKE))
 
 
 def test_decode_rejects_topk_lists_beyond_32_bit_offsets(L):

@@ -73,7 +73,7 @@ def compare(inp, out, lse, batches=None, rtol=0.0, scale=None):
         i = np.unravel_index(np.argmax(exc), exc.shape)
         sc_i = "none" if scale is None else f"{scale[sel][i]:.6g}"
         _say(f"   worst at {i}: gpu={go[i]:.6g} ref={ro[i]:.6g} scale={sc_i} "
-             f"lse gpu={gl[i[:2]]:.6g} ref={rl[i[:2]]:.6g}")
+             f"lse gpu={gl[i[:-1]]:.6g} ref={rl[i[:-1]]:.6g}")
     _say(f"   max|dO|={err_o:.3e} (max|O|={np.max(np.abs(ro)):.3e}, max excess over rtol term={excess:.3e})"
          f"  max|dLSE|={err_l:.3e}")
     assert err_l <= LSE_TOL
@@ -121,6 +121,24 @@ CASES = {
     "topk_fp8t_h128": dict(seed=106, batch=3, heads=128, seqlens=[3000, 5000, 100], kv_format="fp8_tensor",
                            topk=512, topk_pad_max=100),
     "topk_fp8t_h64": dict(seed=107, batch=4, heads=64, seqlen_range=(200, 4000), kv_format="fp8_tensor", topk=1000),
+    # T new query tokens per sequence, causal: token t sees positions below seqlen - T + 1 + t.
+    # Lengths put the hidden tail inside one slot, across two slots (seqlen % 32 < T - 1) and
+    # before any position (seqlen < T).
+    "mtp_t2_h64": dict(seed=111, batch=5, heads=64, seqlens=[1, 33, 64, 700, 2049], tokens_per_seq=2),
+    "mtp_t3_h128": dict(seed=112, batch=3, heads=128, seqlens=[2, 129, 1500], tokens_per_seq=3),
+    "mtp_t4_h8": dict(seed=113, batch=6, heads=8, seqlens=[3, 4, 32, 34, 97, 1300], tokens_per_seq=4),
+    "mtp_t16_h8": dict(seed=114, batch=3, heads=8, seqlens=[10, 47, 600], tokens_per_seq=16),
+    "mtp_t2_h16_fp8q": dict(seed=115, batch=4, heads=16, seqlen_range=(30, 900), tokens_per_seq=2, q_format="fp8",
+                            q_descale=8.0),
+    "mtp_t2_h64_fp8": dict(seed=116, batch=4, heads=64, seqlens=[1, 65, 500, 1025], tokens_per_seq=2,
+                           kv_format="fp8"),
+    "mtp_t3_h32_fp8t": dict(seed=117, batch=4, heads=32, seqlens=[2, 35, 300, 999], tokens_per_seq=3,
+                            kv_format="fp8_tensor"),
+    "mtp_long_split_t2_h128": dict(seed=118, batch=1, heads=128, seqlens=[20000], tokens_per_seq=2),
+    "mtp_topk_t2_h64_fp8": dict(seed=119, batch=3, heads=64, seqlens=[3000, 800, 40], tokens_per_seq=2,
+                                kv_format="fp8", topk=512, topk_pad_max=60),
+    "mtp_topk_t3_h128_bf16": dict(seed=120, batch=2, heads=128, seqlens=[2000, 300], tokens_per_seq=3, topk=256,
+                                  topk_pad_max=30),
 }
 
 
@@ -129,6 +147,27 @@ def test_decode_matches_oracle(name):
     kw = dict(CASES[name])
     inp = synth.make_decode_inputs(kw.pop("seed"), **kw)
     _say(f"[decode parity] case={name} B={inp['batch']} H={inp['heads']} seqlens[:8]={inp['seqlens'][:8].tolist()}")
+    out, lse = run_gpu(inp)
+    compare(inp, out, lse)
+
+
+def test_multi_token_causal_boundary():
+    """Every query row points at the first position its token must not see
+    (q = 8 k at that position; the last token, which sees everything, points
+    at its own position): a row that leaked it would put nearly all its weight
+    there, far outside the tolerance."""
+    T = 3
+    inp = synth.make_decode_inputs(121, batch=4, heads=64, seqlens=[3, 40, 64, 1111], tokens_per_seq=T)
+    kv = inp["kv"].reshape(-1, 576)
+    q = np.empty_like(inp["q"])
+    for b in range(4):
+        for t in range(T):
+            lim = mo.causal_limit(inp["seqlens"][b], T, t)
+            pos = min(lim, int(inp["seqlens"][b]) - 1)
+            row = mo.physical_rows(inp["block_table"][b], np.array([pos]))[0]
+            q[b, t] = codecs.f64_to_bf16_bits(8.0 * codecs.bf16_bits_to_f64(kv[row]))[None]
+    inp["q"] = q
+    _say("[decode causal boundary] T=3 H=64")
     out, lse = run_gpu(inp)
     compare(inp, out, lse)
 
@@ -290,7 +329,7 @@ def test_page_permutation_invariance_bitwise():
 
 
 @pytest.mark.parametrize("name", ["paged_bf16_4096", "paged_bf16", "query_decode", "fp8_cache", "topk_sparse",
-                                  "insert_decode"])
+                                  "insert_decode", "mtp_bf16"])
 def test_full_size_workloads_sampled(name):
     """The full-size decode workloads, in the launch configuration the
     benchmark times, checked on a sample of sequences the oracle computes."""
