@@ -242,10 +242,17 @@ def mla_decode(
             O[b, t], LSE[b, t], _ = attend(qf, kf, softmax_scale)
     if T == 1:
         O, LSE = O[:, 0], LSE[:, 0]
+    # stored forms, of the computed rows only when a subset was asked for
+    if batches is None:
+        out_bf16 = f64_to_bf16_bits(O)
+    else:
+        idx = sorted(set(int(b) for b in batches))
+        out_bf16 = np.zeros(O.shape, dtype=np.uint16)
+        out_bf16[idx] = f64_to_bf16_bits(O[idx])
     return {
         "O": O,
         "LSE": LSE,
-        "out_bf16": f64_to_bf16_bits(O),
+        "out_bf16": out_bf16,
         "lse_f32": LSE.astype(np.float32),
     }
 
