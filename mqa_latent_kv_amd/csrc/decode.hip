@@ -52,6 +52,13 @@
 //    the e4m3 codes become bf16 exactly.  Tile scales multiply the partial
 //    scores in fp32; the per-tensor 1/k_scale_inv folds into the score scale
 //    and the output normalisation.
+//  * Several query tokens per sequence (CAUSAL): the T*H query rows of a
+//    sequence are packed like heads (row t*H + h), so one read of each KV row
+//    serves all of them; row t sees positions below seqlen - T + 1 + t.  The
+//    rows' limits differ only in the last T - 1 positions, so the masked
+//    softmax runs only from the first slot that hides a position from some
+//    row.  Top-k lists are per query token: each token is its own sequence
+//    of H rows, and the row prepass cuts its list at the token's limit.
 //  * Softmax in base 2 against a fixed reference per head: the first slot's
 //    max.  Later slots may exceed it by up to 16 (P <= 2^16, exact in fp32 and
 //    as relative bf16); if any head's scores rise further, the workgroup
