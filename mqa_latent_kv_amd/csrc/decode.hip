@@ -1344,43 +1344,78 @@ struct MergeArgs {
   int32_t heads;
 };
 
-constexpr int kMergeHeads = 2;  // heads per merge workgroup, 128 threads each
+constexpr int kMergeHeads = 4;  // heads per merge workgroup, 64 threads each
 
 // O = sum_s 2^(lse_s - M) O_s / sum_s 2^(lse_s - M) with M = max_s lse_s, and
 // LSE = M + log2 sum_s 2^(lse_s - M) (back to natural log), for sequences the
 // decode kernel split over several ranges; piece s sits in workspace slot
-// first + s.  A thread owns one float4 column group of one head, so the grid
-// has B * H / 2 workgroups, and keeps the loads of up to eight pieces in
-// flight.
+// first + s.  A thread owns two float4 column groups of one head, and the
+// grid has B * H / 4 workgroups.  Pieces go in chunks of up to eight whose LSEs
+// and O columns are all requested together (one memory latency per chunk);
+// a later chunk with a larger max rescales the sums so far (up to eight
+// pieces, M is the max of all of them, as written above).
+constexpr int kMergeChunk = 8;
+constexpr int kMergeU = kDV / 4 / (kThreads / kMergeHeads);  // float4 columns per thread
+
+// Pieces s0 .. s0+N-1 of one column group: every load issued before any is
+// used (a fixed count, so no branch separates them).
+template <int N>
+__device__ __forceinline__ void merge_chunk(const float* lse_col, const f32x4* src0, size_t pstride, int heads,
+                                            int s0, f32x4 (&acc)[kMergeU], float& mx, float& wsum) {
+  constexpr int TPH = kThreads / kMergeHeads;
+  float l[N];
+  f32x4 v[N][kMergeU];
+#pragma unroll
+  for (int i = 0; i < N; ++i) {
+    l[i] = lse_col[(size_t)(s0 + i) * heads];
+#pragma unroll
+    for (int u = 0; u < kMergeU; ++u) v[i][u] = src0[(s0 + i) * pstride + u * TPH];
+  }
+  float cm = mx;
+#pragma unroll
+  for (int i = 0; i < N; ++i) cm = fmaxf(cm, l[i]);
+  // rescale what the earlier chunks summed (nothing before the first)
+  const float r = mx == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(mx - cm);
+#pragma unroll
+  for (int u = 0; u < kMergeU; ++u) acc[u] *= r;
+  wsum *= r;
+#pragma unroll
+  for (int i = 0; i < N; ++i) {
+    const float wgt = l[i] == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(l[i] - cm);
+#pragma unroll
+    for (int u = 0; u < kMergeU; ++u) acc[u] += wgt * v[i][u];
+    wsum += wgt;
+  }
+  mx = cm;
+}
+
 __global__ void __launch_bounds__(kThreads) mla_merge_kernel(MergeArgs m) {
   const int b = blockIdx.x;
   const int2 info = m.seq[b];
   const int first = info.x, nsplit = info.y;
   if (nsplit <= 1) return;
   constexpr int TPH = kThreads / kMergeHeads;
-  constexpr int U = kDV / 4 / TPH;
   const int head = blockIdx.y * kMergeHeads + threadIdx.x / TPH, sub = threadIdx.x % TPH;
   if (head >= m.heads) return;
   const float* lse_col = m.ws_lse + (size_t)first * m.heads + head;
-  float mx = -INFINITY;
-  for (int s = 0; s < nsplit; ++s) mx = fmaxf(mx, lse_col[(size_t)s * m.heads]);
   const size_t pstride = (size_t)m.heads * (kDV / 4);  // float4 per piece
   const f32x4* src0 = (const f32x4*)(m.ws_o + ((size_t)first * m.heads + head) * kDV) + sub;
+  constexpr int U = kMergeU;
   f32x4 acc[U];
 #pragma unroll
   for (int u = 0; u < U; ++u) acc[u] = f32x4{};
-  float wsum = 0.0f;
-#pragma unroll 8
-  for (int s = 0; s < nsplit; ++s) {
-    const float l = lse_col[(size_t)s * m.heads];
-    const float wgt = l == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(l - mx);
-    const f32x4* ps = src0 + s * pstride;
-    f32x4 v[U];
-#pragma unroll
-    for (int u = 0; u < U; ++u) v[u] = ps[u * TPH];
-#pragma unroll
-    for (int u = 0; u < U; ++u) acc[u] += wgt * v[u];
-    wsum += wgt;
+  float mx = -INFINITY, wsum = 0.0f;
+  for (int s0 = 0; s0 < nsplit; s0 += kMergeChunk) {
+    switch (min(kMergeChunk, nsplit - s0)) {  // uniform over the workgroup
+      case 1: merge_chunk<1>(lse_col, src0, pstride, m.heads, s0, acc, mx, wsum); break;
+      case 2: merge_chunk<2>(lse_col, src0, pstride, m.heads, s0, acc, mx, wsum); break;
+      case 3: merge_chunk<3>(lse_col, src0, pstride, m.heads, s0, acc, mx, wsum); break;
+      case 4: merge_chunk<4>(lse_col, src0, pstride, m.heads, s0, acc, mx, wsum); break;
+      case 5: merge_chunk<5>(lse_col, src0, pstride, m.heads, s0, acc, mx, wsum); break;
+      case 6: merge_chunk<6>(lse_col, src0, pstride, m.heads, s0, acc, mx, wsum); break;
+      case 7: merge_chunk<7>(lse_col, src0, pstride, m.heads, s0, acc, mx, wsum); break;
+      default: merge_chunk<8>(lse_col, src0, pstride, m.heads, s0, acc, mx, wsum); break;
+    }
   }
   const float inv = wsum > 0.0f ? 1.0f / wsum : 0.0f;
   bf16x4* dst = (bf16x4*)((__bf16*)m.out + ((size_t)b * m.heads + head) * kDV) + sub;

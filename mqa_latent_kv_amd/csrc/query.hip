@@ -149,13 +149,17 @@ __global__ void __launch_bounds__(kThreads) mla_kv_insert_kernel(InsertArgs a) {
   const int lane = threadIdx.x & 63;
   const int t = blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6);
   if (t >= a.tokens) return;  // whole waves
+  // every load is issued before the slot decides anything (one memory latency)
   const int64_t slot = a.slots[t];
-  if (slot < 0 || slot >= a.cache_rows) return;  // skipped token (uniform per wave)
   const __bf16* row = a.qkv + (size_t)t * a.qkv_stride;
   const bf16x8 x = *(const bf16x8*)(row + kQkvLatent + 8 * lane);
   const bf16x8 wv = *(const bf16x8*)(a.w_kva + 8 * lane);
   const float rope = (float)row[kQkvRope + lane];
   const float ksi = *a.k_scale_inv;
+  // (the empty asm takes the loaded values, so the compiler cannot sink the
+  // loads below the branch)
+  asm volatile("" ::"v"(x), "v"(wv), "v"(rope), "s"(ksi));
+  if (slot < 0 || slot >= a.cache_rows) return;  // skipped token (uniform per wave)
   float ss = 0.0f;
 #pragma unroll
   for (int i = 0; i < 8; ++i) ss = __builtin_fmaf((float)x[i], (float)x[i], ss);
