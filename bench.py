@@ -1,7 +1,7 @@
 """Benchmark of the MLA decode hot path on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
-                    [--no-cpu-baseline] [--profile-run]
+                    [--no-cpu-baseline] [--profile-run] [--graph]
 
 A step is one pass of the hot path over one batch of synthetic input, with
 every input resident in HBM before timing:
@@ -27,7 +27,11 @@ every input resident in HBM before timing:
 
 The decode call runs the work split, block-table translation (or the top-k
 prepass), KV streaming, QK^T, softmax, PV, epilogue and the split-KV merge on
-the GPU.  Prints one JSON line: algorithmic HBM throughput (GB/s) as
+the GPU.  Each step calls the entry points from Python; with --graph the
+step's calls are recorded once into a HIP graph and every timed step replays
+it (measured slower on this ROCm: the replay adds more per-kernel time than the
+calls cost the host, and the host stays ahead of the GPU either way).  Either
+way the timed steps must reproduce the first step's output bit for bit.  Prints one JSON line: algorithmic HBM throughput (GB/s) as
 `value`, µs/step, tokens/s, a `roofline` object (the step's kernels timed with
 HIP events on their stream) and a `cpu_baseline` object (the float64 CPU
 oracle on a bounded sample of the same workload).
@@ -207,6 +211,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="paged_bf16_4096", choices=list(WORKLOADS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--graph", action="store_true",
+                    help="replay a HIP graph of the step instead of calling the entry points every step")
     ap.add_argument("--profile-run", action="store_true",
                     help="for rocprofv3 counter runs: run the steps untimed, then a plain device copy of "
                          f"{CALIB_BYTES >> 20} MiB (read {CALIB_BYTES >> 20} MiB, write as much) per step as the "
@@ -256,22 +262,41 @@ def main():
         qws = torch.empty(max(mla.mla_query_workspace_size(mla.QueryParams(B, H, 1536, qin["eps"])), 1),
                           dtype=torch.uint8, device=dev)
 
+    # every call goes to the current stream (the capture stream while a graph
+    # of the step is recorded)
     def step():
         if ins is not None:
-            mla.mla_kv_insert(di["qkv"], di["w_kva"], di["slots"], d["kv_scales"], d["kv"], eps=ins["eps"],
-                              stream=stream)
+            mla.mla_kv_insert(di["qkv"], di["w_kva"], di["slots"], d["kv_scales"], d["kv"], eps=ins["eps"])
         if qin is not None:
             mla.mla_query(dq["qkv"], dq["w_qa"], dq["w_qb"], dq["w_uk"], dq["q_scale_inv"], out=q, eps=qin["eps"],
-                          workspace=qws, stream=stream)
+                          workspace=qws)
         mla.mla_decode(q, d["kv"], d["block_table"], d["seqlens"], d["topk_idx"], d["kv_scales"], out=out, lse=lse,
-                       q_descale=inp["q_descale"], workspace=ws, stream=stream)
+                       q_descale=inp["q_descale"], workspace=ws)
 
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
+    first_out = (out.clone(), lse.clone())
+    run = step
+    if args.graph:
+        # the step's kernels recorded once into a HIP graph and replayed: the
+        # same launches with the same arguments, without the Python and
+        # launch overhead of every call (no memset nodes: the library clears
+        # nothing with hipMemsetAsync)
+        side = torch.cuda.Stream(device=dev)
+        side.wait_stream(stream)
+        with torch.cuda.stream(side):
+            step()
+        stream.wait_stream(side)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            step()
+        torch.cuda.synchronize()
+        run = graph.replay
     if args.profile_run:
         for _ in range(args.steps):
-            step()
+            run()
         src = torch.empty(CALIB_BYTES // 4, dtype=torch.int32, device=dev).fill_(1)
         dst = torch.empty_like(src)
         torch.cuda.synchronize()
@@ -290,11 +315,16 @@ def main():
     t_all0.record(stream)
     for e0, e1 in evs:
         e0.record(stream)
-        step()
+        run()
         e1.record(stream)
     t_all1.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
+    # the timed steps must reproduce the warm-up's output bit for bit (the kernels are deterministic)
+    if not (torch.equal(out.view(torch.int16), first_out[0].view(torch.int16))
+            and torch.equal(lse.view(torch.int32), first_out[1].view(torch.int32))):
+        print("bench.py: the timed steps did not reproduce the warm-up step's output", file=sys.stderr)
+        sys.exit(1)
     total_ms = t_all0.elapsed_time(t_all1)
     kern_ms = np.array([e0.elapsed_time(e1) for e0, e1 in evs])
     ms_per_step = total_ms / args.steps
@@ -307,7 +337,7 @@ def main():
         flush.fill_(1)
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record(stream)
-        step()
+        run()
         e1.record(stream)
         torch.cuda.synchronize()
         cold.append(e0.elapsed_time(e1))
@@ -376,6 +406,8 @@ def main():
         ins["slots"] = slots
     if T > 1:
         res["config"]["tokens_per_seq"] = T
+    res["config"]["launch"] = "HIP graph of the step's kernels, one replay per step" if args.graph else \
+        "one call per entry point per step"
     res["cpu_baseline"] = None if args.no_cpu_baseline else cpu_baseline(inp, nbytes, qin=qin, ins=ins)
     print(json.dumps(res), flush=True)
 
