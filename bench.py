@@ -175,6 +175,16 @@ def cpu_threads() -> int:
                     if i.get("internal_api") in ("openblas", "mkl", "blis")] or [1]))
 
 
+def cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(inp, nbytes: int, budget_s: float = 12.0, qin=None, ins=None):
     """The float64 oracle (as it stands) on whole sequences of the workload
     until the time budget is spent, scaled to the metric's unit."""
@@ -198,6 +208,7 @@ def cpu_baseline(inp, nbytes: int, budget_s: float = 12.0, qin=None, ins=None):
         "unit": "GB/s",
         "cores": cpu_threads(),
         "kind": "oracle",
+        "cpu_model": cpu_model(),
         "sample": f"{done} of {inp['batch']} sequences{' plus the whole query front end' if qin else ''}"
                   f"{' plus the whole insert' if ins else ''}, "
                   f"{dt:.1f} s; host has {os.cpu_count()} logical CPUs",
@@ -341,7 +352,19 @@ def main():
         e1.record(stream)
         torch.cuda.synchronize()
         cold.append(e0.elapsed_time(e1))
-    del flush
+    # context: a plain device copy of 1 GiB (read 1 GiB, write 1 GiB), the
+    # bandwidth a streaming kernel reaches on this GPU
+    src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    c0.record(stream)
+    for _ in range(5):
+        dst.copy_(src)
+    c1.record(stream)
+    torch.cuda.synchronize()
+    copy_gbs = 5 * 2 * (1 << 30) / (c0.elapsed_time(c1) / 1e3) / 1e9
+    del flush, src, dst
 
     nbytes = decode_bytes(inp) + (query_bytes(qin) if qin else 0) + (insert_bytes(B) if ins else 0)
     flops = decode_flops(inp) + (query_flops(qin) if qin else 0) + (insert_flops(B) if ins else 0)
@@ -349,12 +372,12 @@ def main():
     achieved = nbytes / kern_avg_s / 1e9
     tflops = flops / kern_avg_s / 1e12
     value = nbytes / (ms_per_step / 1e3) / 1e9
-    kernels = {"topk_sparse": "mla_topk_rows_kernel + mla_decode_kernel<2,false,2> + mla_merge_kernel",
-               "fp8_cache": "mla_decode_kernel<2,false,1> + mla_merge_kernel",
-               "query_decode": "mla_qb_kernel + mla_ql_kernel + mla_decode_kernel<4,true,0> + mla_merge_kernel",
-               "insert_decode": "mla_kv_insert_kernel + mla_decode_kernel<2,false,4> + mla_merge_kernel",
+    kernels = {"topk_sparse": "mla_topk_rows_kernel + mla_decode_kernel<2,false,2,false> + mla_merge_kernel",
+               "fp8_cache": "mla_decode_kernel<2,false,1,false> + mla_merge_kernel",
+               "query_decode": "mla_qb_kernel + mla_ql_kernel + mla_decode_kernel<4,true,0,false> + mla_merge_kernel",
+               "insert_decode": "mla_kv_insert_kernel + mla_decode_kernel<2,false,4,false> + mla_merge_kernel",
                "mtp_bf16": "mla_decode_kernel<2,false,0,true> + mla_merge_kernel"}
-    kernel = kernels.get(name, "mla_decode_kernel<2,false,0> + mla_merge_kernel")
+    kernel = kernels.get(name, "mla_decode_kernel<2,false,0,false> + mla_merge_kernel")
     # above the ridge (2.5 PFLOP/s over 8 TB/s = 312.5 flop/B) the step is bound by the bf16 MFMA rate:
     # top-k (345 flop/B) and the per-tensor FP8 cache at 128 heads (432 flop/B)
     mfma_bound = flops / nbytes > MFMA_BF16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9)
@@ -369,6 +392,7 @@ def main():
         "kernel_us_avg": round(kern_avg_s * 1e6, 2),
         "hbm_gbs": round(achieved, 1),
         "mfma_tflops": round(tflops, 1),
+        "copy_ceiling_gbs": round(copy_gbs, 1),
     }
     seq = inp["seqlens"]
     res = {
