@@ -26,7 +26,7 @@ every input resident in HBM before timing:
       every KV row once.
 
 The decode call runs the work split, block-table translation (or the top-k
-prepass), KV streaming, QK^T, softmax, PV, epilogue and the split-KV merge on
+translation), KV streaming, QK^T, softmax, PV, epilogue and the split-KV merge on
 the GPU.  Each step calls the entry points from Python; with --graph the
 step's calls are recorded once into a HIP graph and every timed step replays
 it (measured slower on this ROCm: the replay adds more per-kernel time than the
@@ -372,7 +372,7 @@ def main():
     achieved = nbytes / kern_avg_s / 1e9
     tflops = flops / kern_avg_s / 1e12
     value = nbytes / (ms_per_step / 1e3) / 1e9
-    kernels = {"topk_sparse": "mla_topk_rows_kernel + mla_decode_kernel<2,false,2,false> + mla_merge_kernel",
+    kernels = {"topk_sparse": "mla_decode_kernel<2,false,2,false> + mla_merge_kernel",
                "fp8_cache": "mla_decode_kernel<2,false,1,false> + mla_merge_kernel",
                "query_decode": "mla_qb_kernel + mla_ql_kernel + mla_decode_kernel<4,true,0,false> + mla_merge_kernel",
                "insert_decode": "mla_kv_insert_kernel + mla_decode_kernel<2,false,4,false> + mla_merge_kernel",

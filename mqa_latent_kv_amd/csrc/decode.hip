@@ -58,7 +58,7 @@
 //    rows' limits differ only in the last T - 1 positions, so the masked
 //    softmax runs only from the first slot that hides a position from some
 //    row.  Top-k lists are per query token: each token is its own sequence
-//    of H rows, and the row prepass cuts its list at the token's limit.
+//    of H rows, and the fill pipeline cuts its list at the token's limit.
 //  * Softmax in base 2 against a fixed reference per head: the first slot's
 //    max.  Later slots may exceed it by up to 16 (P <= 2^16, exact in fp32 and
 //    as relative bf16); if any head's scores rise further, the workgroup
@@ -111,9 +111,7 @@ struct DecodeArgs {
   float* ws_o;    // [(ranges + B) slots][H][512] normalised partial O, fp32
   float* ws_lse;  // [(ranges + B)][H] base-2 LSE of partials
   int2* ws_seq;   // [B] {workspace slot of piece 0, pieces}; pieces 0: nothing to attend
-  const int32_t* ws_rows;    // top-k: [B][topk] physical row per entry, -1 for a masked entry
-  const uint32_t* ws_masks;  // top-k: [B][mask_words] validity bits per 32-entry slot
-  int32_t mask_words;        // ceil(topk / 32)
+  int32_t topk_tq;           // top-k: lists per sequence (T); list b belongs to sequence b / T
   int32_t batch, heads, num_pages, max_pages, topk;
   int32_t tq;         // dense, several query tokens: T (rows of a sequence = T x heads_tok), else 1
   int32_t heads_tok;  // query heads per token
@@ -948,8 +946,7 @@ __device__ __forceinline__ void pv_slot(const lds_char* buf, const VBlock& va0, 
 
 struct SegCtx {
   const int32_t* bt_seg;     // block-table entries of the segment's pages
-  const int32_t* rows_seg;   // top-k: physical row of each entry (-1: masked) from tok0 on
-  const uint32_t* mask_seg;  // top-k: validity word of each 32-entry slot from tok0 on
+  const int32_t* idx_seg;    // top-k: the list's entries from tok0 on
   int tok0, tok1, nslots, npages;
 };
 
@@ -1054,8 +1051,7 @@ mla_decode_kernel(DecodeArgs a) {
       sg.nslots = (sg.tok1 - sg.tok0 + kTS - 1) / kTS;
       sg.npages = (sg.nslots + 1) / 2;
       sg.bt_seg = a.block_table + (size_t)b * a.max_pages + (gs - p);
-      sg.rows_seg = a.ws_rows + (size_t)b * a.topk + sg.tok0;
-      sg.mask_seg = a.ws_masks + (size_t)b * a.mask_words + sg.tok0 / kTS;
+      sg.idx_seg = a.topk_idx + (size_t)b * a.topk + sg.tok0;
       const int first_r = p / pl.C, last_r = (p + n - 1) / pl.C;
       const int nsplit = last_r - first_r + 1;
       const int nslots = sg.nslots;
@@ -1099,29 +1095,50 @@ mla_decode_kernel(DecodeArgs a) {
       const int frow = 8 * w + (lane & 7), fq = lane >> 3;
       // physical row that this lane fills for slot t of the segment (slots
       // past the end repeat the last one; rows past the valid count repeat
-      // the last valid row; masked top-k entries read row 0)
+      // the last valid row)
       auto fill_src = [&](int t) -> int {
         t = min(t, nslots - 1);
-        if constexpr (kv_topk(KVM)) {
-          const int e = t * kTS + frow;
-          const int rw = sg.tok0 + e < sg.tok1 ? sg.rows_seg[e] : -1;
-          return rw < 0 ? 0 : rw;
-        } else {
-          const int page = page_of(pc, sg.bt_seg, t >> 1, sg.npages, lane, a.num_pages);
-          const int nv = min(kTS, sg.tok1 - (sg.tok0 + t * kTS));
-          return page * kPage + (t & 1) * kTS + min(frow, nv - 1);
-        }
+        const int page = page_of(pc, sg.bt_seg, t >> 1, sg.npages, lane, a.num_pages);
+        const int nv = min(kTS, sg.tok1 - (sg.tok0 + t * kTS));
+        return page * kPage + (t & 1) * kTS + min(frow, nv - 1);
+      };
+      // top-k, in two stages one pipeline step apart: the listed position of
+      // this lane's row of slot t (-1 past the segment's end), then its pool
+      // row block_table[b / T][j / 64]*64 + j % 64.  A position is valid iff
+      // 0 <= j < the list's causal limit (seqlen when T = 1); a masked entry
+      // reads row 0, and its p is 0.  Both loads are unconditional, from
+      // clamped addresses.
+      int tk_limit = 0;
+      const int32_t* tk_bt = a.block_table;
+      if constexpr (kv_topk(KVM)) {
+        const int bs = b / a.topk_tq;
+        tk_limit = min(max(a.seqlens[bs], 0), a.max_pages * kPage) - (a.topk_tq - 1 - b % a.topk_tq);
+        tk_bt = a.block_table + (size_t)bs * a.max_pages;
+      }
+      auto topk_pos = [&](int t) -> int {
+        const int e = min(t, nslots - 1) * kTS + frow;
+        const int ne = sg.tok1 - sg.tok0;
+        const int j = sg.idx_seg[min(e, ne - 1)];
+        return e < ne ? j : -1;
+      };
+      auto topk_ok = [&](int j) -> bool { return j >= 0 && j < tk_limit; };
+      auto topk_row = [&](int j) -> int {
+        const int jc = topk_ok(j) ? j : 0;
+        const int row = clamp_page(tk_bt[jc >> 6], a.num_pages) * kPage + (jc & (kPage - 1));
+        return topk_ok(j) ? row : 0;
+      };
+      // top-k validity words, one per ring position (the fill of a slot sets
+      // byte w from wave w's eight rows), after the scale tables
+      LDS_AS uint32_t* const tk_masks = (LDS_AS uint32_t*)(ring + kFillRing * kSlotBytes + 2048);
+      auto put_mask = [&](int pos, bool ok) {
+        const uint32_t bits = (uint32_t)__ballot(ok) & 0xFFu;  // lanes 0..7: rows 8w .. 8w+7
+        if (lane == 0) ((LDS_AS uint8_t*)(tk_masks + pos))[w] = (uint8_t)bits;
       };
       // validity of the tokens of slot s (dense: only the last slot is
-      // short; top-k: the prepass's words, cached 64 slots at a time, one
-      // per lane, like the page numbers)
-      PageCache mc;
-      const int mwords = nslots;
-      if constexpr (kv_topk(KVM)) page_cache_load(mc, (const int32_t*)sg.mask_seg, 0, mwords, lane);
+      // short; top-k: the word its fill wrote, at position s % 3)
       auto slot_mask = [&](int s) -> uint32_t {
         if constexpr (kv_topk(KVM)) {
-          if (s >= mc.base + 64) page_cache_load(mc, (const int32_t*)sg.mask_seg, s, mwords, lane);
-          return (uint32_t)__builtin_amdgcn_readlane(mc.v, s - mc.base);
+          return tk_masks[s % kFillRing];
         } else {
           return low_mask(sg.tok1 - (sg.tok0 + s * kTS));
         }
@@ -1207,7 +1224,24 @@ mla_decode_kernel(DecodeArgs a) {
           // before the first is needed: one memory latency, not three)
           RawRow<KVM> rr;
           int next_row;
-          {
+          bool rr_ok = true, next_ok = true;  // top-k: validity of the rows of rr / next_row
+          int next_j = 0;                     // top-k: listed position of slot s+5
+          if constexpr (kv_topk(KVM)) {
+            const int j0 = topk_pos(0), j1 = topk_pos(1), j2 = topk_pos(2), j3 = topk_pos(3);
+            next_j = topk_pos(4);
+            const int i0 = topk_row(j0), i1 = topk_row(j1), i2 = topk_row(j2);
+            next_row = topk_row(j3);
+            next_ok = topk_ok(j3);
+            RawRow<KVM> r0, r1;
+            load_row<KVM>(r0, a, i0, fq);
+            load_row<KVM>(r1, a, i1, fq);
+            load_row<KVM>(rr, a, i2, fq);
+            rr_ok = topk_ok(j2);
+            fill_row<KVM>(pos_buf(0), pos_tab(0), r0, frow, fq);
+            put_mask(0, topk_ok(j0));
+            fill_row<KVM>(pos_buf(1), pos_tab(1), r1, frow, fq);
+            put_mask(1, topk_ok(j1));
+          } else {
             const int i0 = fill_src(0), i1 = fill_src(1), i2 = fill_src(2);
             next_row = fill_src(3);
             RawRow<KVM> r0, r1;
@@ -1253,7 +1287,15 @@ mla_decode_kernel(DecodeArgs a) {
             pv_slot<NSPLIT, TILED>(side.pvbuf, va0, po, tab, acc);
             fill_row<KVM>(pos_buf(p2), pos_tab(p2), rr, frow, fq);
             const int row = next_row;
-            next_row = fill_src(s + 4);
+            if constexpr (kv_topk(KVM)) {
+              put_mask(p2, rr_ok);
+              rr_ok = next_ok;
+              next_ok = topk_ok(next_j);
+              next_row = topk_row(next_j);  // slot s+4
+              next_j = topk_pos(s + 5);
+            } else {
+              next_row = fill_src(s + 4);
+            }
             load_row<KVM>(rr, a, row, fq);
             wait_vm_lgkm0<63>();  // this wave's LDS reads and writes are done
             barrier();
@@ -1292,7 +1334,6 @@ mla_decode_kernel(DecodeArgs a) {
         if (!__builtin_amdgcn_readfirstlane(vote)) break;
         st.m_ref = st.m_seen;
         if (!kv_topk(KVM) && sg.npages > 64) page_cache_load(pc, sg.bt_seg, 0, sg.npages, lane);
-        if (kv_topk(KVM) && nslots > 64) page_cache_load(mc, (const int32_t*)sg.mask_seg, 0, mwords, lane);
       }
 
       // ---- epilogue: normalise and store this wave's columns (final output,
@@ -1424,44 +1465,6 @@ __global__ void __launch_bounds__(kThreads) mla_merge_kernel(MergeArgs m) {
   if (sub == 0) m.lse[(size_t)b * m.heads + head] = wsum > 0.0f ? (mx + __builtin_amdgcn_logf(wsum)) * kLn2 : -INFINITY;
 }
 
-// ---------------------------------------------------------------- top-k rows
-
-struct TopkArgs {
-  const int32_t* topk_idx;  // [B*T][topk] logical positions, one list per query token
-  const int32_t* block_table;
-  const int32_t* seqlens;
-  int32_t* rows;     // [B*T][topk] physical row, -1 for a masked entry
-  uint32_t* masks;   // [B*T][mask_words] validity bits per 32-entry slot
-  int32_t topk, mask_words, max_pages, num_pages;
-  int32_t tq;        // query tokens per sequence (T)
-};
-
-// Translate every top-k entry of list blockIdx.y = b*T + t (query token t of
-// sequence b): logical position j is valid iff 0 <= j < seqlen - T + 1 + t
-// (its causal limit; seqlen when T = 1), and lives in row
-// block_table[b][j / 64]*64 + j % 64 (integer arithmetic, exact).  One thread
-// per entry.
-__global__ void __launch_bounds__(kThreads) mla_topk_rows_kernel(TopkArgs t) {
-  const int bt = blockIdx.y;
-  const int b = bt / t.tq;
-  const int k = blockIdx.x * kThreads + threadIdx.x;
-  bool valid = false;
-  if (k < t.topk) {
-    const int j = t.topk_idx[(size_t)bt * t.topk + k];
-    const int seqlen = min(max(t.seqlens[b], 0), t.max_pages * kPage) - (t.tq - 1 - bt % t.tq);
-    int row = -1;
-    if (j >= 0 && j < seqlen) {
-      valid = true;
-      row = clamp_page(t.block_table[(size_t)b * t.max_pages + (j >> 6)], t.num_pages) * kPage + (j & (kPage - 1));
-    }
-    t.rows[(size_t)bt * t.topk + k] = row;
-  }
-  const uint64_t bits = __ballot(valid);
-  const int word = k / kTS;
-  if ((threadIdx.x & (kTS - 1)) == 0 && word < t.mask_words)
-    t.masks[(size_t)bt * t.mask_words + word] = (uint32_t)(bits >> (threadIdx.x & 32));
-}
-
 int nsplit_for_heads(int heads) { return heads > 32 ? 2 : 4; }
 int heads_per_slab(int heads) { return 32 * (kWaves / nsplit_for_heads(heads)); }
 int slabs_for_heads(int heads) { return (heads + heads_per_slab(heads) - 1) / heads_per_slab(heads); }
@@ -1491,16 +1494,13 @@ int32_t decode_ranges(int32_t cus, int32_t batch, int32_t max_pages, int32_t top
   return (int32_t)r;
 }
 
-int32_t mask_words_for(int32_t topk) { return (topk + kTS - 1) / kTS; }
 
-// Workspace: [B] int2 piece records | [(ranges + B)][H] fp32 LSE | [(ranges + B)][H][512] fp32 O
-// | top-k only: [B][topk] int32 rows | [B][ceil(topk / 32)] uint32 masks.
+// Workspace: [B] int2 piece records | [(ranges + B)][H] fp32 LSE | [(ranges + B)][H][512] fp32 O.
 size_t decode_workspace_bytes(int32_t ranges, int32_t batch, int32_t heads, int32_t topk) {
   const size_t slots = (size_t)ranges + (size_t)batch;
   size_t n = align256(sizeof(int2) * (size_t)batch) + align256(sizeof(float) * slots * heads) +
              align256(sizeof(float) * slots * heads * kDV);
-  if (topk > 0)
-    n += align256(sizeof(int32_t) * (size_t)batch * topk) + align256(sizeof(uint32_t) * (size_t)batch * mask_words_for(topk));
+  (void)topk;
   return n;
 }
 
@@ -1537,12 +1537,7 @@ hipError_t launch_decode(const DecodeLaunch& din, hipStream_t stream) {
   ws += align256(sizeof(float) * slots * d.heads);
   a.ws_o = (float*)ws;
   ws += align256(sizeof(float) * slots * d.heads * kDV);
-  a.mask_words = mask_words_for(d.topk);
-  int32_t* ws_rows = (int32_t*)ws;
-  ws += d.topk > 0 ? align256(sizeof(int32_t) * (size_t)d.batch * d.topk) : 0;
-  uint32_t* ws_masks = (uint32_t*)ws;
-  a.ws_rows = ws_rows;
-  a.ws_masks = ws_masks;
+  a.topk_tq = din.topk > 0 ? din.tq : 1;
   a.batch = d.batch;
   a.heads = d.heads;
   a.num_pages = d.num_pages;
@@ -1555,23 +1550,6 @@ hipError_t launch_decode(const DecodeLaunch& din, hipStream_t stream) {
   a.scale_log2 = d.softmax_scale * kLog2e;
   a.q_descale = d.q_descale;
 
-  if (d.topk > 0) {
-    TopkArgs t;
-    t.topk_idx = d.topk_idx;
-    t.block_table = d.block_table;
-    t.seqlens = d.seqlens;
-    t.rows = ws_rows;
-    t.masks = ws_masks;
-    t.topk = d.topk;
-    t.mask_words = a.mask_words;
-    t.max_pages = d.max_pages;
-    t.num_pages = d.num_pages;
-    t.tq = din.tq;
-    hipLaunchKernelGGL(mla_topk_rows_kernel, dim3((d.topk + kThreads - 1) / kThreads, d.batch), dim3(kThreads), 0,
-                       stream, t);
-    const hipError_t e0 = hipGetLastError();
-    if (e0 != hipSuccess) return e0;
-  }
   const int kvm = d.kv_format == kKvFormatFp8Tile     ? (d.topk > 0 ? kKvFp8TopK : kKvFp8)
                   : d.kv_format == kKvFormatFp8Tensor ? (d.topk > 0 ? kKvFp8TTopK : kKvFp8T)
                                                       : (d.topk > 0 ? kKvBf16TopK : kKvBf16);
