@@ -95,6 +95,9 @@ CASES = {
     "one_long_seq": dict(seed=19, batch=1, heads=128, seqlens=[20000]),
     "with_empty_seqs": dict(seed=20, batch=5, heads=64, seqlens=[0, 77, 0, 300, 0], pages_per_seq=5),
     "exact_pages": dict(seed=21, batch=3, heads=128, seqlens=[64, 128, 4096]),
+    # 128 heads: ranges of many short sequences, empty sequences
+    "h128_many_short": dict(seed=23, batch=300, heads=128, seqlen_range=(1, 100)),
+    "h128_with_empty_seqs": dict(seed=24, batch=5, heads=128, seqlens=[0, 33, 0, 1000, 0], pages_per_seq=16),
     # FP8 cache: e4m3 codes with one fp32 scale per row and 128-column tile
     "fp8_h128_ragged": dict(seed=71, batch=3, heads=128, seqlens=[1, 300, 2100], kv_format="fp8"),
     "fp8_h64_ragged": dict(seed=72, batch=5, heads=64, seqlen_range=(1, 1500), kv_format="fp8"),
