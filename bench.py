@@ -73,6 +73,8 @@ WORKLOADS = {
                      "4096-page pool",
     "mtp_bf16": "paged bf16 MLA decode of 2 new query tokens per sequence (causal): batch 64, 128 heads, "
                 "seq_len 4096 each, 4096-page pool",
+    "query_narrow_decode": "MLA query front end in its narrow-batch form (4 tokens, 128 heads: RMSNorm, Q_B "
+                           "24576x1536, W_UK, FP8) then decode of the FP8 queries over bf16 pages, 8192 tokens each",
 }
 
 
@@ -281,7 +283,9 @@ def main():
     torch.cuda.set_device(dev)
     name = args.workload
     inp = synth.workload_inputs(name)
-    qin = synth.make_query_inputs(5, batch=64, heads=8) if name == "query_decode" else None
+    qin = None
+    if name in ("query_decode", "query_narrow_decode"):
+        qin = synth.make_query_inputs(5 if name == "query_decode" else 8, batch=inp["batch"], heads=inp["heads"])
     d = mla.to_device(inp, dev)
     B, H = inp["batch"], inp["heads"]
     ins = None
@@ -422,6 +426,8 @@ def main():
     kernels = {"topk_sparse": "mla_decode_kernel<2,false,2,false> + mla_merge_kernel",
                "fp8_cache": "mla_decode_kernel<2,false,1,false> + mla_merge_kernel",
                "query_decode": "mla_qb_kernel + mla_ql_kernel + mla_decode_kernel<4,true,0,false> + mla_merge_kernel",
+               "query_narrow_decode": "mla_qb_gemv_kernel + mla_ql_gemv_kernel + mla_decode_kernel<2,true,0,false> + "
+                                      "mla_merge_kernel",
                "insert_decode": "mla_kv_insert_kernel + mla_decode_kernel<2,false,4,false> + mla_merge_kernel",
                "mtp_bf16": "mla_decode_kernel<2,false,0,true> + mla_merge_kernel"}
     kernel = kernels.get(name, "mla_decode_kernel<2,false,0,false> + mla_merge_kernel")

@@ -22,6 +22,10 @@
 //    reduction runs over p), the A operand is the bf16 nope q from the
 //    workspace.
 //
+// Up to eight tokens take the page's narrow-batch form instead: the two
+// products are GEMVs bound by reading the weights, computed with wave FMAs
+// in many small workgroups (mla_qb_gemv_kernel, mla_ql_gemv_kernel).
+//
 // And the KV-cache insert of the same page (method `insert`), per new token t
 // with slot >= 0:
 //   rr   = 1 / sqrt(sum_k x[k]^2 / 512 + eps)      x = qkv[t, 1536:2048]
@@ -357,6 +361,136 @@ __global__ void __launch_bounds__(kThreads) mla_ql_kernel(QueryArgs a) {
   }
 }
 
+
+// ---------------------------------------------------------------- narrow batch: wave FMAs
+
+// Up to kNarrow tokens, the MlaQuery page's narrow-batch form: the products
+// are GEMVs whose cost is reading the weights once, so the weights are
+// spread over many workgroups and reduced with wave FMAs; no MFMA tile would
+// be more than a quarter full.
+constexpr int kNarrow = 8;                                  // batches up to this size take this path
+constexpr int kQbRowsPerWave = 2;
+constexpr int kQbRowsPerWg = kQbRowsPerWave * (kThreads / 64);  // 8 W_qb rows per workgroup
+
+// RMSNorm + Q_B: a workgroup owns 8 rows of W_qb (2 per wave) for every
+// token.  Lane l holds columns 512k + 8l .. +7 (k = 0..2) of a W_qb row, of
+// w_qa and of a token's q_a row; each wave normalises tokens w, w + 4 into
+// LDS, then every wave forms its rows' dot products with every token: 24
+// FMAs per lane in fp32, then the wave sum.
+__global__ void __launch_bounds__(kThreads) mla_qb_gemv_kernel(QueryArgs a) {
+  __shared__ __attribute__((aligned(16))) bf16x8 xn[kNarrow][kQA / 8];  // normalised tokens, 24 KB
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int nrows = a.heads * kQB;
+  const int n0 = blockIdx.x * kQbRowsPerWg + kQbRowsPerWave * w;
+  // every load first: this wave's W_qb rows (clamped, unconditional), w_qa
+  // and the q_a rows of the tokens it normalises
+  bf16x8 wr[kQbRowsPerWave][3];
+#pragma unroll
+  for (int j = 0; j < kQbRowsPerWave; ++j) {
+    const int row = min(n0 + j, nrows - 1);
+#pragma unroll
+    for (int k = 0; k < 3; ++k) wr[j][k] = *(const bf16x8*)(a.w_qb + (size_t)row * kQA + 512 * k + 8 * lane);
+  }
+  bf16x8 wq[3], xr[2][3];
+#pragma unroll
+  for (int k = 0; k < 3; ++k) wq[k] = *(const bf16x8*)(a.w_qa + 512 * k + 8 * lane);
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int t = min(w + 4 * i, a.batch - 1);
+#pragma unroll
+    for (int k = 0; k < 3; ++k) xr[i][k] = *(const bf16x8*)(a.qkv + (size_t)t * a.qkv_stride + 512 * k + 8 * lane);
+  }
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int t = w + 4 * i;
+    if (t >= a.batch) break;  // wave-uniform
+    float x[24];
+#pragma unroll
+    for (int k = 0; k < 3; ++k)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) x[8 * k + e] = (float)xr[i][k][e];
+    float ss = 0.0f;
+#pragma unroll
+    for (int e = 0; e < 24; ++e) ss += x[e] * x[e];
+    ss = wave_sum(ss);
+    const float rr = 1.0f / __builtin_sqrtf(ss / (float)kQA + a.eps);
+#pragma unroll
+    for (int k = 0; k < 3; ++k) {
+      bf16x8 o;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) o[e] = (__bf16)((x[8 * k + e] * rr) * (float)wq[k][e]);
+      xn[t][64 * k + lane] = o;
+    }
+  }
+  __syncthreads();
+  const float qsi = a.q_scale_inv[0];
+#pragma unroll
+  for (int j = 0; j < kQbRowsPerWave; ++j) {
+    const int row = n0 + j;
+    if (row >= nrows) break;  // wave-uniform
+    const int head = row / kQB, r = row % kQB;
+    for (int t = 0; t < a.batch; ++t) {
+      float d = 0.0f;
+#pragma unroll
+      for (int k = 0; k < 3; ++k) {
+        const bf16x8 xv = xn[t][64 * k + lane];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) d = __builtin_fmaf((float)xv[e], (float)wr[j][k][e], d);
+      }
+      d = wave_sum(d);
+      if (lane == 0) {
+        const __bf16 v = (__bf16)d;
+        if (r < kNope) a.qn[((size_t)t * a.heads + head) * kNope + r] = v;
+        else a.out[((size_t)t * a.heads + head) * kOut + kDV + (r - kNope)] = e4m3_of_product((float)v, qsi);
+      }
+    }
+  }
+}
+
+// W_UK absorption + FP8: a workgroup owns one head and 64 output columns for
+// every token.  Thread t takes columns c0 + 8(t%8) .. +7 of the W_uk rows p =
+// t/8 + 32j (j = 0..3): each row's 128 bytes come from eight neighbouring
+// threads.  The 32 partial sums of a column are added in LDS in a fixed
+// order, then rounded to bf16 and encoded.
+constexpr int kQlCols = 64;
+__global__ void __launch_bounds__(kThreads) mla_ql_gemv_kernel(QueryArgs a) {
+  __shared__ __attribute__((aligned(16))) __bf16 qs[kNarrow][kNope];                 // the tokens' nope q, 2 KB
+  __shared__ __attribute__((aligned(16))) f32x4 red[32][kNarrow][kQlCols / 4];       // partial sums, 64 KB
+  const int tid = threadIdx.x;
+  const int head = blockIdx.x, c0 = blockIdx.y * kQlCols;
+  const int cg = tid & 7, g = tid >> 3;
+  u32x4 wv[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+    wv[j] = *(const u32x4*)(a.w_uk + ((size_t)head * kNope + g + 32 * j) * kDV + c0 + 8 * cg);
+  {
+    // nope q of every token: thread t loads 4 values of token t/32
+    const int t = tid >> 5, p4 = 4 * (tid & 31);
+    if (t < a.batch) *(LDS_AS bf16x4*)&qs[t][p4] = *(const bf16x4*)(a.qn + ((size_t)t * a.heads + head) * kNope + p4);
+  }
+  __syncthreads();
+  for (int t = 0; t < a.batch; ++t) {
+    float acc[8] = {};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const float qv = (float)qs[t][g + 32 * j];
+      const bf16x8 wb = __builtin_bit_cast(bf16x8, wv[j]);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[e] = __builtin_fmaf(qv, (float)wb[e], acc[e]);
+    }
+    red[g][t][2 * cg] = f32x4{acc[0], acc[1], acc[2], acc[3]};
+    red[g][t][2 * cg + 1] = f32x4{acc[4], acc[5], acc[6], acc[7]};
+  }
+  __syncthreads();
+  const float qsi = a.q_scale_inv[0];
+  for (int o = tid; o < a.batch * kQlCols; o += kThreads) {
+    const int t = o / kQlCols, c = o % kQlCols;
+    float s = 0.0f;
+    for (int gg = 0; gg < 32; ++gg) s += red[gg][t][c >> 2][c & 3];
+    const float v = (float)(__bf16)s;
+    a.out[((size_t)t * a.heads + head) * kOut + c0 + c] = e4m3_of_product(v, qsi);
+  }
+}
 }  // namespace
 
 hipError_t launch_kv_insert(const InsertLaunch& k, hipStream_t stream) {
@@ -390,6 +524,14 @@ hipError_t launch_query(const QueryLaunch& q, hipStream_t stream) {
   a.heads = q.heads;
   a.qkv_stride = q.qkv_stride;
   a.eps = q.eps;
+  if (q.batch <= kNarrow) {
+    hipLaunchKernelGGL(mla_qb_gemv_kernel, dim3((q.heads * kQB + kQbRowsPerWg - 1) / kQbRowsPerWg), dim3(kThreads), 0,
+                       stream, a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(mla_ql_gemv_kernel, dim3(q.heads, kDV / kQlCols), dim3(kThreads), 0, stream, a);
+    return hipGetLastError();
+  }
   const int mt = (q.batch + kTok - 1) / kTok;
   hipLaunchKernelGGL(mla_qb_kernel, dim3((q.heads * kQB + 31) / 32, mt), dim3(kThreads), 0, stream, a);
   hipError_t e = hipGetLastError();

@@ -222,6 +222,8 @@ WORKLOADS = {
     "insert_decode": dict(seed=6, batch=64, heads=128, seqlens=[4096] * 64, num_pages=4096, pages_per_seq=64, kv_format="fp8_tensor"),
     "mtp_bf16": dict(seed=7, batch=64, heads=128, seqlens=[4096] * 64, num_pages=4096, pages_per_seq=64, tokens_per_seq=2),
     "query_decode": dict(seed=5, batch=64, heads=8, seqlens=[8192] * 64, num_pages=8192, pages_per_seq=128, q_format="fp8", q_descale=8.0),
+    # the narrow-batch form of the query front end: 4 tokens, all 128 heads
+    "query_narrow_decode": dict(seed=8, batch=4, heads=128, seqlens=[8192] * 4, num_pages=512, pages_per_seq=128, q_format="fp8", q_descale=8.0),
 }
 
 

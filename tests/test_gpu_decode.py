@@ -331,7 +331,7 @@ def test_page_permutation_invariance_bitwise():
     assert torch.equal(lse1.view(torch.int32), lse2.view(torch.int32))
 
 
-@pytest.mark.parametrize("name", ["paged_bf16_4096", "paged_bf16", "query_decode", "fp8_cache", "topk_sparse",
+@pytest.mark.parametrize("name", ["paged_bf16_4096", "paged_bf16", "query_decode", "query_narrow_decode", "fp8_cache", "topk_sparse",
                                   "insert_decode", "mtp_bf16"])
 def test_full_size_workloads_sampled(name):
     """The full-size decode workloads, in the launch configuration the

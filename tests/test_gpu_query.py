@@ -54,6 +54,12 @@ CASES = {
     "wide_rows_2112": dict(seed=54, batch=40, heads=4, width=2112),
     "eps_large": dict(seed=55, batch=20, heads=2, eps=0.5),
     "qsi_not_pow2": dict(seed=56, batch=24, heads=4, q_scale_inv=0.3),
+    # the narrow-batch (wave FMA) form: up to 8 tokens
+    "narrow_b1_h8": dict(seed=61, batch=1, heads=8),
+    "narrow_b4_h128": dict(seed=62, batch=4, heads=128),
+    "narrow_b8_h16_qsi": dict(seed=63, batch=8, heads=16, q_scale_inv=0.3),
+    "narrow_b3_h3_wide_rows": dict(seed=64, batch=3, heads=3, width=2112),
+    "mfma_b9_h8": dict(seed=65, batch=9, heads=8),
 }
 
 
