@@ -9,18 +9,19 @@
 //   out = e4m3(ql * qsi) | e4m3(qb[:, 128:] * qsi)  qsi = q_scale_inv[0]
 // with e4m3 rounded to nearest even and saturated to +-448.
 //
-// Two kernels, both on v_mfma_f32_32x32x16_bf16 with 32 tokens as M:
-//  * mla_qb_kernel: a workgroup owns 32 tokens and 32 rows of W_qb.  It
-//    normalises its tokens into LDS (bf16, the A operand), then its four
-//    waves each take a quarter of the 1536-long reduction with the W_qb
-//    fragments loaded straight from HBM (all 24 of a wave in flight at
-//    once); the four partial tiles are summed in LDS in a fixed order.  Nope
-//    rows go to the workspace as bf16, rope rows straight to FP8.
+// Three kernels, the products on v_mfma_f32_32x32x16_bf16 with 32 tokens as M:
+//  * mla_norm_kernel: the RMSNorm of every token, once, into the workspace.
+//  * mla_qb_kernel: a workgroup owns 32 tokens, 32 rows of W_qb and (when
+//    the tiles alone would not fill the chip, e.g. 64 tokens x 8 heads) a
+//    quarter of the 1536-long reduction; its four waves each take a quarter
+//    of its columns with both operands loaded straight from memory, the four
+//    partial tiles are summed in LDS in a fixed order and stored as fp32.
 //  * mla_ql_kernel: a workgroup owns 32 tokens, one head and 128 output
 //    columns; the W_uk tile [128 p][128 c] is staged in LDS and read as the B
 //    operand with ds_read_b64_tr_b16 (W_uk is stored c-contiguous, the
-//    reduction runs over p), the A operand is the bf16 nope q from the
-//    workspace.
+//    reduction runs over p).  The A operand is the nope q: the Q_B partials
+//    added in split order and rounded to bf16.  The workgroups of column
+//    block 0 also encode the rope rows of Q_B to FP8.
 //
 // Up to eight tokens take the page's narrow-batch form instead: the two
 // products are GEMVs bound by reading the weights, computed with wave FMAs
@@ -55,7 +56,6 @@ constexpr int kDV = 512;        // absorbed latent width
 constexpr int kOut = 576;       // output row: 512 latent + 64 rope
 constexpr int kThreads = 256;
 constexpr int kTok = 32;        // tokens per workgroup (MFMA M)
-constexpr int kXnPitch = kQA * 2 + 16;  // LDS row pitch of the normalised tile (bank spread)
 
 struct QueryArgs {
   const __bf16* qkv;
@@ -64,7 +64,9 @@ struct QueryArgs {
   const __bf16* w_uk;
   const float* q_scale_inv;
   uint8_t* out;
-  __bf16* qn;  // workspace: [B][H][128] bf16 nope rows of Q_B
+  __bf16* qn;   // workspace, narrow batch: [B][H][128] bf16 nope rows of Q_B
+  __bf16* xn;   // workspace, tiled: [B][1536] normalised q_a rows
+  float* qbp;   // workspace, tiled: [ksplit][B][H*192] fp32 partial Q_B products
   int32_t batch, heads, qkv_stride;
   float eps;
 };
@@ -185,76 +187,74 @@ __global__ void __launch_bounds__(kThreads) mla_kv_insert_kernel(InsertArgs a) {
 
 // ---------------------------------------------------------------- RMSNorm + Q_B
 
-__global__ void __launch_bounds__(kThreads) mla_qb_kernel(QueryArgs a) {
-  __shared__ __attribute__((aligned(16))) char xn_mem[kTok * kXnPitch];  // normalised tokens, bf16
-  __shared__ __attribute__((aligned(16))) f32x4 red[4 * 4 * 64];          // partial tiles of waves 1..3
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  const int n0 = blockIdx.x * 32;     // first W_qb row (output column) of this workgroup
-  const int m0 = blockIdx.y * kTok;   // first token
+// RMSNorm of the q_a rows into the workspace (bf16): one wave per token,
+// lane l holding columns 512k + 8l .. +7 (k = 0..2).
+__global__ void __launch_bounds__(kThreads) mla_norm_kernel(QueryArgs a) {
+  const int lane = threadIdx.x & 63;
+  const int t = blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6);
+  if (t >= a.batch) return;  // wave-uniform
+  bf16x8 xr[3], wq[3];
+#pragma unroll
+  for (int k = 0; k < 3; ++k) {
+    xr[k] = *(const bf16x8*)(a.qkv + (size_t)t * a.qkv_stride + 512 * k + 8 * lane);
+    wq[k] = *(const bf16x8*)(a.w_qa + 512 * k + 8 * lane);
+  }
+  float x[24];
+#pragma unroll
+  for (int k = 0; k < 3; ++k)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) x[8 * k + e] = (float)xr[k][e];
+  float ss = 0.0f;
+#pragma unroll
+  for (int e = 0; e < 24; ++e) ss += x[e] * x[e];
+  ss = wave_sum(ss);
+  const float rr = 1.0f / __builtin_sqrtf(ss / (float)kQA + a.eps);
+#pragma unroll
+  for (int k = 0; k < 3; ++k) {
+    bf16x8 o;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) o[e] = (__bf16)((x[8 * k + e] * rr) * (float)wq[k][e]);
+    *(bf16x8*)(a.xn + (size_t)t * kQA + 512 * k + 8 * lane) = o;
+  }
+}
 
-  // Every load is issued before any is needed (one memory latency for the
-  // whole workgroup): this wave's W_qb fragments, w_qa and the q_a rows of
-  // the eight tokens it normalises.
-  // B fragments of this wave's 24 k-steps (reduction columns 384w ..): lane
-  // l holds W_qb row n0 + l%32, columns 16ks + 8*(l/32) .. +7
-  constexpr int KSW = kQA / 16 / 4;
+// Q_B: a workgroup owns 32 tokens, 32 rows of W_qb and 1/KSPLIT of the
+// 1536-long reduction (KSPLIT = 4 when the tiles alone would leave most
+// compute units idle, e.g. 64 tokens x 8 heads); its four waves take a
+// quarter of its columns each, with both operands loaded straight from
+// memory (all of a wave's fragments in flight at once).  The four partial
+// tiles are summed in LDS in a fixed order and stored as an fp32 partial.
+template <int KSPLIT>
+__global__ void __launch_bounds__(kThreads) mla_qb_kernel(QueryArgs a) {
+  __shared__ __attribute__((aligned(16))) f32x4 red[4 * 4 * 64];  // partial tiles of waves 1..3
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int n0 = blockIdx.x * 32;    // first W_qb row (output column) of this workgroup
+  const int m0 = blockIdx.y * kTok;  // first token
+  constexpr int KW = kQA / KSPLIT / 4;  // reduction columns per wave
+  constexpr int KSW = KW / 16;          // k-steps per wave
+  const int k0 = blockIdx.z * (kQA / KSPLIT) + KW * w;
+  const int nrows = a.heads * kQB;
+  // lane l: B = W_qb row n0 + l%32, A = token m0 + l%32, columns 16i + 8*(l/32)
+  // .. +7 of this wave's range (clamped rows, unconditional loads; values of
+  // rows past the end are zeroed)
   const int nrow = n0 + (lane & 31), h8 = 8 * (lane >> 5);
-  const bool row_ok = nrow < a.heads * kQB;
-  // (loads are unconditional, from a clamped valid address, and the value is
-  // dropped afterwards: a guarded load becomes a branch around it, and the
-  // branches serialise the loads)
-  const int nrow_c = row_ok ? nrow : a.heads * kQB - 1;
-  bf16x8 bf[KSW];
+  const bool row_ok = nrow < nrows;
+  const int nrow_c = row_ok ? nrow : nrows - 1;
+  const int b = m0 + (lane & 31);
+  const bool b_ok = b < a.batch;
+  const int b_c = b_ok ? b : a.batch - 1;
+  bf16x8 bf[KSW], af[KSW];
 #pragma unroll
   for (int i = 0; i < KSW; ++i) {
-    const int k = 16 * (KSW * w + i) + h8;
-    bf[i] = *(const bf16x8*)(a.w_qb + (size_t)nrow_c * kQA + k);
+    bf[i] = *(const bf16x8*)(a.w_qb + (size_t)nrow_c * kQA + k0 + 16 * i + h8);
+    af[i] = *(const bf16x8*)(a.xn + (size_t)b_c * kQA + k0 + 16 * i + h8);
   }
-#pragma unroll
-  for (int i = 0; i < KSW; ++i) bf[i] = row_ok ? bf[i] : bf16x8{};
-  // RMSNorm: wave w normalises tokens m0 + 8w .. +7; lane i holds columns
-  // 8i + 512k .. +7 (k = 0..2)
-  bf16x8 wq[3], xr[8][3];
-#pragma unroll
-  for (int k = 0; k < 3; ++k) wq[k] = *(const bf16x8*)(a.w_qa + 512 * k + 8 * lane);
-#pragma unroll
-  for (int t = 0; t < 8; ++t) {
-    const int b = min(m0 + 8 * w + t, a.batch - 1);
-#pragma unroll
-    for (int k = 0; k < 3; ++k) xr[t][k] = *(const bf16x8*)(a.qkv + (size_t)b * a.qkv_stride + 512 * k + 8 * lane);
-  }
-#pragma unroll
-  for (int t = 0; t < 8; ++t)
-#pragma unroll
-    for (int k = 0; k < 3; ++k) xr[t][k] = m0 + 8 * w + t < a.batch ? xr[t][k] : bf16x8{};
-#pragma unroll
-  for (int t = 0; t < 8; ++t) {
-    const int m = 8 * w + t;
-    float x[24];
-#pragma unroll
-    for (int k = 0; k < 3; ++k)
-#pragma unroll
-      for (int e = 0; e < 8; ++e) x[8 * k + e] = (float)xr[t][k][e];
-    float ss = 0.0f;
-#pragma unroll
-    for (int e = 0; e < 24; ++e) ss += x[e] * x[e];
-    ss = wave_sum(ss);
-    const float rr = 1.0f / __builtin_sqrtf(ss / (float)kQA + a.eps);
-#pragma unroll
-    for (int k = 0; k < 3; ++k) {
-      bf16x8 o;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) o[e] = (__bf16)((x[8 * k + e] * rr) * (float)wq[k][e]);
-      *(LDS_AS bf16x8*)((lds_char*)xn_mem + m * kXnPitch + 2 * (512 * k + 8 * lane)) = o;
-    }
-  }
-  __syncthreads();
   f32x16 acc = {};
 #pragma unroll
   for (int i = 0; i < KSW; ++i) {
-    const int k = 16 * (KSW * w + i) + h8;
-    const bf16x8 af = *(const LDS_AS bf16x8*)((const lds_char*)xn_mem + (lane & 31) * kXnPitch + 2 * k);
-    acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, bf[i], acc, 0, 0, 0);
+    const bf16x8 x = b_ok ? af[i] : bf16x8{};
+    const bf16x8 y = row_ok ? bf[i] : bf16x8{};
+    acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(x, y, acc, 0, 0, 0);
   }
   // fixed-order sum of the four partial tiles
   if (w > 0) {
@@ -273,16 +273,13 @@ __global__ void __launch_bounds__(kThreads) mla_qb_kernel(QueryArgs a) {
     for (int e = 0; e < 4; ++e) acc[4 * r4 + e] = s[e];
   }
   if (!row_ok) return;
-  // lane l, register r: token 8*(r/4) + 4*(l/32) + r%4, W_qb row nrow
-  const int head = nrow / kQB, r = nrow % kQB;
-  const float qsi = a.q_scale_inv[0];
+  // lane l, register r: token m0 + 8*(r/4) + 4*(l/32) + r%4, W_qb row nrow
+  float* const dst = a.qbp + (size_t)blockIdx.z * a.batch * nrows;
 #pragma unroll
   for (int i = 0; i < 16; ++i) {
-    const int b = m0 + 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3);
-    if (b >= a.batch) continue;
-    const __bf16 v = (__bf16)acc[i];
-    if (r < kNope) a.qn[((size_t)b * a.heads + head) * kNope + r] = v;
-    else a.out[((size_t)b * a.heads + head) * kOut + kDV + (r - kNope)] = e4m3_of_product((float)v, qsi);
+    const int bb = m0 + 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3);
+    if (bb >= a.batch) continue;
+    dst[(size_t)bb * nrows + nrow] = acc[i];
   }
 }
 
@@ -294,23 +291,35 @@ __global__ void __launch_bounds__(kThreads) mla_qb_kernel(QueryArgs a) {
 constexpr int kUkGroup = 128 * 128;  // bytes per column group
 __device__ __forceinline__ int uk_swz(int m) { return (((m >> 1) & 1) << 2) | (((m >> 3) & 1) << 1) | ((m >> 2) & 1); }
 
+constexpr int kQsPitch = kNope + 8;  // LDS row pitch (bf16 elements) of the nope q tile
+template <int KSPLIT>
 __global__ void __launch_bounds__(kThreads) mla_ql_kernel(QueryArgs a) {
   __shared__ __attribute__((aligned(16))) char uk_mem[2 * kUkGroup];
+  __shared__ __attribute__((aligned(16))) __bf16 qs_mem[kTok * kQsPitch];  // nope q tile, bf16
+  LDS_AS __bf16* const qs = (LDS_AS __bf16*)qs_mem;
   lds_char* const uk = (lds_char*)uk_mem;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int head = blockIdx.x, c0 = blockIdx.y * 128, m0 = blockIdx.z * kTok;
 
-  // A fragments: token m0 + l%32, nope columns 16ks + 8*(l/32) .. +7
-  // (unconditional loads from a clamped row; rows past the batch are zeroed)
+  // this lane's token in the A operand (rows past the batch are zeroed)
   const int b = m0 + (lane & 31);
   const bool b_ok = b < a.batch;
-  const int b_c = b_ok ? b : a.batch - 1;
-  bf16x8 af[kNope / 16];
+  // The nope q tile [32 tokens][128] in LDS as bf16: the KSPLIT fp32 partials
+  // of Q_B added in split order and rounded once.  Thread i reads four
+  // consecutive values of token i/32 from each partial (a token's 512 bytes
+  // come from 32 neighbouring threads).
+  const size_t nrows = (size_t)a.heads * kQB;
+  f32x4 qp[4][KSPLIT];
 #pragma unroll
-  for (int ks = 0; ks < kNope / 16; ++ks)
-    af[ks] = *(const bf16x8*)(a.qn + ((size_t)b_c * a.heads + head) * kNope + 16 * ks + 8 * (lane >> 5));
-  // stage W_uk[head][0..127][c0..c0+127]: 2048 chunks of 16 bytes, all eight
-  // of a thread loaded before any is stored
+  for (int j = 0; j < 4; ++j) {
+    const int i = tid + j * kThreads, t = i >> 5, c4 = 4 * (i & 31);
+    const int bt = min(m0 + t, a.batch - 1);
+#pragma unroll
+    for (int k = 0; k < KSPLIT; ++k)
+      qp[j][k] = *(const f32x4*)(a.qbp + ((size_t)k * a.batch + bt) * nrows + (size_t)head * kQB + c4);
+  }
+  // W_uk[head][0..127][c0..c0+127]: 2048 chunks of 16 bytes, all eight of a
+  // thread requested (with the partials above) before anything is stored
   constexpr int kStage = 128 * 16 / kThreads;
   u32x4 wv[kStage];
 #pragma unroll
@@ -319,14 +328,28 @@ __global__ void __launch_bounds__(kThreads) mla_ql_kernel(QueryArgs a) {
     wv[j] = *(const u32x4*)(a.w_uk + ((size_t)head * kNope + p) * kDV + c0 + 8 * ch);
   }
 #pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int i = tid + j * kThreads, t = i >> 5, c4 = 4 * (i & 31);
+    f32x4 sum = qp[j][0];
+#pragma unroll
+    for (int k = 1; k < KSPLIT; ++k) sum += qp[j][k];
+    *(LDS_AS bf16x4*)(qs + t * kQsPitch + c4) = __builtin_convertvector(sum, bf16x4);
+  }
+#pragma unroll
   for (int j = 0; j < kStage; ++j) {
     const int i = tid + j * kThreads, p = i >> 4, ch = i & 15;
     const int g = ch >> 3, x = ch & 7;
     *(LDS_AS u32x4*)(uk + g * kUkGroup + p * 128 + 16 * (x ^ uk_swz(p))) = wv[j];
   }
-#pragma unroll
-  for (int ks = 0; ks < kNope / 16; ++ks) af[ks] = b_ok ? af[ks] : bf16x8{};
   __syncthreads();
+  // A fragments: token m0 + l%32 (rows past the batch zeroed), nope columns
+  // 16ks + 8*(l/32) .. +7
+  bf16x8 af[kNope / 16];
+#pragma unroll
+  for (int ks = 0; ks < kNope / 16; ++ks) {
+    af[ks] = *(const LDS_AS bf16x8*)(qs + (lane & 31) * kQsPitch + 16 * ks + 8 * (lane >> 5));
+    af[ks] = b_ok ? af[ks] : bf16x8{};
+  }
   // B operand B[k][n] = W_uk[head][16ks + k][c] by transposed reads: lane l
   // needs column n = l%32 of rows k = 8*(l/32) + i, i = 0..7, the order the A
   // operand uses.  Wave w owns columns c0 + 32w .. +31; within 16-lane group
@@ -358,6 +381,27 @@ __global__ void __launch_bounds__(kThreads) mla_ql_kernel(QueryArgs a) {
     if (bb >= a.batch) continue;
     const float v = (float)(__bf16)acc[i];
     a.out[((size_t)bb * a.heads + head) * kOut + c] = e4m3_of_product(v, qsi);
+  }
+  // the rope rows of Q_B go to the output as they are (bf16 of the summed
+  // partials, then FP8): the workgroups of column block 0, eight values per
+  // thread
+  if (blockIdx.y == 0) {
+    const int t = m0 + (tid >> 3), r0 = kNope + 8 * (tid & 7);
+    if (t < a.batch) {
+      f32x4 s0 = {}, s1 = {};
+#pragma unroll
+      for (int k = 0; k < KSPLIT; ++k) {
+        const float* src = a.qbp + ((size_t)k * a.batch + t) * nrows + (size_t)head * kQB + r0;
+        s0 += *(const f32x4*)src;
+        s1 += *(const f32x4*)(src + 4);
+      }
+      uint8_t* dst = a.out + ((size_t)t * a.heads + head) * kOut + kDV + (r0 - kNope);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        dst[e] = e4m3_of_product((float)(__bf16)s0[e], qsi);
+        dst[4 + e] = e4m3_of_product((float)(__bf16)s1[e], qsi);
+      }
+    }
   }
 }
 
@@ -509,7 +553,20 @@ hipError_t launch_kv_insert(const InsertLaunch& k, hipStream_t stream) {
   return hipGetLastError();
 }
 
-size_t query_workspace_bytes(int32_t batch, int32_t heads) { return (size_t)batch * heads * kNope * 2 + 256; }
+// Q_B reduction split over workgroups when the 32-token x 32-row tiles
+// alone would leave most compute units idle
+int query_ksplit(int32_t batch, int32_t heads) {
+  const int tiles = ((heads * kQB + 31) / 32) * ((batch + kTok - 1) / kTok);
+  return tiles < 256 ? 4 : 1;
+}
+
+// Narrow batch: [B][H][128] bf16.  Tiled: [B][1536] bf16 normalised rows,
+// then [ksplit][B][H*192] fp32 Q_B partials.
+size_t query_workspace_bytes(int32_t batch, int32_t heads) {
+  if (batch <= kNarrow) return (size_t)batch * heads * kNope * 2 + 256;
+  return (((size_t)batch * kQA * 2 + 255) & ~(size_t)255) +
+         (size_t)query_ksplit(batch, heads) * batch * heads * kQB * 4 + 256;
+}
 
 hipError_t launch_query(const QueryLaunch& q, hipStream_t stream) {
   QueryArgs a;
@@ -520,6 +577,8 @@ hipError_t launch_query(const QueryLaunch& q, hipStream_t stream) {
   a.q_scale_inv = q.q_scale_inv;
   a.out = (uint8_t*)q.out;
   a.qn = (__bf16*)q.workspace;
+  a.xn = (__bf16*)q.workspace;
+  a.qbp = (float*)((char*)q.workspace + (((size_t)q.batch * kQA * 2 + 255) & ~(size_t)255));
   a.batch = q.batch;
   a.heads = q.heads;
   a.qkv_stride = q.qkv_stride;
@@ -533,10 +592,16 @@ hipError_t launch_query(const QueryLaunch& q, hipStream_t stream) {
     return hipGetLastError();
   }
   const int mt = (q.batch + kTok - 1) / kTok;
-  hipLaunchKernelGGL(mla_qb_kernel, dim3((q.heads * kQB + 31) / 32, mt), dim3(kThreads), 0, stream, a);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(mla_ql_kernel, dim3(q.heads, kDV / 128, mt), dim3(kThreads), 0, stream, a);
+  const int ksplit = query_ksplit(q.batch, q.heads);
+  hipLaunchKernelGGL(mla_norm_kernel, dim3((q.batch + 3) / 4), dim3(kThreads), 0, stream, a);
+  const dim3 qb_grid((q.heads * kQB + 31) / 32, mt, ksplit), ql_grid(q.heads, kDV / 128, mt);
+  if (ksplit == 4) {
+    hipLaunchKernelGGL(mla_qb_kernel<4>, qb_grid, dim3(kThreads), 0, stream, a);
+    hipLaunchKernelGGL(mla_ql_kernel<4>, ql_grid, dim3(kThreads), 0, stream, a);
+  } else {
+    hipLaunchKernelGGL(mla_qb_kernel<1>, qb_grid, dim3(kThreads), 0, stream, a);
+    hipLaunchKernelGGL(mla_ql_kernel<1>, ql_grid, dim3(kThreads), 0, stream, a);
+  }
   return hipGetLastError();
 }
 
