@@ -90,3 +90,29 @@ def test_large_insert():
     _say(f"   identical {np.mean(got == want) * 100:.4f}%, max step {step.max()}")
     assert step.max() <= 1 and np.mean(step[:, :, 512:] == 0) == 1.0
     assert np.mean(got == want) >= 0.999
+
+
+@pytest.mark.parametrize("batch,heads", [(8192, 8), (8, 128)])
+def test_query_largest_batch_per_form(batch, heads):
+    """The query front end at the largest batch of its wide (MFMA) form and
+    of its narrow (wave FMA) form, checked on sampled tokens: every token's
+    output depends on its own q_a row only, so the oracle runs on those rows.
+    Bars as in the query parity tests: every code equal to the oracle's or
+    one e4m3 step away, at least 99.9 % identical."""
+    qin = synth.make_query_inputs(205 + heads, batch=batch, heads=heads)
+    _say(f"[limits] query B={batch} H={heads}")
+    d = mla.query_to_device(qin)
+    out = mla.mla_query(d["qkv"], d["w_qa"], d["w_qb"], d["w_uk"], d["q_scale_inv"], eps=qin["eps"])
+    torch.cuda.synchronize()
+    got = out.cpu().numpy()
+    sample = sorted(set([0, batch - 1] + list(np.random.default_rng(9).choice(batch, min(batch, 6), replace=False))))
+    want = mo.mla_query(qin["qkv"][sample], qin["w_qa"], qin["w_qb"], qin["w_uk"], qin["q_scale_inv"],
+                        eps=qin["eps"])["out"]
+    g = got[sample]
+    assert not np.any(g == 0xFF) and not np.any(g == 0x7F), "NaN code for finite input"
+    rank = lambda c: np.where(np.asarray(c, np.int32) & 0x80, -(np.asarray(c, np.int32) & 0x7F),
+                              np.asarray(c, np.int32) & 0x7F)
+    step = np.abs(rank(g) - rank(want))
+    same = np.mean(step == 0)
+    _say(f"   codes identical {same * 100:.3f}%, max step {step.max()}")
+    assert step.max() <= 1 and same >= 0.999
