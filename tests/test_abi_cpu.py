@@ -240,3 +240,27 @@ def test_binding_raises_without_library(monkeypatch):
     monkeypatch.setattr(mla, "LIB_PATH", "/nonexistent/libmla.so")
     with pytest.raises(mla.MlaError):
         mla.lib()
+
+
+def test_query_workspace_sizes_per_form(L):
+    """The query's workspace follows its form: up to 8 tokens the bf16 nope
+    rows [B][H][128]; above, the bf16 normalised rows [B][1536] (256-byte
+    aligned) then the fp32 Q_B partials [ksplit][B][H*192], with the
+    reduction split in four when the 32 x 32 tiles would number under 256."""
+    def size(b, h):
+        n = ctypes.c_size_t(0)
+        assert L.mla_query_workspace_size(ctypes.byref(mla.QueryParams(b, h, 1536, 1e-6)), ctypes.byref(n)) == 0
+        return n.value
+
+    def align(x):
+        return (x + 255) & ~255
+
+    def tiles(b, h):
+        return ((h * 192 + 31) // 32) * ((b + 31) // 32)
+
+    for b, h in [(1, 1), (4, 128), (8, 8)]:
+        assert size(b, h) == b * h * 128 * 2 + 256
+    for b, h in [(9, 8), (64, 8), (64, 128), (8192, 8)]:
+        ksplit = 4 if tiles(b, h) < 256 else 1
+        assert size(b, h) == align(b * 1536 * 2) + ksplit * b * h * 192 * 4 + 256, (b, h)
+    assert tiles(64, 8) < 256 and tiles(64, 128) >= 256  # both forms of the split occur above
