@@ -260,6 +260,7 @@ struct LaneTables {
   uint32_t kaddr[4];  // QK^T A operand of this wave's k-step i: kaddr[i & 3] + 4096 * (i >> 2)
   uint32_t kaddr_r[2];  // tiled split: the rope k-steps
   uint32_t vaddr[2];  // PV A operand (tr reads) of this wave's first column block, rows 8tt + 4h + j: [tt]
+  uint32_t vswap;     // token-split softmax, part 1: 2048 (its PV k-step 0 is the slot's rows 16..31), else 0
 };
 
 // How the QK^T reduction is cut between the NSPLIT waves of a head group.
@@ -288,21 +289,25 @@ __device__ __forceinline__ int global_step(int part, int i) {
 
 // LDS address of the K fragment of global k-step g for this lane: logical
 // chunk 2g + h of row m (dims 16g + 8h .. +7), column group g / 4
-__device__ __forceinline__ uint32_t k_frag_addr(int g, int lane) {
-  const int m = lane & 31, h = lane >> 5;
+__device__ __forceinline__ uint32_t k_frag_addr(int g, int lane, int perm = 0) {
+  const int m = (lane & 31) ^ perm, h = lane >> 5;
   return kGroupBytes * (g >> 2) + m * 128 + 16 * ((2 * (g & 3) + h) ^ row_swz(m));
 }
 
 // Wave part `part` of a head group covers the k-steps above and column
 // blocks part*NCB .. +NCB-1.
+// perm = 16 (token-split softmax, part 1): the QK^T A operand takes the
+// slot's rows in the order 16..31, 0..15, so that this wave's own token half
+// lands in S^T registers 0..7 as it does for part 0.
 template <int NSPLIT, bool TILED>
-__device__ __forceinline__ void make_tables(LaneTables& t, int lane, int w, int part) {
+__device__ __forceinline__ void make_tables(LaneTables& t, int lane, int w, int part, int perm = 0) {
   using T = Tiling<NSPLIT>;
   constexpr int NCB = kCB / NSPLIT;
   t.dma = dma_lane_off(lane, w, kTS);
+  t.vswap = perm ? 2048u : 0u;
   // steps g0 + 4q + j (code steps, contiguous) differ from step g0 + j by q
   // column groups
-  for (int j = 0; j < 4; ++j) t.kaddr[j] = k_frag_addr(global_step<NSPLIT, TILED>(part, j), lane);
+  for (int j = 0; j < 4; ++j) t.kaddr[j] = k_frag_addr(global_step<NSPLIT, TILED>(part, j), lane, perm);
   for (int k = 0; k < 2; ++k) t.kaddr_r[k] = TILED && k < T::RS ? k_frag_addr(global_step<NSPLIT, TILED>(part, T::CS + k), lane) : 0;
   {
     // ds_read_b64_tr_b16 for column block cb, k-step 0: within 16-lane group
@@ -538,6 +543,8 @@ __device__ __forceinline__ void keep_alive(const T& v) {
 // What rides between the QK^T MFMAs of a step: the next slot's copies, the
 // previous slot's softmax, and (top-k) that softmax's validity mask.
 constexpr int kPipeDma = 1, kPipeSoft = 2, kPipeMask = 4;
+constexpr int kPipeHalf = 8;   // token-split softmax: this wave's 16 tokens (S^T registers 0..7) only
+constexpr int kPipeOwnL = 16;  // full softmax, but only registers 0..7 (this wave's tokens) enter l_sum
 constexpr int kFenceValu = 0x2 | 0x400;  // sched_barrier mask: VALU and transcendental may cross
 
 // Publish this wave's partial: [wave][r4][lane] 16-byte rows, lane-contiguous.
@@ -549,16 +556,27 @@ __device__ __forceinline__ void put_partial(LDS_AS f32x4* xch, const f32x16& s, 
   }
 }
 
+// Token-split softmax (two parts): the partner needs only S^T registers
+// 8..15 of this wave's partial (its own token half); r4 slot 0 of this
+// wave's region then carries this wave's bf16 P^T half.
+__device__ __forceinline__ void put_partial_half(LDS_AS f32x4* xch, const f32x16& s, int w, int lane) {
+#pragma unroll
+  for (int r4 = 2; r4 < 4; ++r4) xch[(w * 4 + r4) * 64 + lane] = f32x4{s[4 * r4], s[4 * r4 + 1], s[4 * r4 + 2], s[4 * r4 + 3]};
+}
+
 // Full S^T of the head group.  Two parts: own + partner (fp32 addition is
 // commutative, so both waves get the same bits).  Four parts: (p0 + p1) +
 // (p2 + p3), every term read back from LDS.
 template <int NSPLIT>
-__device__ __forceinline__ f32x16 total_scores(const LDS_AS f32x4* xch, const f32x16& own, int w, int lane) {
+__device__ __forceinline__ f32x16 total_scores(const LDS_AS f32x4* xch, const f32x16& own, int w, int lane,
+                                               int cross = 0) {
   f32x16 tot;
   if constexpr (NSPLIT == 2) {
 #pragma unroll
     for (int r4 = 0; r4 < 4; ++r4) {
-      const f32x4 v = xch[((w ^ 1) * 4 + r4) * 64 + lane];
+      // (cross = 2, token-split softmax: the partner holds this wave's
+      // registers 0..7 in its 8..15 and the reverse)
+      const f32x4 v = xch[((w ^ 1) * 4 + (r4 ^ cross)) * 64 + lane];
 #pragma unroll
       for (int e = 0; e < 4; ++e) tot[4 * r4 + e] = own[4 * r4 + e] + v[e];
     }
@@ -612,6 +630,7 @@ struct SoftCtx {
   const LDS_AS f32x4* xch;
   int w, lane;
   float scale_log2;
+  int cross = 0;  // token-split softmax: partner register group of r4 is r4 ^ 2
 };
 
 // Scores of tokens whose bit in `mask` is clear become -inf.  Lane l,
@@ -635,7 +654,7 @@ template <int NSPLIT>
 __device__ __forceinline__ void soft_read(SoftPipe& sp, const SoftCtx& c) {
   if constexpr (NSPLIT == 2) {
 #pragma unroll
-    for (int r4 = 0; r4 < 4; ++r4) sp.xr[r4] = c.xch[((c.w ^ 1) * 4 + r4) * 64 + c.lane];
+    for (int r4 = 0; r4 < 4; ++r4) sp.xr[r4] = c.xch[((c.w ^ 1) * 4 + (r4 ^ c.cross)) * 64 + c.lane];
   } else {
     const int g0 = c.w & ~3;
 #pragma unroll
@@ -643,6 +662,13 @@ __device__ __forceinline__ void soft_read(SoftPipe& sp, const SoftCtx& c) {
 #pragma unroll
       for (int r4 = 0; r4 < 4; ++r4) sp.xr[4 * q + r4] = c.xch[((g0 + q) * 4 + r4) * 64 + c.lane];
   }
+}
+
+// Token-split softmax, steady state: only the partner's registers 8..15
+// (this wave's token half)
+__device__ __forceinline__ void soft_read_half(SoftPipe& sp, const SoftCtx& c) {
+  sp.xr[0] = c.xch[((c.w ^ 1) * 4 + 2) * 64 + c.lane];
+  sp.xr[1] = c.xch[((c.w ^ 1) * 4 + 3) * 64 + c.lane];
 }
 
 enum : int {
@@ -656,7 +682,40 @@ enum : int {
   kStLsum = kStExp0 + 8,
   kSoftStages
 };
-template <int NSPLIT, int ST, bool MASKED>
+// The token-split softmax stages: 8 scores per lane (x[0..7] = own
+// registers 0..7 + the partner's 8..15), 8 exponentials into p0.
+template <int ST>
+__device__ __forceinline__ void soft_stage_half(SoftPipe& sp, SoftmaxState& st, const SoftCtx& c) {
+  if constexpr (ST == kStSum0) {
+#pragma unroll
+    for (int r4 = 0; r4 < 2; ++r4) {
+      const f32x4 v = f32x4{sp.own[4 * r4], sp.own[4 * r4 + 1], sp.own[4 * r4 + 2], sp.own[4 * r4 + 3]} + sp.xr[r4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) sp.x[4 * r4 + e] = v[e];
+    }
+  } else if constexpr (ST == kStMaxA) {
+    sp.t[0] = fmaxf(fmaxf(sp.x[0], sp.x[1]), sp.x[2]);
+    sp.t[1] = fmaxf(fmaxf(sp.x[3], sp.x[4]), sp.x[5]);
+    sp.t[2] = fmaxf(sp.x[6], sp.x[7]);
+  } else if constexpr (ST == kStMaxB) {
+    sp.mx = fmaxf(fmaxf(sp.t[0], sp.t[1]), sp.t[2]);
+  } else if constexpr (ST == kStHalves) {
+    sp.mx = max_halves(sp.mx) * c.scale_log2;
+  } else if constexpr (ST == kStRef) {
+    st.m_ref = st.m_ref == -INFINITY ? sp.mx : st.m_ref;
+    st.m_seen = fmaxf(st.m_seen, sp.mx);
+    sp.nref = neg_ref(st.m_ref);
+  } else if constexpr (ST >= kStExp0 && ST < kStExp0 + 8) {
+    constexpr int k = ST - kStExp0;
+    sp.p0[k] = __builtin_amdgcn_exp2f(__builtin_fmaf(sp.x[k], c.scale_log2, sp.nref));
+    if constexpr (k == 1) sp.la = sp.p0[0];
+    else if constexpr (k > 1) sp.la += sp.p0[k - 1];
+  } else if constexpr (ST == kStLsum) {
+    st.l_sum += sp.la + sp.p0[7];
+  }
+}
+
+template <int NSPLIT, int ST, bool MASKED, bool OWNL = false>
 __device__ __forceinline__ void soft_stage(SoftPipe& sp, SoftmaxState& st, const SoftCtx& c) {
   if constexpr (ST == kStSum0 || ST == kStSum1) {
     constexpr int r0 = ST == kStSum0 ? 0 : 2;  // first row group of four
@@ -695,7 +754,8 @@ __device__ __forceinline__ void soft_stage(SoftPipe& sp, SoftmaxState& st, const
       sp.lb += sp.p1[k - 1];
     }
   } else if constexpr (ST == kStLsum) {
-    st.l_sum += (sp.la + sp.p0[7]) + (sp.lb + sp.p1[7]);
+    if constexpr (OWNL) st.l_sum += sp.la + sp.p0[7];
+    else st.l_sum += (sp.la + sp.p0[7]) + (sp.lb + sp.p1[7]);
   }
 }
 
@@ -715,11 +775,12 @@ constexpr int stage_hi(int KS, int I) {
 }
 static_assert(stage_hi(18, 17) == kSoftStages && stage_hi(9, 8) == kSoftStages, "every stage is scheduled");
 
-template <int NSPLIT, int ST0, int ST1, bool MASKED>
+template <int NSPLIT, int ST0, int ST1, bool MASKED, int PIPE = 0>
 __device__ __forceinline__ void soft_stages(SoftPipe& sp, SoftmaxState& st, const SoftCtx& c) {
   if constexpr (ST0 < ST1 && ST0 < kSoftStages) {
-    soft_stage<NSPLIT, ST0, MASKED>(sp, st, c);
-    soft_stages<NSPLIT, ST0 + 1, ST1, MASKED>(sp, st, c);
+    if constexpr ((PIPE & kPipeHalf) != 0) soft_stage_half<ST0>(sp, st, c);
+    else soft_stage<NSPLIT, ST0, MASKED, (PIPE & kPipeOwnL) != 0>(sp, st, c);
+    soft_stages<NSPLIT, ST0 + 1, ST1, MASKED, PIPE>(sp, st, c);
   }
 }
 
@@ -741,10 +802,11 @@ __device__ __forceinline__ void pv_load(const lds_char* buf, const LaneTables& t
   const uint32_t x = (cb & 1) ? 64u : 0u;
   const lds_char* p0 = buf + (t.vaddr[0] ^ x) + kGroupBytes * (cb >> 1);
   const lds_char* p1 = buf + (t.vaddr[1] ^ x) + kGroupBytes * (cb >> 1);
-  v[0] = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((LDS_AS bf16x4*)p0);
-  v[1] = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((LDS_AS bf16x4*)p1);
-  v[2] = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((LDS_AS bf16x4*)(p0 + 16 * 128));
-  v[3] = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((LDS_AS bf16x4*)(p1 + 16 * 128));
+  // (k-step 0 reads rows 0..15 of the slot, or 16..31 when vswap = 2048)
+  v[0] = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((LDS_AS bf16x4*)(p0 + t.vswap));
+  v[1] = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((LDS_AS bf16x4*)(p1 + t.vswap));
+  v[2] = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((LDS_AS bf16x4*)(p0 + (16 * 128 - t.vswap)));
+  v[3] = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((LDS_AS bf16x4*)(p1 + (16 * 128 - t.vswap)));
 }
 
 // The first kRA - 1 K fragments of a slot, issued before the rest of the
@@ -787,7 +849,7 @@ __device__ __forceinline__ void qk_steps(f32x16 (&acc)[kMaxAcc], bf16x8 (&kb)[kR
       if constexpr (I % R == R - 1) dma_issue<I / R>(side.job);
     }
     if constexpr ((PIPE & kPipeSoft) != 0) {
-      soft_stages<NSPLIT, stage_lo(KS, I), stage_hi(KS, I), (PIPE & kPipeMask) != 0>(sp, st, c);
+      soft_stages<NSPLIT, stage_lo(KS, I), stage_hi(KS, I), (PIPE & kPipeMask) != 0, PIPE>(sp, st, c);
       // the PV that follows starts on data already in registers
       if constexpr (I == KS - 3) pv_load(side.pvbuf, t, 0, *side.va0);
     }
@@ -850,7 +912,7 @@ __device__ __forceinline__ f32x16 qk_partial(bf16x8 (&kb)[kRA], const lds_char* 
 // holds token 8*(r/4) + 4*(l/32) + r%4 of head l%32; tokens at and beyond
 // nvalid (only the last slot of a segment has any) get p = 0.
 __device__ __forceinline__ void softmax_slot(const f32x16& s, uint32_t mask, SoftmaxState& st, float scale_log2,
-                                             f32x8& p0, f32x8& p1, int lane) {
+                                             f32x8& p0, f32x8& p1, int lane, bool own_l = false) {
   f32x16 x = s;
   apply_mask(x, mask, lane);
   float mx = x[0];
@@ -868,8 +930,9 @@ __device__ __forceinline__ void softmax_slot(const f32x16& s, uint32_t mask, Sof
     p1[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(x[r + 8], scale_log2, nref));
   }
   float lsum = 0.0f;
+  // (own_l: token-split softmax, only this wave's tokens, registers 0..7)
 #pragma unroll
-  for (int r = 0; r < 8; ++r) lsum += p0[r] + p1[r];
+  for (int r = 0; r < 8; ++r) lsum += own_l ? p0[r] : p0[r] + p1[r];
   st.l_sum += lsum;
 }
 
@@ -988,6 +1051,14 @@ mla_decode_kernel(DecodeArgs a) {
   constexpr int NCB = kCB / NSPLIT;
   constexpr int HG = kWaves / NSPLIT;  // 32-head groups per workgroup
   constexpr bool TILED = kv_fp8(KVM);  // FP8 cache: tiled QK^T split, scales applied in fp32
+  // Token-split softmax (bf16 copy ring, two parts, no causal mask): after a
+  // segment's first slot, each wave of a pair takes the softmax of its own 16
+  // tokens only and the pair swaps bf16 P^T halves before PV.  Part 1 reads
+  // its K rows as 16..31, 0..15, so its own tokens sit in S^T registers 0..7
+  // as part 0's do.  The first slot runs the full exchange, so the two waves
+  // fix the same reference; l_sum holds own tokens only and the pair adds its
+  // two sums at the end.
+  constexpr bool TSOFT = NSPLIT == 2 && KVM == kKvBf16 && !CAUSAL;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -1028,7 +1099,7 @@ mla_decode_kernel(DecodeArgs a) {
   if constexpr (CAUSAL) lag = a.tq - 1 - min(head, a.heads - 1) / a.heads_tok;
 
   LaneTables tab;
-  make_tables<NSPLIT, TILED>(tab, lane, w, part);
+  make_tables<NSPLIT, TILED>(tab, lane, w, part, TSOFT && part == 1 ? 16 : 0);
 
   int b = pl.b0, p = pl.p0;
   bool first_seg = true;
@@ -1155,7 +1226,7 @@ mla_decode_kernel(DecodeArgs a) {
         for (int c = 0; c < NCB; ++c) acc.o[c] = f32x16{};
         st.l_sum = 0.0f;
         st.m_seen = -INFINITY;
-        const SoftCtx sctx{xch, w, lane, scale_log2};
+        const SoftCtx sctx{xch, w, lane, scale_log2, TSOFT ? 2 : 0};
         SoftPipe sp;
         POps<NSPLIT, TILED> po;
         bf16x8 kb[kRA];
@@ -1177,7 +1248,62 @@ mla_decode_kernel(DecodeArgs a) {
           // softmax of slot s with the copies of slot s+3 (into the ring
           // position that slot s-1 left) between its MFMAs, then PV of slot
           // s; a second barrier frees ring position s and the exchange buffer
-          for (int s = 0; s + 1 < nslots; ++s) {
+          int s_first = 0;
+          if constexpr (TSOFT) {
+            if (nslots > 1) {
+              // slot 0 as below, full exchange (own tokens into l_sum)
+              put_partial(xch, sc, w, lane);
+              wait_vm_lgkm0<kDmaPerWave>();
+              barrier();
+              const lds_char* const kbuf = ring + kSlotBytes;
+              qk_preload<NSPLIT, false>(kb, kbuf, tab);
+              soft_read<NSPLIT>(sp, sctx);
+              __builtin_amdgcn_sched_barrier(0);
+              QkSide side;
+              side.job = prep_slot(3, 3, ring, a, sg, pc, tab, w, lane);
+              side.pvbuf = ring;
+              side.va0 = &va0;
+              sp.own = sc;
+              sc = qk_partial<NSPLIT, kPipeDma | kPipeSoft | kPipeOwnL>(kb, kbuf, qf, tab, side, sp, st, sctx);
+              make_pops<NSPLIT, TILED>(po, sp.p0, sp.p1, nullptr, part, lane);
+              pv_slot<NSPLIT, TILED>(side.pvbuf, va0, po, tab, acc);
+              wait_vm_lgkm0<63>();
+              barrier();
+              s_first = 1;
+            }
+            // slots 1 ..: the partner needs only this wave's registers
+            // 8..15; after the QK^T of slot s+1 (with the own-half softmax of
+            // slot s) the pair swaps P^T halves through r4 slot 0 of each
+            // wave's exchange region; a barrier orders the swap, and the
+            // next slot's first barrier (after lgkmcnt(0)) frees the ring
+            // position and the exchange buffer
+            for (int s = s_first; s + 1 < nslots; ++s) {
+              put_partial_half(xch, sc, w, lane);
+              wait_vm_lgkm0<kDmaPerWave>();
+              barrier();
+              const lds_char* const kbuf = ring + ((s + 1) & (kRing - 1)) * kSlotBytes;
+              qk_preload<NSPLIT, false>(kb, kbuf, tab);
+              soft_read_half(sp, sctx);
+              __builtin_amdgcn_sched_barrier(0);
+              QkSide side;
+              side.job = prep_slot(s + 3, s + 3, ring, a, sg, pc, tab, w, lane);
+              side.pvbuf = ring + (s & (kRing - 1)) * kSlotBytes;
+              side.va0 = &va0;
+              sp.own = sc;
+              sc = qk_partial<NSPLIT, kPipeDma | kPipeSoft | kPipeHalf>(kb, kbuf, qf, tab, side, sp, st, sctx);
+              const bf16x8 mine = __builtin_convertvector(sp.p0, bf16x8);
+              *(LDS_AS bf16x8*)(xch + (w * 4) * 64 + lane) = mine;
+              wait_vm_lgkm0<63>();
+              barrier();
+              po.b0[0] = mine;
+              po.b1[0] = *(const LDS_AS bf16x8*)(xch + ((w ^ 1) * 4) * 64 + lane);
+              pv_slot<NSPLIT, TILED>(side.pvbuf, va0, po, tab, acc);
+            }
+            // the partner may still be reading this wave's P^T half
+            wait_vm_lgkm0<63>();
+            barrier();
+          }
+          for (int s = 0; !TSOFT && s + 1 < nslots; ++s) {
             put_partial(xch, sc, w, lane);
             wait_vm_lgkm0<kDmaPerWave>();
             barrier();
@@ -1311,9 +1437,12 @@ mla_decode_kernel(DecodeArgs a) {
         {
           // last slot (the only dense one that can be short)
           barrier();
-          const f32x16 tot = total_scores<NSPLIT>(xch, sc, w, lane);
+          const f32x16 tot = total_scores<NSPLIT>(xch, sc, w, lane, TSOFT ? 2 : 0);
           f32x8 q0, q1;
-          softmax_slot(tot, CAUSAL ? causal_mask(nslots - 1) : slot_mask(nslots - 1), st, scale_log2, q0, q1, lane);
+          uint32_t lmask = CAUSAL ? causal_mask(nslots - 1) : slot_mask(nslots - 1);
+          // (token-split, part 1: register r holds token t ^ 16)
+          if (TSOFT && part == 1) lmask = (lmask >> 16) | (lmask << 16);
+          softmax_slot(tot, lmask, st, scale_log2, q0, q1, lane, TSOFT);
           const LDS_AS float* ltab = (const LDS_AS float*)(ring + kFillRing * kSlotBytes) + last_pos * (4 * kTS);
           pv_load(ring + last_pos * kSlotBytes, tab, 0, va0);
           make_pops<NSPLIT, TILED>(po, q0, q1, ltab, part, lane);
@@ -1324,21 +1453,35 @@ mla_decode_kernel(DecodeArgs a) {
         barrier();
         const int my_vote = __any(st.m_seen > st.m_ref + kTau) ? 1 : 0;  // all lanes vote
         if (lane == 0) votes[w] = my_vote;
+        // token-split: m_seen covers this wave's tokens; a redo takes the
+        // pair's max (exchanged beside the votes)
+        LDS_AS float* const mx_x = (LDS_AS float*)xbuf + 1024;
+        if constexpr (TSOFT) mx_x[w * 64 + lane] = st.m_seen;
         wait_vm_lgkm0<0>();
         barrier();
         int vote = 0;
 #pragma unroll
         for (int i = 0; i < kWaves; ++i) vote |= votes[i];
+        float m_pair = st.m_seen;
+        if constexpr (TSOFT) m_pair = fmaxf(m_pair, mx_x[(w ^ 1) * 64 + lane]);
         wait_vm_lgkm0<0>();
         barrier();  // votes read before the buffer is reused
         if (!__builtin_amdgcn_readfirstlane(vote)) break;
-        st.m_ref = st.m_seen;
+        st.m_ref = m_pair;
         if (!kv_topk(KVM) && sg.npages > 64) page_cache_load(pc, sg.bt_seg, 0, sg.npages, lane);
       }
 
       // ---- epilogue: normalise and store this wave's columns (final output,
       // or this piece's partial in its workspace slot)
-      const float l_tot = sum_halves(st.l_sum);
+      float l_tot = sum_halves(st.l_sum);
+      if constexpr (TSOFT) {
+        // the pair's two token halves (the buffer is free after the vote)
+        LDS_AS float* const l_x = (LDS_AS float*)xbuf + 2048;
+        l_x[w * 64 + lane] = l_tot;
+        wait_vm_lgkm0<0>();
+        barrier();
+        l_tot += l_x[(w ^ 1) * 64 + lane];
+      }
       const float inv = l_tot > 0.0f ? kdesc / l_tot : 0.0f;
       const float lse2 = l_tot > 0.0f ? st.m_ref + __builtin_amdgcn_logf(l_tot) : -INFINITY;
       if (head_ok) {
