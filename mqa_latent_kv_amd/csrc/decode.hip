@@ -545,6 +545,7 @@ __device__ __forceinline__ void keep_alive(const T& v) {
 constexpr int kPipeDma = 1, kPipeSoft = 2, kPipeMask = 4;
 constexpr int kPipeHalf = 8;   // token-split softmax: this wave's 16 tokens (S^T registers 0..7) only
 constexpr int kPipeOwnL = 16;  // full softmax, but only registers 0..7 (this wave's tokens) enter l_sum
+constexpr int kPipePv2 = 32;   // the PV that follows reads two V^T blocks ahead (pv_slot2)
 constexpr int kFenceValu = 0x2 | 0x400;  // sched_barrier mask: VALU and transcendental may cross
 
 // Publish this wave's partial: [wave][r4][lane] 16-byte rows, lane-contiguous.
@@ -826,6 +827,7 @@ struct QkSide {
   DmaJob job;
   const lds_char* pvbuf;  // slot whose PV follows
   VBlock* va0;            // where its first V^T block goes
+  VBlock* va1;            // (kPipePv2) where its second V^T block goes
 };
 
 template <int NSPLIT, int I, int PIPE, bool TILED>
@@ -852,6 +854,7 @@ __device__ __forceinline__ void qk_steps(f32x16 (&acc)[kMaxAcc], bf16x8 (&kb)[kR
       soft_stages<NSPLIT, stage_lo(KS, I), stage_hi(KS, I), (PIPE & kPipeMask) != 0, PIPE>(sp, st, c);
       // the PV that follows starts on data already in registers
       if constexpr (I == KS - 3) pv_load(side.pvbuf, t, 0, *side.va0);
+      if constexpr ((PIPE & kPipePv2) != 0 && I == KS - 2) pv_load(side.pvbuf, t, 1, *side.va1);
     }
     qk_steps<NSPLIT, I + 1, PIPE, TILED>(acc, kb, buf, qf, t, side, sp, st, c);
   }
@@ -995,6 +998,43 @@ __device__ __forceinline__ void pv_slot(const lds_char* buf, const VBlock& va0, 
     // this block's operands, and the previous block's (its MFMAs are
     // independent of these and may still be in the matrix core), stay
     // out of the reads' way
+    keep_alive(v0);
+    keep_alive(v1);
+    if (cb > 0) {
+      keep_alive(prev0);
+      keep_alive(prev1);
+    }
+    prev0 = v0;
+    prev1 = v1;
+  }
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+// pv_slot with the reads two column blocks ahead: blocks 0 and 1 arrive
+// loaded, and the reads for block cb + 2 go to the buffer of block cb - 2
+// (four buffers), whose MFMAs have left the matrix core.  Token-split
+// softmax: the PV starts right after the barrier that publishes the
+// partner's P^T half, and its read is then the only one in flight.
+template <int NSPLIT>
+__device__ __forceinline__ void pv_slot2(const lds_char* buf, const VBlock& va0, const VBlock& va1,
+                                         const POps<NSPLIT, false>& po, const LaneTables& t, Acc<NSPLIT>& acc) {
+  constexpr int NCB = kCB / NSPLIT;
+  VBlock va[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    va[0][i] = va0[i];
+    va[1][i] = va1[i];
+  }
+  bf16x8 prev0 = {}, prev1 = {};
+#pragma unroll
+  for (int cb = 0; cb < NCB; ++cb) {
+    __builtin_amdgcn_sched_barrier(0);
+    const VBlock& v = va[cb % 4];
+    const bf16x8 v0 = __builtin_shufflevector(v[0], v[1], 0, 1, 2, 3, 4, 5, 6, 7);
+    const bf16x8 v1 = __builtin_shufflevector(v[2], v[3], 0, 1, 2, 3, 4, 5, 6, 7);
+    acc.o[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(v0, po.b0[0], acc.o[cb], 0, 0, 0);
+    acc.o[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(v1, po.b1[0], acc.o[cb], 0, 0, 0);
+    if (cb + 2 < NCB) pv_load(buf, t, cb + 2, va[(cb + 2) % 4]);
     keep_alive(v0);
     keep_alive(v1);
     if (cb > 0) {
@@ -1230,7 +1270,7 @@ mla_decode_kernel(DecodeArgs a) {
         SoftPipe sp;
         POps<NSPLIT, TILED> po;
         bf16x8 kb[kRA];
-        VBlock va0;
+        VBlock va0, va1;
         f32x16 sc;
         int last_pos;  // ring position of the last slot
         if constexpr (KVM == kKvBf16) {
@@ -1289,15 +1329,17 @@ mla_decode_kernel(DecodeArgs a) {
               side.job = prep_slot(s + 3, s + 3, ring, a, sg, pc, tab, w, lane);
               side.pvbuf = ring + (s & (kRing - 1)) * kSlotBytes;
               side.va0 = &va0;
+              side.va1 = &va1;
               sp.own = sc;
-              sc = qk_partial<NSPLIT, kPipeDma | kPipeSoft | kPipeHalf>(kb, kbuf, qf, tab, side, sp, st, sctx);
+              sc = qk_partial<NSPLIT, kPipeDma | kPipeSoft | kPipeHalf | kPipePv2>(kb, kbuf, qf, tab, side, sp, st,
+                                                                                   sctx);
               const bf16x8 mine = __builtin_convertvector(sp.p0, bf16x8);
               *(LDS_AS bf16x8*)(xch + (w * 4) * 64 + lane) = mine;
               wait_vm_lgkm0<63>();
               barrier();
               po.b0[0] = mine;
               po.b1[0] = *(const LDS_AS bf16x8*)(xch + ((w ^ 1) * 4) * 64 + lane);
-              pv_slot<NSPLIT, TILED>(side.pvbuf, va0, po, tab, acc);
+              pv_slot2<NSPLIT>(side.pvbuf, va0, va1, po, tab, acc);
             }
             // the partner may still be reading this wave's P^T half
             wait_vm_lgkm0<63>();

@@ -193,6 +193,28 @@ def test_running_max_jumps(heads):
     compare(inp, out, lse, rtol=2.0**-7, scale=abs_weighted_v(inp))
 
 
+@pytest.mark.parametrize("half", [0, 1])
+def test_running_max_jumps_in_one_token_half(half):
+    """As above, but only the positions in one half of every 32-token slot
+    (p % 32 < 16, or >= 16) grow: with 128 heads the two waves of a head
+    group each take the softmax of one token half after a segment's first
+    slot, so only one wave sees the jumps and the restart must still use the
+    maximum over both halves."""
+    inp = synth.make_decode_inputs(131 + half, batch=3, heads=128, seqlens=[700, 1500, 129], pages_per_seq=24)
+    kv = codecs.bf16_bits_to_f64(inp["kv"]).reshape(-1, 576)
+    bt = inp["block_table"]
+    for b in range(3):
+        n = int(inp["seqlens"][b])
+        pos = np.arange(n)
+        rows = mo.physical_rows(bt[b], pos)
+        grow = ((pos % 32) >= 16) == bool(half)
+        kv[rows] *= np.where(grow, 1.0 + pos / 16.0, 1.0)[:, None]
+    inp["kv"] = codecs.f64_to_bf16_bits(kv).reshape(inp["kv"].shape)
+    _say(f"[decode growing scores, token half {half}] H=128")
+    out, lse = run_gpu(inp)
+    compare(inp, out, lse, rtol=2.0**-7, scale=abs_weighted_v(inp))
+
+
 def test_topk_masking_rules():
     """Entries that are -1, negative, or at/after seqlen contribute nothing; a
     sequence whose entries are all masked gets O = 0 and LSE = -inf."""
