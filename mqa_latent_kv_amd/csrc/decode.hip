@@ -685,7 +685,7 @@ enum : int {
 };
 // The token-split softmax stages: 8 scores per lane (x[0..7] = own
 // registers 0..7 + the partner's 8..15), 8 exponentials into p0.
-template <int ST>
+template <int ST, bool MASKED>
 __device__ __forceinline__ void soft_stage_half(SoftPipe& sp, SoftmaxState& st, const SoftCtx& c) {
   if constexpr (ST == kStSum0) {
 #pragma unroll
@@ -694,6 +694,8 @@ __device__ __forceinline__ void soft_stage_half(SoftPipe& sp, SoftmaxState& st, 
 #pragma unroll
       for (int e = 0; e < 4; ++e) sp.x[4 * r4 + e] = v[e];
     }
+    // (the mask as this wave's registers see the tokens)
+    if constexpr (MASKED) apply_mask<0, 8>(sp.x, sp.mask, c.lane);
   } else if constexpr (ST == kStMaxA) {
     sp.t[0] = fmaxf(fmaxf(sp.x[0], sp.x[1]), sp.x[2]);
     sp.t[1] = fmaxf(fmaxf(sp.x[3], sp.x[4]), sp.x[5]);
@@ -779,7 +781,7 @@ static_assert(stage_hi(18, 17) == kSoftStages && stage_hi(9, 8) == kSoftStages, 
 template <int NSPLIT, int ST0, int ST1, bool MASKED, int PIPE = 0>
 __device__ __forceinline__ void soft_stages(SoftPipe& sp, SoftmaxState& st, const SoftCtx& c) {
   if constexpr (ST0 < ST1 && ST0 < kSoftStages) {
-    if constexpr ((PIPE & kPipeHalf) != 0) soft_stage_half<ST0>(sp, st, c);
+    if constexpr ((PIPE & kPipeHalf) != 0) soft_stage_half<ST0, MASKED>(sp, st, c);
     else soft_stage<NSPLIT, ST0, MASKED, (PIPE & kPipeOwnL) != 0>(sp, st, c);
     soft_stages<NSPLIT, ST0 + 1, ST1, MASKED, PIPE>(sp, st, c);
   }
@@ -1091,14 +1093,17 @@ mla_decode_kernel(DecodeArgs a) {
   constexpr int NCB = kCB / NSPLIT;
   constexpr int HG = kWaves / NSPLIT;  // 32-head groups per workgroup
   constexpr bool TILED = kv_fp8(KVM);  // FP8 cache: tiled QK^T split, scales applied in fp32
-  // Token-split softmax (bf16 copy ring, two parts, no causal mask): after a
+  // Token-split softmax (bf16 copy ring, two parts): after a
   // segment's first slot, each wave of a pair takes the softmax of its own 16
   // tokens only and the pair swaps bf16 P^T halves before PV.  Part 1 reads
   // its K rows as 16..31, 0..15, so its own tokens sit in S^T registers 0..7
   // as part 0's do.  The first slot runs the full exchange, so the two waves
   // fix the same reference; l_sum holds own tokens only and the pair adds its
-  // two sums at the end.
-  constexpr bool TSOFT = NSPLIT == 2 && KVM == kKvBf16 && !CAUSAL;
+  // two sums at the end.  Part 1 applies token masks rotated by 16
+  // (own_mask).  A row whose tokens in the first slot are all
+  // masked sees none later in the segment either (the limit only falls
+  // behind), so its reference stays -inf in both waves.
+  constexpr bool TSOFT = NSPLIT == 2 && KVM == kKvBf16;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -1178,6 +1183,8 @@ mla_decode_kernel(DecodeArgs a) {
         const int nv = lim - (sg.tok0 + s * kTS);
         return nv <= 0 ? 0u : low_mask(nv);
       };
+      // a token mask as this wave's S^T registers hold the tokens
+      auto own_mask = [&](uint32_t m) -> uint32_t { return TSOFT && part == 1 ? (m >> 16) | (m << 16) : m; };
 
       // query fragments (B operand of S^T = K.Q^T): head `head`, columns
       // 16g + 8*(lane/32) .. +7 for global k-step g of this wave's local step i
@@ -1304,7 +1311,13 @@ mla_decode_kernel(DecodeArgs a) {
               side.pvbuf = ring;
               side.va0 = &va0;
               sp.own = sc;
-              sc = qk_partial<NSPLIT, kPipeDma | kPipeSoft | kPipeOwnL>(kb, kbuf, qf, tab, side, sp, st, sctx);
+              if (CAUSAL && causal_from == 0) {
+                sp.mask = own_mask(causal_mask(0));
+                sc = qk_partial<NSPLIT, kPipeDma | kPipeSoft | kPipeOwnL | kPipeMask>(kb, kbuf, qf, tab, side, sp, st,
+                                                                                    sctx);
+              } else {
+                sc = qk_partial<NSPLIT, kPipeDma | kPipeSoft | kPipeOwnL>(kb, kbuf, qf, tab, side, sp, st, sctx);
+              }
               make_pops<NSPLIT, TILED>(po, sp.p0, sp.p1, nullptr, part, lane);
               pv_slot<NSPLIT, TILED>(side.pvbuf, va0, po, tab, acc);
               wait_vm_lgkm0<63>();
@@ -1331,8 +1344,14 @@ mla_decode_kernel(DecodeArgs a) {
               side.va0 = &va0;
               side.va1 = &va1;
               sp.own = sc;
-              sc = qk_partial<NSPLIT, kPipeDma | kPipeSoft | kPipeHalf | kPipePv2>(kb, kbuf, qf, tab, side, sp, st,
-                                                                                   sctx);
+              if (CAUSAL && s >= causal_from) {
+                sp.mask = own_mask(causal_mask(s));
+                sc = qk_partial<NSPLIT, kPipeDma | kPipeSoft | kPipeHalf | kPipePv2 | kPipeMask>(kb, kbuf, qf, tab, side,
+                                                                                               sp, st, sctx);
+              } else {
+                sc = qk_partial<NSPLIT, kPipeDma | kPipeSoft | kPipeHalf | kPipePv2>(kb, kbuf, qf, tab, side, sp, st,
+                                                                                     sctx);
+              }
               const bf16x8 mine = __builtin_convertvector(sp.p0, bf16x8);
               *(LDS_AS bf16x8*)(xch + (w * 4) * 64 + lane) = mine;
               wait_vm_lgkm0<63>();
@@ -1481,9 +1500,7 @@ mla_decode_kernel(DecodeArgs a) {
           barrier();
           const f32x16 tot = total_scores<NSPLIT>(xch, sc, w, lane, TSOFT ? 2 : 0);
           f32x8 q0, q1;
-          uint32_t lmask = CAUSAL ? causal_mask(nslots - 1) : slot_mask(nslots - 1);
-          // (token-split, part 1: register r holds token t ^ 16)
-          if (TSOFT && part == 1) lmask = (lmask >> 16) | (lmask << 16);
+          const uint32_t lmask = own_mask(CAUSAL ? causal_mask(nslots - 1) : slot_mask(nslots - 1));
           softmax_slot(tot, lmask, st, scale_log2, q0, q1, lane, TSOFT);
           const LDS_AS float* ltab = (const LDS_AS float*)(ring + kFillRing * kSlotBytes) + last_pos * (4 * kTS);
           pv_load(ring + last_pos * kSlotBytes, tab, 0, va0);

@@ -138,6 +138,10 @@ CASES = {
     "mtp_t3_h32_fp8t": dict(seed=117, batch=4, heads=32, seqlens=[2, 35, 300, 999], tokens_per_seq=3,
                             kv_format="fp8_tensor"),
     "mtp_long_split_t2_h128": dict(seed=118, batch=1, heads=128, seqlens=[20000], tokens_per_seq=2),
+    # the hidden tail reaches back into the first of two or more slots (lengths 33, 40 with T = 16;
+    # 33 with T = 3), or into a slot before the last (65 with T = 3), at 128 and 384 query rows
+    "mtp_t16_h8_first_slot_masked": dict(seed=122, batch=4, heads=8, seqlens=[33, 40, 47, 64], tokens_per_seq=16),
+    "mtp_t3_h128_first_slot_masked": dict(seed=123, batch=3, heads=128, seqlens=[33, 34, 65], tokens_per_seq=3),
     "mtp_topk_t2_h64_fp8": dict(seed=119, batch=3, heads=64, seqlens=[3000, 800, 40], tokens_per_seq=2,
                                 kv_format="fp8", topk=512, topk_pad_max=60),
     "mtp_topk_t3_h128_bf16": dict(seed=120, batch=2, heads=128, seqlens=[2000, 300], tokens_per_seq=3, topk=256,
