@@ -24,6 +24,13 @@
 //    same sum in either wave), so all of them hold bit-identical scores and
 //    softmax state.  A wave keeps 144/NSPLIT query VGPRs and 256/NSPLIT
 //    accumulator AGPRs.
+//  * Token-split softmax (bf16 rows copied by the DMA, two parts): after a
+//    segment's first slot, each wave of a pair forms the scores and the
+//    softmax of its own 16 tokens only (half of the partner's partial read,
+//    8 exponentials per lane instead of 16), and the pair swaps bf16 P^T
+//    halves through LDS for the PV.  Both keep the reference the first slot
+//    fixed; each sums p over its own tokens, and the two sums are added
+//    once at the end.
 //  * Slabs: H = 128 runs as two 64-head workgroups per KV range, on one XCD,
 //    so the second reader of every KV line finds it in that XCD's L2.
 //  * KV streaming: 32-token slots of 36 KB in a 4-deep LDS ring filled by
@@ -36,7 +43,8 @@
 //    into O, the partial QK^T of slot s+1 runs on the matrix core; two more
 //    slots are in flight from HBM.  Two workgroup barriers per slot: one
 //    publishes the partial scores (and the landed slot), one frees the ring
-//    slot and the exchange buffer.
+//    slot and the exchange buffer (token-split: one publishes the P^T
+//    halves, and the next slot's first barrier frees the ring slot).
 //  * Split-KV: pages of all sequences are laid end to end and cut into equal
 //    ranges, one per workgroup and slab (a static form of the persistent
 //    scheduler the STAGE_D2 note describes under "Grid vs. Persistent Tile
