@@ -24,7 +24,8 @@
 //    same sum in either wave), so all of them hold bit-identical scores and
 //    softmax state.  A wave keeps 144/NSPLIT query VGPRs and 256/NSPLIT
 //    accumulator AGPRs.
-//  * Token-split softmax (bf16 rows copied by the DMA, two parts): after a
+//  * Token-split softmax (bf16 rows copied by the DMA, or per-tensor FP8
+//    rows through the register fill; two parts): after a
 //    segment's first slot, each wave of a pair forms the scores and the
 //    softmax of its own 16 tokens only (half of the partner's partial read,
 //    8 exponentials per lane instead of 16), and the pair swaps bf16 P^T
@@ -1101,7 +1102,7 @@ mla_decode_kernel(DecodeArgs a) {
   constexpr int NCB = kCB / NSPLIT;
   constexpr int HG = kWaves / NSPLIT;  // 32-head groups per workgroup
   constexpr bool TILED = kv_fp8(KVM);  // FP8 cache: tiled QK^T split, scales applied in fp32
-  // Token-split softmax (bf16 copy ring, two parts): after a
+  // Token-split softmax (bf16 copy ring or per-tensor FP8 fill, two parts): after a
   // segment's first slot, each wave of a pair takes the softmax of its own 16
   // tokens only and the pair swaps bf16 P^T halves before PV.  Part 1 reads
   // its K rows as 16..31, 0..15, so its own tokens sit in S^T registers 0..7
@@ -1111,7 +1112,9 @@ mla_decode_kernel(DecodeArgs a) {
   // (own_mask).  A row whose tokens in the first slot are all
   // masked sees none later in the segment either (the limit only falls
   // behind), so its reference stays -inf in both waves.
-  constexpr bool TSOFT = NSPLIT == 2 && KVM == kKvBf16;
+  // (dense caches without tile scales: a top-k slot 0 may be all padding
+  // while later slots are not, which would leave the two references apart)
+  constexpr bool TSOFT = NSPLIT == 2 && (KVM == kKvBf16 || KVM == kKvFp8T);
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -1456,17 +1459,46 @@ mla_decode_kernel(DecodeArgs a) {
           // slot s+3
           int p0 = 0, p1 = 1, p2 = 2;  // positions of slots s, s+1, s+2
           for (int s = 0; s + 1 < nslots; ++s) {
-            put_partial(xch, sc, w, lane);
+            // token-split: slot 0 as the copy ring's first slot, later
+            // slots with the half exchange and the P^T swap, whose barrier
+            // takes the place of the end-of-slot one
+            const bool half = TSOFT && s > 0;
+            if (half) put_partial_half(xch, sc, w, lane);
+            else put_partial(xch, sc, w, lane);
             wait_vm_lgkm0<63>();
             barrier();
             qk_preload<NSPLIT, TILED>(kb, pos_buf(p1), tab);
-            soft_read<NSPLIT>(sp, sctx);
+            if (half) soft_read_half(sp, sctx);
+            else soft_read<NSPLIT>(sp, sctx);
             __builtin_amdgcn_sched_barrier(0);
             QkSide side;
             side.pvbuf = pos_buf(p0);
             side.va0 = &va0;
             sp.own = sc;
-            if constexpr (kv_topk(KVM)) {
+            if constexpr (TSOFT) {
+              const bool masked = CAUSAL && s >= causal_from;
+              if (masked) sp.mask = own_mask(causal_mask(s));
+              if (half) {
+                if (masked)
+                  sc = qk_partial<NSPLIT, kPipeSoft | kPipeHalf | kPipeMask>(kb, pos_buf(p1), qf, tab, side, sp, st,
+                                                                            sctx);
+                else
+                  sc = qk_partial<NSPLIT, kPipeSoft | kPipeHalf>(kb, pos_buf(p1), qf, tab, side, sp, st, sctx);
+                const bf16x8 mine = __builtin_convertvector(sp.p0, bf16x8);
+                *(LDS_AS bf16x8*)(xch + (w * 4) * 64 + lane) = mine;
+                wait_vm_lgkm0<63>();
+                barrier();
+                po.b0[0] = mine;
+                po.b1[0] = *(const LDS_AS bf16x8*)(xch + ((w ^ 1) * 4) * 64 + lane);
+              } else {
+                if (masked)
+                  sc = qk_partial<NSPLIT, kPipeSoft | kPipeOwnL | kPipeMask>(kb, pos_buf(p1), qf, tab, side, sp, st,
+                                                                            sctx);
+                else
+                  sc = qk_partial<NSPLIT, kPipeSoft | kPipeOwnL>(kb, pos_buf(p1), qf, tab, side, sp, st, sctx);
+                make_pops<NSPLIT, TILED>(po, sp.p0, sp.p1, nullptr, part, lane);
+              }
+            } else if constexpr (kv_topk(KVM)) {
               sp.mask = slot_mask(s);
               sc = qk_partial<NSPLIT, kPipeSoft | kPipeMask, TILED>(kb, pos_buf(p1), qf, tab, side, sp, st, sctx,
                                                                    pos_tab(p1), part);
@@ -1478,7 +1510,7 @@ mla_decode_kernel(DecodeArgs a) {
               sc = qk_partial<NSPLIT, kPipeSoft, TILED>(kb, pos_buf(p1), qf, tab, side, sp, st, sctx, pos_tab(p1),
                                                         part);
             }
-            make_pops<NSPLIT, TILED>(po, sp.p0, sp.p1, pos_tab(p0), part, lane);
+            if constexpr (!TSOFT) make_pops<NSPLIT, TILED>(po, sp.p0, sp.p1, pos_tab(p0), part, lane);
             pv_slot<NSPLIT, TILED>(side.pvbuf, va0, po, tab, acc);
             fill_row<KVM>(pos_buf(p2), pos_tab(p2), rr, frow, fq);
             const int row = next_row;
@@ -1492,12 +1524,19 @@ mla_decode_kernel(DecodeArgs a) {
               next_row = fill_src(s + 4);
             }
             load_row<KVM>(rr, a, row, fq);
-            wait_vm_lgkm0<63>();  // this wave's LDS reads and writes are done
-            barrier();
+            if (!half) {
+              wait_vm_lgkm0<63>();  // this wave's LDS reads and writes are done
+              barrier();
+            }
             const int pn = p0;
             p0 = p1;
             p1 = p2;
             p2 = pn;
+          }
+          if constexpr (TSOFT) {
+            // the partner may still be reading this wave's P^T half
+            wait_vm_lgkm0<63>();
+            barrier();
           }
           put_partial(xch, sc, w, lane);
           wait_vm_lgkm0<63>();
