@@ -1,0 +1,529 @@
+// decode_ws.hip - the wave-specialised absorbed MLA decode for gfx950
+// (MI355X): paged bf16 caches, 64 query rows per workgroup.
+//
+// What is computed is the same as in decode.hip: for every query row (head)
+// of a sequence, scores against the shared 576-wide latent rows, a scaled
+// softmax per row, O = P.V with V the 512 latent columns, and the
+// natural-log LSE.
+//
+// Design.  A workgroup of eight waves, two per SIMD, holds one slab of 64
+// query rows of one sequence (the STAGE_D2 note's head-packed tile, "Strategy
+// A: Head-Packed M Dimension": every KV row is read once for all 64).  Waves
+// w and w+4 share a SIMD and have different jobs, so that one issues matrix
+// instructions while the other waits for LDS or runs its softmax:
+//  * score waves (0..3): wave q takes rows 32*(q&1) .. +31 and the token half
+//    (q>>1) of every 32-token slot, over the whole 576-wide reduction
+//    (v_mfma_f32_16x16x32_bf16: tokens on M, rows on N, the queries of its 32
+//    rows in 144 VGPRs).  With the full reduction in one wave no partial
+//    scores cross LDS; the wave forms its own exponentials and writes them as
+//    bf16 into a P tile in LDS.
+//  * value waves (4..7): wave 4+v owns output columns 128v .. +127 of all 64
+//    rows (v_mfma_f32_32x32x16_bf16: rows on M, columns on N, 128 fp32
+//    accumulators), reading P from the tile and V through transposing LDS
+//    reads; each V fragment serves both 32-row blocks.  They also issue the
+//    direct global->LDS copies of the KV slots.
+// One workgroup barrier per slot.  Between barriers B_i and B_i+1 the score
+// waves work on slot i, while the value waves multiply slot i-1 (its P was
+// written before B_i, its V fragments read into registers during i-1) and
+// copy slot i+3 into the ring position of slot i-1, which nobody reads after
+// B_i.  The ring holds four
+// 36 KB slots (three in flight); the P tile is double-buffered.
+// The two roles run their own copies of the segment and slot loops with the
+// same barrier sequence: the score waves' queries and the value waves'
+// accumulators are then never live in the same code, and each role fits the
+// 256 registers of a wave at two waves per SIMD.
+//
+// Softmax: base 2 against a fixed reference per row, the maximum of the
+// segment's first slot (the two token halves exchange their maxima once, in
+// LDS).  Later slots may rise above it by up to 16 (p <= 2^16, exact in fp32,
+// a relative rounding in bf16); if a row rises further the workgroup redoes
+// the segment with the true maxima.  O is never rescaled.
+//
+// Split-KV: the same plan as decode.hip (units of all sequences laid end to
+// end, cut into equal ranges); a piece of a split sequence writes its
+// normalised partial and base-2 LSE to the workspace for mla_merge_kernel.
+#include "decode_common.h"
+
+namespace mla {
+namespace {
+
+constexpr int kWsWaves = 8;
+constexpr int kWsThreads = 64 * kWsWaves;
+constexpr int kWsRows = 64;       // query rows per workgroup
+constexpr int kQk = kD / 32;      // 18 k-steps of 32 in the 576-wide reduction
+constexpr int kPRowBytes = 80;    // a row of the P tile: 32 bf16 + 16 bytes of pad
+constexpr int kPTile = kWsRows * kPRowBytes;
+constexpr int kKRead = 4;         // K fragments in flight ahead of their MFMA
+
+// s_waitcnt vmcnt(N) alone (LDS reads stay in flight), GFX9 encoding
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// vm operations of copy epoch e of an n-slot segment, per value wave: the
+// nine copies of slot e+3
+__device__ __forceinline__ int epoch_ops(int e, int n) { return e + 3 < n ? kDmaPerWave : 0; }
+
+// s_waitcnt vmcnt(k) lgkmcnt(0) for the counts epoch_ops can add up to
+// (anything else waits for everything, which is always safe)
+__device__ __forceinline__ void wait_ops_lgkm0(int k) {
+  if (k == 2 * kDmaPerWave) wait_vm_lgkm0<2 * kDmaPerWave>();
+  else if (k == kDmaPerWave) wait_vm_lgkm0<kDmaPerWave>();
+  else wait_vm_lgkm0<0>();
+}
+
+// The P tile: [row][position] bf16, 80-byte rows (the 16-byte reads of 16
+// consecutive rows then hit 16 distinct bank groups).  Position p of a
+// 16-token k-step holds token pi(p), pi swapping bits 2 and 3: the order in
+// which the transposing V reads hand a lane its eight tokens (lane half h:
+// tokens 4h .. 4h+3, then 8+4h .. 8+4h+3).  pi is its own inverse.
+
+// LDS address (slot-relative) of the K fragment of token half th for an
+// even (odd = 0) or odd k-step: row m = 16th + (lane & 15), 16-byte chunk
+// 4*odd + lane/16 of the k-step pair's column group, in the swizzled layout;
+// k-step g adds g/2 column groups.
+__device__ __forceinline__ uint32_t ws_kaddr(int th, int lane, int odd) {
+  const int m = 16 * th + (lane & 15);
+  const int c = 4 * odd + (lane >> 4);
+  return m * 128 + 16 * (c ^ row_swz(m));
+}
+
+// Transposing V reads of value wave v: for column block cb (columns
+// 128v + 32cb .. +31) and k-step ks (slot tokens 16ks .. +15) the two reads
+// give lane l column 128v + 32cb + l%32 of tokens pi(8h + e), h = l/32.
+// Within 16-lane group G lane 4j + q reads columns 16(G&1) + 4q .. +3 of row
+// 4(G>>1) + j (tt = 0) and of row 8 + 4(G>>1) + j (tt = 1).
+__device__ __forceinline__ uint32_t ws_vaddr(int v, int lane, int tt) {
+  const int G = lane >> 4, i = lane & 15, j = i >> 2, q = i & 3;
+  const int m = 8 * tt + 4 * (G >> 1) + j;
+  return kGroupBytes * (2 * v) + m * 128 + 16 * ((2 * (G & 1) + (q >> 1)) ^ row_swz(m)) + 8 * (q & 1);
+}
+
+typedef bf16x4 VFrag[4];  // [2 * ks + tt]
+
+__device__ __forceinline__ void ws_vload(const lds_char* buf, const uint32_t (&va)[2], int cb, VFrag& f) {
+  const uint32_t x = (cb & 1) ? 64u : 0u;  // odd 32-column block: chunk bit 2
+  const lds_char* p0 = buf + (va[0] ^ x) + kGroupBytes * (cb >> 1);
+  const lds_char* p1 = buf + (va[1] ^ x) + kGroupBytes * (cb >> 1);
+  f[0] = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((LDS_AS bf16x4*)p0);
+  f[1] = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((LDS_AS bf16x4*)p1);
+  f[2] = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((LDS_AS bf16x4*)(p0 + 16 * 128));
+  f[3] = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((LDS_AS bf16x4*)(p1 + 16 * 128));
+}
+
+// max / sum over lanes l, l^16, l^32, l^48: the four token groups of one row
+// in a 16x16 score fragment
+__device__ __forceinline__ float max_rows4(float v) {
+  auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float sum_rows4(float v) {
+  auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+  r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// Score wave, QK^T of one slot: S^T[16 tokens][32 rows] as two 16x16
+// fragments; lane l, register e: token 4(l/16) + e of the wave's half, row
+// 16j + l%16 of its block.
+__device__ __forceinline__ void ws_scores(const lds_char* buf, const uint32_t (&ka)[2], const bf16x8 (&qf)[kQk][2],
+                                          f32x4 (&s)[2]) {
+  bf16x8 kb[kKRead];
+#pragma unroll
+  for (int g = 0; g < kKRead - 1; ++g) kb[g] = *(const LDS_AS bf16x8*)(buf + ka[g & 1] + kGroupBytes * (g >> 1));
+#pragma unroll
+  for (int g = 0; g < kQk; ++g) {
+    constexpr int A = kKRead - 1;
+    // (a scheduling fence per k-step keeps each read kKRead - 1 steps ahead
+    // of its MFMAs instead of letting the scheduler sink it next to them)
+    __builtin_amdgcn_sched_barrier(0);
+    if (g + A < kQk) kb[(g + A) % kKRead] = *(const LDS_AS bf16x8*)(buf + ka[(g + A) & 1] + kGroupBytes * ((g + A) >> 1));
+    s[0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kb[g % kKRead], qf[g][0], g == 0 ? f32x4{} : s[0], 0, 0, 0);
+    s[1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kb[g % kKRead], qf[g][1], g == 0 ? f32x4{} : s[1], 0, 0, 0);
+  }
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+// LDS shared by the two roles.
+struct WsLds {
+  lds_char* ring;    // KV ring, kRing slots
+  lds_char* ptile;   // two P tiles
+  LDS_AS float* xref;  // [half][row]: first-slot maxima
+  LDS_AS float* xl;    // [half][row]: sums of p
+  LDS_AS float* xm;    // [half][row]: largest scores seen (base 2)
+  LDS_AS int* votes;   // [score wave]: redo votes
+};
+
+// One segment of the range: sequence b, tokens [tok0, tok1).
+struct WsSeg {
+  int b;
+  SegCtx sg;
+  int seglen;
+  int first_r, nsplit;
+};
+
+// Calls body(seg) for every segment of the range, in order, with a barrier
+// between segments (every wave is done with the ring and the exchanges).
+template <class F>
+__device__ __forceinline__ void for_segments(const DecodeArgs& a, const Plan& pl, F&& body) {
+  int b = pl.b0, p = pl.p0;
+  bool first = true;
+  while (true) {
+    const int n = units_of(a, b);
+    const int gs = max(pl.start, p), ge = min(pl.end, p + n);
+    if (gs < ge) {
+      if (!first) {
+        wait_vm_lgkm0<0>();
+        barrier();
+      }
+      first = false;
+      WsSeg s;
+      s.b = b;
+      s.seglen = min(max(a.seqlens[b], 0), a.max_pages * kPage);
+      s.sg.tok0 = (gs - p) * kPage;
+      s.sg.tok1 = min((ge - p) * kPage, s.seglen);
+      s.sg.nslots = (s.sg.tok1 - s.sg.tok0 + kTS - 1) / kTS;
+      s.sg.npages = (s.sg.nslots + 1) / 2;
+      s.sg.bt_seg = a.block_table + (size_t)b * a.max_pages + (gs - p);
+      s.sg.idx_seg = nullptr;
+      s.first_r = p / pl.C;
+      s.nsplit = (p + n - 1) / pl.C - s.first_r + 1;
+      body(s);
+    }
+    p += n;
+    ++b;
+    if (p >= pl.end || b >= a.batch) break;
+  }
+}
+
+// ---------------------------------------------------------------- score waves
+
+template <bool Q_FP8, bool CAUSAL>
+__device__ __forceinline__ void score_role(const DecodeArgs& a, const Plan& pl, const WsLds& L, int w, int lane,
+                                           int row0, int r) {
+  // (lane and wave pass through empty asm statements: nothing computed from
+  // them can be hoisted above the role split, where it would stay live in the
+  // other role's code too)
+  asm volatile("" : "+v"(lane), "+s"(w));
+  const int hb = w & 1, th = w >> 1;
+  const int i16 = lane & 15, g4 = lane >> 4;
+  const float scale_log2 = a.scale_log2;
+  int qrow[2], lag[2] = {0, 0};
+  bool qok[2];
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    qrow[j] = row0 + 32 * hb + 16 * j + i16;
+    qok[j] = qrow[j] < a.heads;
+    if constexpr (CAUSAL) lag[j] = a.tq - 1 - min(qrow[j], a.heads - 1) / a.heads_tok;
+  }
+  const uint32_t ka[2] = {ws_kaddr(th, lane, 0), ws_kaddr(th, lane, 1)};
+  // this lane's four p of block j: row 32hb + 16j + i16 of the P tile,
+  // positions 16th + 4*pi-group(lane / 16) .. +3
+  const int g4p = ((g4 & 1) << 1) | (g4 >> 1);
+  uint32_t pw[2];
+#pragma unroll
+  for (int j = 0; j < 2; ++j) pw[j] = (32 * hb + 16 * j + i16) * kPRowBytes + (16 * th + 4 * g4p) * 2;
+  const int xrow = 32 * hb + i16;  // + 16j: this lane's rows in the exchange arrays
+
+  for_segments(a, pl, [&](const WsSeg& sgm) {
+    const int b = sgm.b;
+    const int nslots = sgm.sg.nslots;
+    int lim[2];
+#pragma unroll
+    for (int j = 0; j < 2; ++j) lim[j] = CAUSAL ? min(sgm.sg.tok1, sgm.seglen - lag[j]) : sgm.sg.tok1;
+    const int lim_lo = min(lim[0], lim[1]);
+
+    // queries (B operand): row qrow[j], columns 32k + 8(lane/16) .. +7
+    bf16x8 qf[kQk][2];
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int rr = qok[j] ? qrow[j] : 0;
+      if constexpr (!Q_FP8) {
+        const bf16x8* qp = (const bf16x8*)((const __bf16*)a.q + ((size_t)b * a.heads + rr) * kD);
+#pragma unroll
+        for (int k = 0; k < kQk; ++k) {
+          const bf16x8 x = qp[4 * k + g4];
+          qf[k][j] = qok[j] ? x : bf16x8{};
+        }
+      } else {
+        const uint2* qp = (const uint2*)((const uint8_t*)a.q + ((size_t)b * a.heads + rr) * kD);
+#pragma unroll
+        for (int k = 0; k < kQk; ++k) {
+          const uint2 x = qp[4 * k + g4];
+          qf[k][j] = qok[j] ? fp8x8_to_bf16(x, a.q_descale) : bf16x8{};
+        }
+      }
+    }
+    wait_vm_lgkm0<0>();
+
+    float ref[2] = {-INFINITY, -INFINITY};  // base-2 reference per row
+    for (int pass = 0; pass < 2; ++pass) {
+      float lsum[2] = {0.0f, 0.0f};
+      float mraw[2] = {-INFINITY, -INFINITY};  // largest raw score seen
+      barrier();  // B_0: slot 0 landed
+      for (int it = 0; it <= nslots; ++it) {
+        if (it < nslots) {
+          const lds_char* buf = L.ring + (it & (kRing - 1)) * kSlotBytes;
+          f32x4 s[2];
+          // the score MFMAs go first on the SIMD's matrix core; the value
+          // wave's MFMAs then fill the time of this wave's softmax
+          __builtin_amdgcn_s_setprio(1);
+          ws_scores(buf, ka, qf, s);
+          __builtin_amdgcn_s_setprio(0);
+          const int tk = sgm.sg.tok0 + it * kTS + 16 * th + 4 * g4;  // this lane's first token
+          if (sgm.sg.tok0 + it * kTS + kTS > lim_lo) {
+#pragma unroll
+            for (int j = 0; j < 2; ++j)
+#pragma unroll
+              for (int e = 0; e < 4; ++e) s[j][e] = tk + e < lim[j] ? s[j][e] : -INFINITY;
+          }
+#pragma unroll
+          for (int j = 0; j < 2; ++j) mraw[j] = fmaxf(mraw[j], fmaxf(fmaxf(s[j][0], s[j][1]), fmaxf(s[j][2], s[j][3])));
+          if (pass == 0 && it == 0) {
+            // the first slot fixes the reference: the max over both token halves
+            float mx[2];
+#pragma unroll
+            for (int j = 0; j < 2; ++j) mx[j] = max_rows4(mraw[j]);
+            if (g4 == 0) {
+#pragma unroll
+              for (int j = 0; j < 2; ++j) L.xref[th * 64 + xrow + 16 * j] = mx[j];
+            }
+            wait_vm_lgkm0<0>();
+            barrier();
+#pragma unroll
+            for (int j = 0; j < 2; ++j) ref[j] = fmaxf(mx[j], L.xref[(th ^ 1) * 64 + xrow + 16 * j]) * scale_log2;
+          }
+#pragma unroll
+          for (int j = 0; j < 2; ++j) {
+            const float nref = neg_ref(ref[j]);
+            f32x4 pj;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) pj[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[j][e], scale_log2, nref));
+            lsum[j] += (pj[0] + pj[1]) + (pj[2] + pj[3]);
+            *(LDS_AS bf16x4*)(L.ptile + (it & 1) * kPTile + pw[j]) = __builtin_convertvector(pj, bf16x4);
+          }
+          wait_vm_lgkm0<0>();
+        }
+        barrier();  // B_it+1
+      }
+      // end of the pass: row sums, largest scores, redo vote
+      bool up = false;
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const float l = sum_rows4(lsum[j]);
+        const float m = max_rows4(mraw[j]);
+        const float ms = m == -INFINITY ? -INFINITY : m * scale_log2;
+        up |= ms > ref[j] + kTau;
+        if (g4 == 0) {
+          L.xl[th * 64 + xrow + 16 * j] = l;
+          L.xm[th * 64 + xrow + 16 * j] = ms;
+        }
+      }
+      const bool vote = __any(up);
+      if (lane == 0) L.votes[w] = vote ? 1 : 0;
+      wait_vm_lgkm0<0>();
+      barrier();
+      const int votes = L.votes[0] | L.votes[1] | L.votes[2] | L.votes[3];
+      if (__builtin_amdgcn_readfirstlane(votes) == 0) {
+        // LSE of rows 32hb + 16j + i16 (token half 0 writes it)
+        if (th == 0 && g4 == 0) {
+          const size_t pslot = (size_t)(b + r);
+#pragma unroll
+          for (int j = 0; j < 2; ++j) {
+            const int lr = xrow + 16 * j;
+            const float lt = L.xl[lr] + L.xl[64 + lr];
+            const float lse2 = lt > 0.0f ? ref[j] + __builtin_amdgcn_logf(lt) : -INFINITY;
+            if (qok[j]) {
+              if (sgm.nsplit == 1) a.lse[(size_t)b * a.heads + qrow[j]] = lse2 * kLn2;
+              else a.ws_lse[pslot * a.heads + qrow[j]] = lse2;
+            }
+          }
+        }
+        if (w == 0 && lane == 0) a.ws_seq[b] = int2{b + sgm.first_r, sgm.nsplit};
+        break;
+      }
+      // redo with the true maxima (then p <= 1)
+#pragma unroll
+      for (int j = 0; j < 2; ++j) ref[j] = fmaxf(L.xm[xrow + 16 * j], L.xm[64 + xrow + 16 * j]);
+      wait_vm_lgkm0<0>();
+      barrier();  // every wave has read the votes
+    }
+  });
+}
+
+// ---------------------------------------------------------------- value waves
+
+__device__ __forceinline__ void value_role(const DecodeArgs& a, const Plan& pl, const WsLds& L, int v, int lane,
+                                           int row0, int r) {
+  asm volatile("" : "+v"(lane), "+s"(v));  // (as in score_role)
+  const int i32 = lane & 31, h2 = lane >> 5;
+  // P fragment (A operand) of row block rb, k-step ks: row 32rb + i32 of the
+  // tile, positions 16ks + 8h2 .. +7
+  const uint32_t prd = i32 * kPRowBytes + 16 * h2;
+  const uint32_t va[2] = {ws_vaddr(v, lane, 0), ws_vaddr(v, lane, 1)};
+  const uint32_t dma_off = dma_lane_off(lane, v, kTS);
+
+  for_segments(a, pl, [&](const WsSeg& sgm) {
+    const int b = sgm.b;
+    const SegCtx& sg = sgm.sg;
+    const int nslots = sg.nslots;
+    PageCache pc;
+    page_cache_load(pc, sg.bt_seg, 0, sg.npages, lane);
+    for (int pass = 0; pass < 2; ++pass) {
+      f32x16 o[2][4];
+#pragma unroll
+      for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+        for (int cb = 0; cb < 4; ++cb) o[rb][cb] = f32x16{};
+      // copy epochs -3 .. -1 (the prologue): slots 0 .. 2; slot 0 landed
+      const int pre = min(nslots, 3);
+      for (int s = 0; s < pre; ++s) dma_issue_all(prep_slot(s, s, L.ring, a, sg, pc, dma_off, v, lane));
+      wait_ops_lgkm0(epoch_ops(-2, nslots) + epoch_ops(-1, nslots));
+      barrier();  // B_0
+      VFrag vx[4], vy[4];
+      // iteration it (between B_it and B_it+1): epoch it issues the copies of
+      // slot it+3 (into the ring position of slot it-1, whose last reads were
+      // in iteration it-1); PV of slot it-1 from vc, while the V fragments of
+      // slot it (landed before B_it) are read into vn for the next iteration
+      auto iteration = [&](int it, VFrag (&vc)[4], VFrag (&vn)[4]) {
+        if (it + 3 < nslots) dma_issue_all(prep_slot(it + 3, it + 3, L.ring, a, sg, pc, dma_off, v, lane));
+        const lds_char* nbuf = L.ring + (it & (kRing - 1)) * kSlotBytes;
+        if (it >= 1) {
+          const lds_char* pt = L.ptile + ((it - 1) & 1) * kPTile;
+          bf16x8 pf[2][2];
+#pragma unroll
+          for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+            for (int ks = 0; ks < 2; ++ks) pf[rb][ks] = *(const LDS_AS bf16x8*)(pt + prd + rb * 32 * kPRowBytes + 32 * ks);
+#pragma unroll
+          for (int cb = 0; cb < 4; ++cb) {
+            const bf16x8 v0 = __builtin_shufflevector(vc[cb][0], vc[cb][1], 0, 1, 2, 3, 4, 5, 6, 7);
+            const bf16x8 v1 = __builtin_shufflevector(vc[cb][2], vc[cb][3], 0, 1, 2, 3, 4, 5, 6, 7);
+#pragma unroll
+            for (int rb = 0; rb < 2; ++rb) {
+              o[rb][cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pf[rb][0], v0, o[rb][cb], 0, 0, 0);
+              o[rb][cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pf[rb][1], v1, o[rb][cb], 0, 0, 0);
+            }
+            if (it < nslots) ws_vload(nbuf, va, cb, vn[cb]);
+          }
+        } else if (it < nslots) {
+#pragma unroll
+          for (int cb = 0; cb < 4; ++cb) ws_vload(nbuf, va, cb, vn[cb]);
+        }
+        if (pass == 0 && it == 0) barrier();  // the score waves' reference exchange
+        // slot it+1 landed (the operations of epochs it-1 and it may stay in
+        // flight), and this wave's LDS reads of slot it are done before the
+        // next iteration's copies refill the ring position of slot it-1
+        wait_ops_lgkm0(epoch_ops(it - 1, nslots) + epoch_ops(it, nslots));
+        barrier();  // B_it+1
+      };
+      for (int it = 0; it <= nslots; it += 2) {
+        iteration(it, vy, vx);
+        if (it + 1 <= nslots) iteration(it + 1, vx, vy);
+      }
+      barrier();  // the score waves' sums and votes
+      const int votes = L.votes[0] | L.votes[1] | L.votes[2] | L.votes[3];
+      if (__builtin_amdgcn_readfirstlane(votes) == 0) {
+        // normalise and store this wave's 128 columns of the 64 rows.  The
+        // lane index is passed through an empty asm so that the compiler
+        // cannot hoist these per-lane store addresses out of the slot loop
+        // (they would hold ~70 registers across it).
+        int ln = lane;
+        asm volatile("" : "+v"(ln));
+        const int i32 = ln & 31, h2 = ln >> 5;
+        const size_t pslot = (size_t)(b + r);
+#pragma unroll
+        for (int rb = 0; rb < 2; ++rb) {
+#pragma unroll
+          for (int r4 = 0; r4 < 4; ++r4) {
+            // accumulator registers 4r4 + e: rows 32rb + 8r4 + 4h2 + e
+            const int lr = 32 * rb + 8 * r4 + 4 * h2;
+            const f32x4 l0 = *(const LDS_AS f32x4*)(L.xl + lr);
+            const f32x4 l1 = *(const LDS_AS f32x4*)(L.xl + 64 + lr);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const float lt = l0[e] + l1[e];
+              const float inv = lt > 0.0f ? 1.0f / lt : 0.0f;
+              const int row = row0 + lr + e;
+              if (row < a.heads) {
+#pragma unroll
+                for (int cb = 0; cb < 4; ++cb) {
+                  const int col = 128 * v + 32 * cb + i32;
+                  const float val = o[rb][cb][4 * r4 + e] * inv;
+                  if (sgm.nsplit == 1) ((__bf16*)a.out)[((size_t)b * a.heads + row) * kDV + col] = (__bf16)val;
+                  else a.ws_o[(pslot * a.heads + row) * kDV + col] = val;
+                }
+              }
+            }
+          }
+        }
+        break;
+      }
+      if (sg.npages > 64) page_cache_load(pc, sg.bt_seg, 0, sg.npages, lane);
+      wait_vm_lgkm0<0>();
+      barrier();  // every wave has read the votes
+    }
+  });
+}
+
+template <bool Q_FP8, bool CAUSAL>
+__global__ void __attribute__((amdgpu_flat_work_group_size(kWsThreads, kWsThreads), amdgpu_waves_per_eu(2, 2)))
+mla_decode_ws_kernel(DecodeArgs a) {
+  __shared__ __attribute__((aligned(1024))) char ring_mem[kRing * kSlotBytes];  // KV ring, 4 x 36 KB
+  __shared__ __attribute__((aligned(16))) char ptile_mem[2 * kPTile];           // P tiles, 2 x 5 KB
+  __shared__ __attribute__((aligned(16))) float xs[512];                        // row exchanges, votes
+  WsLds L;
+  L.ring = (lds_char*)ring_mem;
+  L.ptile = (lds_char*)ptile_mem;
+  L.xref = (LDS_AS float*)xs;
+  L.xl = (LDS_AS float*)xs + 128;
+  L.xm = (LDS_AS float*)xs + 256;
+  L.votes = (LDS_AS int*)xs + 384;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int g = blockIdx.x;
+  // XCD-aware mapping, as in decode.hip: workgroup g runs on XCD g % 8, which
+  // gets a run of consecutive ranges with all their slabs
+  const int idx = g / 8;
+  const int r = (g % 8) * a.per_xcd + idx / a.slabs;
+  const int slab = idx % a.slabs;
+  Plan pl;
+  const bool has_work = r < a.ranges && make_plan<kWsThreads>(a, r, (int*)ring_mem, pl);
+  // sequences with nothing to attend: O = 0, LSE = -inf
+  for (int b = g; b < a.batch; b += gridDim.x) {
+    if (units_of(a, b) == 0) {
+      for (int i = tid; i < a.heads * (kDV / 4); i += kWsThreads)
+        *(bf16x4*)((__bf16*)a.out + ((size_t)b * a.heads) * kDV + 4 * i) = bf16x4{};
+      for (int i = tid; i < a.heads; i += kWsThreads) a.lse[(size_t)b * a.heads + i] = -INFINITY;
+      if (tid == 0) a.ws_seq[b] = int2{0, 0};
+    }
+  }
+  if (!has_work) return;
+  const int row0 = slab * kWsRows;
+  if (w < 4) score_role<Q_FP8, CAUSAL>(a, pl, L, w, lane, row0, r);
+  else value_role(a, pl, L, w - 4, lane, row0, r);
+}
+
+}  // namespace
+
+bool decode_ws_supported(int32_t kv_format, int32_t topk, int32_t eff_heads) {
+  return kv_format == kKvFormatBf16 && topk == 0 && eff_heads >= kWsRows;
+}
+
+hipError_t launch_decode_ws(const DecodeArgs& a, bool q_fp8, bool causal, hipStream_t stream) {
+  const dim3 grid(a.per_xcd * 8 * a.slabs), block(kWsThreads);
+  if (!q_fp8 && !causal) hipLaunchKernelGGL((mla_decode_ws_kernel<false, false>), grid, block, 0, stream, a);
+  if (!q_fp8 && causal) hipLaunchKernelGGL((mla_decode_ws_kernel<false, true>), grid, block, 0, stream, a);
+  if (q_fp8 && !causal) hipLaunchKernelGGL((mla_decode_ws_kernel<true, false>), grid, block, 0, stream, a);
+  if (q_fp8 && causal) hipLaunchKernelGGL((mla_decode_ws_kernel<true, true>), grid, block, 0, stream, a);
+  return hipGetLastError();
+}
+
+}  // namespace mla

@@ -27,6 +27,31 @@ struct DecodeLaunch {
   int32_t ranges;  // KV ranges of the split-KV decode (workgroups per head slab)
 };
 
+// The decode kernels' argument block (device pointers and sizes, set up by
+// launch_decode).
+struct DecodeArgs {
+  const void* q;
+  const char* kv;
+  const int32_t* block_table;
+  const int32_t* seqlens;
+  const int32_t* topk_idx;
+  const float* kv_scales;
+  void* out;
+  float* lse;
+  float* ws_o;    // [(ranges + B) slots][H][512] normalised partial O, fp32
+  float* ws_lse;  // [(ranges + B)][H] base-2 LSE of partials
+  int2* ws_seq;   // [B] {workspace slot of piece 0, pieces}; pieces 0: nothing to attend
+  int32_t topk_tq;           // top-k: lists per sequence (T); list b belongs to sequence b / T
+  int32_t batch, heads, num_pages, max_pages, topk;
+  int32_t tq;         // dense, several query tokens: T (rows of a sequence = T x heads_tok), else 1
+  int32_t heads_tok;  // query heads per token
+  int32_t ranges;    // KV ranges (workgroups per head slab)
+  int32_t slabs;     // head slabs per range
+  int32_t per_xcd;   // ranges per XCD in the block -> (range, slab) mapping
+  float scale_log2;  // softmax_scale * log2(e)
+  float q_descale;
+};
+
 // Cache layouts of a decode launch.
 constexpr int32_t kKvFormatBf16 = 0;       // bf16 rows of 576
 constexpr int32_t kKvFormatFp8Tile = 1;    // 512 e4m3 codes + 64 bf16 rope, fp32 scale per 128 columns
@@ -42,6 +67,10 @@ size_t decode_workspace_bytes(int32_t ranges, int32_t batch, int32_t heads, int3
 // Clear the per-sequence piece records of a decode workspace (optional: every call rewrites them).
 hipError_t init_decode_workspace(void* workspace, int32_t batch, int32_t heads, hipStream_t stream);
 hipError_t launch_decode(const DecodeLaunch& d, hipStream_t stream);
+// The wave-specialised decode (decode_ws.hip): bf16 paged caches, dense,
+// at least 64 query rows per sequence.
+bool decode_ws_supported(int32_t kv_format, int32_t topk, int32_t eff_heads);
+hipError_t launch_decode_ws(const DecodeArgs& a, bool q_fp8, bool causal, hipStream_t stream);
 
 struct QueryLaunch {
   const void* qkv;
