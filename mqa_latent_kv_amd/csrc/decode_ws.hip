@@ -366,7 +366,14 @@ __device__ __forceinline__ void value_role(const DecodeArgs& a, const Plan& pl, 
   // tile, positions 16ks + 8h2 .. +7
   const uint32_t prd = i32 * kPRowBytes + 16 * h2;
   const uint32_t va[2] = {ws_vaddr(v, lane, 0), ws_vaddr(v, lane, 1)};
-  const uint32_t dma_off = dma_lane_off(lane, v, kTS);
+  // copies: this wave takes column groups 2v and 2v+1 of all 32 rows (the V
+  // columns it multiplies) and rows 8v .. 8v+7 of the rope group 8, nine
+  // copies of 1 KB per slot
+  uint32_t dfull[4];
+#pragma unroll
+  for (int rb = 0; rb < 4; ++rb) dfull[rb] = dma_lane_off(lane, rb, kTS);
+  const uint32_t dfull_r = dma_lane_off(lane, v, kTS);
+
 
   for_segments(a, pl, [&](const WsSeg& sgm) {
     const int b = sgm.b;
@@ -374,6 +381,33 @@ __device__ __forceinline__ void value_role(const DecodeArgs& a, const Plan& pl, 
     const int nslots = sg.nslots;
     PageCache pc;
     page_cache_load(pc, sg.bt_seg, 0, sg.npages, lane);
+    // this wave's copies of slot s into ring position pos (s < nslots)
+    auto dma_cols = [&](int s, int pos) {
+      const int page = page_of(pc, sg.bt_seg, s >> 1, sg.npages, lane, a.num_pages);
+      const char* src = a.kv + ((size_t)page * kPage + (s & 1) * kTS) * kRowBytes;
+      const int nvalid = min(kTS, sg.tok1 - (sg.tok0 + s * kTS));
+      uint32_t off[4], offr;
+      if (nvalid >= kTS) {
+#pragma unroll
+        for (int rb = 0; rb < 4; ++rb) off[rb] = dfull[rb];
+        offr = dfull_r;
+      } else {
+        // rows at and beyond the valid count re-read the last valid row
+#pragma unroll
+        for (int rb = 0; rb < 4; ++rb) off[rb] = dma_lane_off(lane, rb, nvalid - 1);
+        offr = dma_lane_off(lane, v, nvalid - 1);
+      }
+      const char* s0 = uniform_ptr(src + 256 * v);  // column group 2v
+      const char* s8 = uniform_ptr(src + 8 * 128);  // the rope group
+      const uint32_t base = __builtin_amdgcn_readfirstlane(lds_addr(L.ring + (pos & (kRing - 1)) * kSlotBytes));
+#pragma unroll
+      for (int rb = 0; rb < 4; ++rb) {
+        // (the immediate offset moves the source and the destination alike)
+        dma16<0>(s0, off[rb], base + (2 * v) * kGroupBytes + rb * 1024);
+        dma16<128>(s0, off[rb], base + (2 * v + 1) * kGroupBytes + rb * 1024 - 128);
+      }
+      dma16<0>(s8, offr, base + 8 * kGroupBytes + v * 1024);
+    };
     for (int pass = 0; pass < 2; ++pass) {
       f32x16 o[2][4];
 #pragma unroll
@@ -382,7 +416,7 @@ __device__ __forceinline__ void value_role(const DecodeArgs& a, const Plan& pl, 
         for (int cb = 0; cb < 4; ++cb) o[rb][cb] = f32x16{};
       // copy epochs -3 .. -1 (the prologue): slots 0 .. 2; slot 0 landed
       const int pre = min(nslots, 3);
-      for (int s = 0; s < pre; ++s) dma_issue_all(prep_slot(s, s, L.ring, a, sg, pc, dma_off, v, lane));
+      for (int s = 0; s < pre; ++s) dma_cols(s, s);
       wait_ops_lgkm0(epoch_ops(-2, nslots) + epoch_ops(-1, nslots));
       barrier();  // B_0
       VFrag vx[4], vy[4];
@@ -391,7 +425,7 @@ __device__ __forceinline__ void value_role(const DecodeArgs& a, const Plan& pl, 
       // in iteration it-1); PV of slot it-1 from vc, while the V fragments of
       // slot it (landed before B_it) are read into vn for the next iteration
       auto iteration = [&](int it, VFrag (&vc)[4], VFrag (&vn)[4]) {
-        if (it + 3 < nslots) dma_issue_all(prep_slot(it + 3, it + 3, L.ring, a, sg, pc, dma_off, v, lane));
+        if (it + 3 < nslots) dma_cols(it + 3, it + 3);
         const lds_char* nbuf = L.ring + (it & (kRing - 1)) * kSlotBytes;
         if (it >= 1) {
           const lds_char* pt = L.ptile + ((it - 1) & 1) * kPTile;
