@@ -41,7 +41,8 @@
  *  - Every data pointer is device memory owned by the caller.  The library
  *    keeps no per-call state and allocates no device memory in these calls;
  *    scratch space is the caller's `workspace`, sized by the *_workspace_size
- *    call.  Host structs are read during the call only.
+ *    call, except in mla_decode_noalloc, which uses a library-owned static
+ *    device array instead.  Host structs are read during the call only.
  *  - Calls are asynchronous on `stream` (a hipStream_t; NULL = the legacy
  *    default stream) and may be issued from several host threads on different
  *    streams.  Two calls that share a workspace must be ordered on one stream.
@@ -72,6 +73,7 @@ extern "C" {
 #define MLA_ERR_WORKSPACE (-3)    /* workspace NULL or smaller than required */
 #define MLA_ERR_LAUNCH (-4)       /* a kernel launch failed (hipGetLastError) */
 #define MLA_ERR_DEVICE (-5)       /* no usable HIP device / device query failed */
+#define MLA_ERR_SCRATCH_LIMIT (-6) /* mla_decode_noalloc: the problem needs more than MLA_DECODE_SCRATCH_BYTES */
 
 /* ---- element types ---- */
 #define MLA_DTYPE_BF16 1
@@ -92,6 +94,8 @@ extern "C" {
 #define MLA_MAX_TOKENS_PER_SEQ 16
 #define MLA_MAX_HEADS 128
 #define MLA_MAX_BATCH 8192
+/* Size of the library-owned decode scratch of mla_decode_noalloc (64 MiB per GPU). */
+#define MLA_DECODE_SCRATCH_BYTES ((size_t)64 << 20)
 
 typedef struct mla_decode_params {
   int32_t batch;             /* B >= 1, <= MLA_MAX_BATCH */
@@ -167,6 +171,31 @@ int32_t mla_decode(const mla_decode_params* p, const void* q, const void* kv_cac
                    const int32_t* block_table, const int32_t* seqlens,
                    const int32_t* topk_idx, const float* kv_scales, void* out,
                    float* lse, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * mla_decode for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc): the
+ * same operation, arguments and kernels, with the scratch taken from a
+ * library-owned static device array of MLA_DECODE_SCRATCH_BYTES instead of a
+ * workspace argument.  Each GPU the library runs on holds its own copy of
+ * that array from the library's first use there until the process ends; its
+ * address is looked up on this entry point's first call on a device.
+ *
+ * Returns MLA_ERR_SCRATCH_LIMIT, launching nothing, when
+ * mla_decode_workspace_size(p) exceeds MLA_DECODE_SCRATCH_BYTES (the dense
+ * 64 x 128-head, 4096-token decode needs about 50 MB).  Calls no hipMalloc,
+ * hipFree or allocating library routine.
+ *
+ * Every call on a GPU shares that GPU's array, which keeps what the last call
+ * left (no call relies on its contents at entry: the decode rewrites every
+ * record it reads back).  Calls that overlap on one GPU (on different
+ * streams, or from host threads without ordering) race on it and give wrong
+ * results: order them on one stream.
+ */
+int32_t mla_decode_noalloc(const mla_decode_params* p, const void* q, const void* kv_cache,
+                           const int32_t* block_table, const int32_t* seqlens,
+                           const int32_t* topk_idx, const float* kv_scales, void* out,
+                           float* lse, void* stream);
 
 typedef struct mla_query_params {
   int32_t batch;       /* tokens B >= 1, <= MLA_MAX_BATCH */

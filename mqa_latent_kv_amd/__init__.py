@@ -11,6 +11,7 @@ Entry points (same names as the C ABI):
                out=None, lse=None, ...)
     mla_query(qkv, w_qa, w_qb, w_uk, q_scale_inv, out=None, ...)
     mla_kv_insert(qkv, w_kva, slots, k_scale_inv, kv_cache, ...)
+    mla_decode_noalloc(q, kv_cache, block_table, seqlens, ...)  (library-owned scratch)
     mla_decode_workspace_size(params), mla_decode_workspace_init(params, ws),
     mla_query_workspace_size(params)
     mla_status_string(code), mla_version()
@@ -26,6 +27,8 @@ LIB_PATH = os.path.join(_HERE, "libmla.so")
 MLA_DTYPE_BF16 = 1
 MLA_DTYPE_FP8_E4M3 = 2
 MLA_DTYPE_FP8_E4M3_TENSOR = 3
+MLA_ERR_SCRATCH_LIMIT = -6
+DECODE_SCRATCH_BYTES = 64 << 20
 D_QK = 576
 D_V = 512
 PAGE_SIZE = 64
@@ -93,6 +96,8 @@ def lib() -> ctypes.CDLL:
         L.mla_decode_workspace_init.argtypes = [ctypes.POINTER(DecodeParams), vp, sz, vp]
         L.mla_decode.restype = i32
         L.mla_decode.argtypes = [ctypes.POINTER(DecodeParams), vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+        L.mla_decode_noalloc.restype = i32
+        L.mla_decode_noalloc.argtypes = [ctypes.POINTER(DecodeParams), vp, vp, vp, vp, vp, vp, vp, vp, vp]
         L.mla_query_workspace_size.restype = i32
         L.mla_query_workspace_size.argtypes = [ctypes.POINTER(QueryParams), ctypes.POINTER(sz)]
         L.mla_query.restype = i32
@@ -173,18 +178,8 @@ def decode_workspace(params: DecodeParams, device="cuda", stream=None):
     return ws
 
 
-def mla_decode(q, kv_cache, block_table, seqlens, topk_idx=None, kv_scales=None, out=None, lse=None, *,
-               softmax_scale=192.0**-0.5, q_descale=1.0, workspace=None, stream=None):
-    """Absorbed MLA decode (see include/mla.h).
-
-    q: [B, H, 576] (one query token per sequence) or [B, T, H, 576] (T new
-    tokens, causal), torch.bfloat16, or uint8 / float8_e4m3fn codes.
-    kv_cache: bf16 [P, 64, 576]; or uint8 [P, 64, 640] FP8 rows (then kv_scales
-    float32 [P, 64, 4]); or uint8 [P, 64, 576] per-tensor FP8 rows (then
-    kv_scales the float32 [1] k_scale_inv).  block_table int32 [B, max_pages], seqlens int32 [B],
-    topk_idx int32 [B, topk] ([B, T, topk] for T tokens) or None.  Returns (out bf16 [B, H, 512], lse
-    fp32 [B, H]), or [B, T, H, 512] and [B, T, H] for a 4-D q.
-    """
+def _decode_call(q, kv_cache, block_table, seqlens, topk_idx, kv_scales, out, lse, softmax_scale, q_descale):
+    """Check the tensors of a decode call; returns (params, out, lse)."""
     import torch
 
     _expect(q, "q", (torch.bfloat16, torch.uint8, torch.float8_e4m3fn))
@@ -238,6 +233,26 @@ def mla_decode(q, kv_cache, block_table, seqlens, topk_idx=None, kv_scales=None,
     params = decode_params(batch=B, heads=H, num_pages=P, max_pages_per_seq=block_table.shape[1], topk=topk,
                            q_fp8=q_fp8, kv_format=kv_format, softmax_scale=softmax_scale, q_descale=q_descale,
                            tokens_per_seq=T)
+    return params, out, lse
+
+
+def mla_decode(q, kv_cache, block_table, seqlens, topk_idx=None, kv_scales=None, out=None, lse=None, *,
+               softmax_scale=192.0**-0.5, q_descale=1.0, workspace=None, stream=None):
+    """Absorbed MLA decode (see include/mla.h).
+
+    q: [B, H, 576] (one query token per sequence) or [B, T, H, 576] (T new
+    tokens, causal), torch.bfloat16, or uint8 / float8_e4m3fn codes.
+    kv_cache: bf16 [P, 64, 576]; or uint8 [P, 64, 640] FP8 rows (then kv_scales
+    float32 [P, 64, 4]); or uint8 [P, 64, 576] per-tensor FP8 rows (then
+    kv_scales the float32 [1] k_scale_inv).  block_table int32 [B, max_pages], seqlens int32 [B],
+    topk_idx int32 [B, topk] ([B, T, topk] for T tokens) or None.  Returns (out bf16 [B, H, 512], lse
+    fp32 [B, H]), or [B, T, H, 512] and [B, T, H] for a 4-D q.
+    """
+    import torch
+
+    params, out, lse = _decode_call(q, kv_cache, block_table, seqlens, topk_idx, kv_scales, out, lse,
+                                    softmax_scale, q_descale)
+    dev = q.device
     if workspace is None:
         workspace = decode_workspace(params, dev, stream)
     _expect(workspace, "workspace", (torch.uint8,))
@@ -247,6 +262,22 @@ def mla_decode(q, kv_cache, block_table, seqlens, topk_idx=None, kv_scales=None,
         _stream_handle(stream, dev),
     )
     _check(code, "mla_decode")
+    return out, lse
+
+
+def mla_decode_noalloc(q, kv_cache, block_table, seqlens, topk_idx=None, kv_scales=None, out=None, lse=None, *,
+                       softmax_scale=192.0**-0.5, q_descale=1.0, stream=None):
+    """mla_decode with the library-owned scratch (DECODE_SCRATCH_BYTES per GPU)
+    instead of a workspace: the C entry point allocates nothing.  Pass `out`
+    and `lse` to keep this wrapper from allocating them.  Calls that overlap
+    on one GPU race on the shared scratch; order them on one stream."""
+    params, out, lse = _decode_call(q, kv_cache, block_table, seqlens, topk_idx, kv_scales, out, lse,
+                                    softmax_scale, q_descale)
+    code = lib().mla_decode_noalloc(
+        ctypes.byref(params), _ptr(q), _ptr(kv_cache), _ptr(block_table), _ptr(seqlens), _ptr(topk_idx),
+        _ptr(kv_scales), _ptr(out), _ptr(lse), _stream_handle(stream, q.device),
+    )
+    _check(code, "mla_decode_noalloc")
     return out, lse
 
 

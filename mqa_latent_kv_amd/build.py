@@ -20,7 +20,7 @@ BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libmla.so")
 ARCH = os.environ.get("MLA_OFFLOAD_ARCH", "gfx950")
 
-SOURCES = ["api.cpp", "decode.hip", "decode_ws.hip", "query.hip"]
+SOURCES = ["api.cpp", "decode.hip", "decode_ws.hip", "query.hip", "scratch.hip"]
 
 COMMON = [
     "-O3",

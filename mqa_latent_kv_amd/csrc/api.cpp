@@ -56,55 +56,11 @@ int32_t device_cus(int32_t* cus) {
   return MLA_OK;
 }
 
-}  // namespace
-
-extern "C" {
-
-int32_t mla_version(void) { return 300; }
-
-const char* mla_status_string(int32_t status) {
-  switch (status) {
-    case MLA_OK: return "ok";
-    case MLA_ERR_INVALID_ARG: return "invalid argument";
-    case MLA_ERR_UNSUPPORTED: return "unsupported shape or dtype";
-    case MLA_ERR_WORKSPACE: return "workspace missing or too small";
-    case MLA_ERR_LAUNCH: return "kernel launch failed";
-    case MLA_ERR_DEVICE: return "no usable HIP device";
-    default: return "unknown status";
-  }
-}
-
-int32_t mla_decode_workspace_size(const mla_decode_params* p, size_t* bytes) {
-  if (!bytes) return MLA_ERR_INVALID_ARG;
-  int32_t st = check_decode_params(p);
-  if (st != MLA_OK) return st;
-  int32_t cus = 0;
-  st = device_cus(&cus);
-  if (st != MLA_OK) return st;
-  int32_t eb = 0, eh = 0;
-  mla::effective_dims(p->batch, p->heads, p->topk, p->tokens_per_seq, &eb, &eh);
-  const int32_t ranges = mla::decode_ranges(cus, eb, p->max_pages_per_seq, p->topk, eh);
-  *bytes = mla::decode_workspace_bytes(ranges, eb, eh, p->topk);
-  return MLA_OK;
-}
-
-int32_t mla_decode_workspace_init(const mla_decode_params* p, void* workspace, size_t workspace_bytes,
-                                  void* stream) {
-  size_t need = 0;
-  int32_t st = mla_decode_workspace_size(p, &need);
-  if (st != MLA_OK) return st;
-  if (!workspace || workspace_bytes < need) return MLA_ERR_WORKSPACE;
-  int32_t eb = 0, eh = 0;
-  mla::effective_dims(p->batch, p->heads, p->topk, p->tokens_per_seq, &eb, &eh);
-  if (mla::init_decode_workspace(workspace, eb, eh, (hipStream_t)stream) != hipSuccess)
-    return MLA_ERR_LAUNCH;
-  return MLA_OK;
-}
-
-int32_t mla_decode(const mla_decode_params* p, const void* q, const void* kv_cache,
-                   const int32_t* block_table, const int32_t* seqlens, const int32_t* topk_idx,
-                   const float* kv_scales, void* out, float* lse, void* workspace,
-                   size_t workspace_bytes, void* stream) {
+// Host validation shared by mla_decode and mla_decode_noalloc (a NULL
+// workspace passes here; mla_decode rejects it afterwards).
+int32_t decode_checked(const mla_decode_params* p, const void* q, const void* kv_cache,
+                       const int32_t* block_table, const int32_t* seqlens, const int32_t* topk_idx,
+                       const float* kv_scales, void* out, float* lse, const void* workspace) {
   int32_t st = check_decode_params(p);
   if (st != MLA_OK) return st;
   if (!q || !kv_cache || !block_table || !seqlens || !out || !lse) return MLA_ERR_INVALID_ARG;
@@ -116,14 +72,25 @@ int32_t mla_decode(const mla_decode_params* p, const void* q, const void* kv_cac
     return MLA_ERR_INVALID_ARG;
   if ((p->topk > 0) != (topk_idx != nullptr)) return MLA_ERR_INVALID_ARG;
   if ((p->kv_dtype != MLA_DTYPE_BF16) != (kv_scales != nullptr)) return MLA_ERR_INVALID_ARG;
-  if (!workspace) return MLA_ERR_WORKSPACE;
+  return MLA_OK;
+}
+
+// KV ranges and workspace bytes of a validated decode on the current device.
+int32_t decode_plan(const mla_decode_params* p, int32_t* ranges, size_t* bytes) {
   int32_t cus = 0;
-  st = device_cus(&cus);
+  const int32_t st = device_cus(&cus);
   if (st != MLA_OK) return st;
   int32_t eb = 0, eh = 0;
   mla::effective_dims(p->batch, p->heads, p->topk, p->tokens_per_seq, &eb, &eh);
-  const int32_t ranges = mla::decode_ranges(cus, eb, p->max_pages_per_seq, p->topk, eh);
-  if (workspace_bytes < mla::decode_workspace_bytes(ranges, eb, eh, p->topk)) return MLA_ERR_WORKSPACE;
+  *ranges = mla::decode_ranges(cus, eb, p->max_pages_per_seq, p->topk, eh);
+  *bytes = mla::decode_workspace_bytes(*ranges, eb, eh, p->topk);
+  return MLA_OK;
+}
+
+int32_t decode_launch(const mla_decode_params* p, const void* q, const void* kv_cache,
+                      const int32_t* block_table, const int32_t* seqlens, const int32_t* topk_idx,
+                      const float* kv_scales, void* out, float* lse, void* workspace, int32_t ranges,
+                      void* stream) {
   mla::DecodeLaunch d;
   d.q = q;
   d.kv = kv_cache;
@@ -149,6 +116,81 @@ int32_t mla_decode(const mla_decode_params* p, const void* q, const void* kv_cac
   d.ranges = ranges;
   if (mla::launch_decode(d, (hipStream_t)stream) != hipSuccess) return MLA_ERR_LAUNCH;
   return MLA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t mla_version(void) { return 300; }
+
+const char* mla_status_string(int32_t status) {
+  switch (status) {
+    case MLA_OK: return "ok";
+    case MLA_ERR_INVALID_ARG: return "invalid argument";
+    case MLA_ERR_UNSUPPORTED: return "unsupported shape or dtype";
+    case MLA_ERR_WORKSPACE: return "workspace missing or too small";
+    case MLA_ERR_LAUNCH: return "kernel launch failed";
+    case MLA_ERR_DEVICE: return "no usable HIP device";
+    case MLA_ERR_SCRATCH_LIMIT: return "problem needs more scratch than the library's static decode scratch holds";
+    default: return "unknown status";
+  }
+}
+
+int32_t mla_decode_workspace_size(const mla_decode_params* p, size_t* bytes) {
+  if (!bytes) return MLA_ERR_INVALID_ARG;
+  int32_t st = check_decode_params(p);
+  if (st != MLA_OK) return st;
+  int32_t ranges = 0;
+  return decode_plan(p, &ranges, bytes);
+}
+
+int32_t mla_decode_workspace_init(const mla_decode_params* p, void* workspace, size_t workspace_bytes,
+                                  void* stream) {
+  size_t need = 0;
+  int32_t st = mla_decode_workspace_size(p, &need);
+  if (st != MLA_OK) return st;
+  if (!workspace || workspace_bytes < need) return MLA_ERR_WORKSPACE;
+  int32_t eb = 0, eh = 0;
+  mla::effective_dims(p->batch, p->heads, p->topk, p->tokens_per_seq, &eb, &eh);
+  if (mla::init_decode_workspace(workspace, eb, eh, (hipStream_t)stream) != hipSuccess)
+    return MLA_ERR_LAUNCH;
+  return MLA_OK;
+}
+
+int32_t mla_decode(const mla_decode_params* p, const void* q, const void* kv_cache,
+                   const int32_t* block_table, const int32_t* seqlens, const int32_t* topk_idx,
+                   const float* kv_scales, void* out, float* lse, void* workspace,
+                   size_t workspace_bytes, void* stream) {
+  int32_t st = decode_checked(p, q, kv_cache, block_table, seqlens, topk_idx, kv_scales, out, lse, workspace);
+  if (st != MLA_OK) return st;
+  if (!workspace) return MLA_ERR_WORKSPACE;
+  int32_t ranges = 0;
+  size_t need = 0;
+  st = decode_plan(p, &ranges, &need);
+  if (st != MLA_OK) return st;
+  if (workspace_bytes < need) return MLA_ERR_WORKSPACE;
+  return decode_launch(p, q, kv_cache, block_table, seqlens, topk_idx, kv_scales, out, lse, workspace, ranges,
+                       stream);
+}
+
+int32_t mla_decode_noalloc(const mla_decode_params* p, const void* q, const void* kv_cache,
+                           const int32_t* block_table, const int32_t* seqlens, const int32_t* topk_idx,
+                           const float* kv_scales, void* out, float* lse, void* stream) {
+  int32_t st = decode_checked(p, q, kv_cache, block_table, seqlens, topk_idx, kv_scales, out, lse, nullptr);
+  if (st != MLA_OK) return st;
+  int32_t ranges = 0;
+  size_t need = 0;
+  st = decode_plan(p, &ranges, &need);
+  if (st != MLA_OK) return st;
+  if (need > MLA_DECODE_SCRATCH_BYTES) return MLA_ERR_SCRATCH_LIMIT;
+  void* scratch = nullptr;
+  size_t scratch_bytes = 0;
+  if (mla::decode_scratch(&scratch, &scratch_bytes) != hipSuccess || !scratch || !aligned16(scratch) ||
+      scratch_bytes < need)
+    return MLA_ERR_DEVICE;
+  return decode_launch(p, q, kv_cache, block_table, seqlens, topk_idx, kv_scales, out, lse, scratch, ranges,
+                       stream);
 }
 
 int32_t mla_query_workspace_size(const mla_query_params* p, size_t* bytes) {

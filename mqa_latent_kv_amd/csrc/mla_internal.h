@@ -67,6 +67,9 @@ size_t decode_workspace_bytes(int32_t ranges, int32_t batch, int32_t heads, int3
 // Clear the per-sequence piece records of a decode workspace (optional: every call rewrites them).
 hipError_t init_decode_workspace(void* workspace, int32_t batch, int32_t heads, hipStream_t stream);
 hipError_t launch_decode(const DecodeLaunch& d, hipStream_t stream);
+// The library-owned decode scratch of the current device (scratch.hip): its
+// device address and size.  Looks the address up on a device's first call.
+hipError_t decode_scratch(void** ptr, size_t* bytes);
 // The wave-specialised decode (decode_ws.hip): bf16 paged caches, dense,
 // at least 64 query rows per sequence.
 bool decode_ws_supported(int32_t kv_format, int32_t topk, int32_t eff_heads);
