@@ -210,7 +210,9 @@ int32_t mla_query(const mla_query_params* p, const void* qkv, const void* w_qa, 
   int32_t st = mla_query_workspace_size(p, &need);
   if (st != MLA_OK) return st;
   if (!qkv || !w_qa || !w_qb || !w_uk || !q_scale_inv || !out) return MLA_ERR_INVALID_ARG;
-  if (!aligned16(qkv) || !aligned16(w_qa) || !aligned16(w_qb) || !aligned16(w_uk) || !aligned16(workspace))
+  // q_scale_inv is read as a uniform scalar load, which ignores the low address bits
+  if (!aligned16(qkv) || !aligned16(w_qa) || !aligned16(w_qb) || !aligned16(w_uk) || !aligned16(workspace) ||
+      ((uintptr_t)q_scale_inv & 3))
     return MLA_ERR_INVALID_ARG;
   if (!workspace || workspace_bytes < need) return MLA_ERR_WORKSPACE;
   mla::QueryLaunch ql;

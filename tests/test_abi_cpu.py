@@ -191,6 +191,9 @@ def test_query_validation(L):
     assert q(mla.QueryParams(64, 8, 2112, 1e-6), ws_bytes=1) == -3  # valid up to the workspace size
     for name in ("qkv", "wqa", "wqb", "wuk", "ws"):
         assert q(good, **{name: MISALIGNED}) == -1, name
+    # q_scale_inv is one float: 4-byte alignment is required and enough
+    assert q(good, qsi=ctypes.c_void_p(0x1002)) == -1
+    assert q(good, ws_bytes=1, qsi=ctypes.c_void_p(0x1004)) == -3
     n = ctypes.c_size_t(0)
     assert L.mla_query_workspace_size(ctypes.byref(good), ctypes.byref(n)) == 0 and n.value > 0
 

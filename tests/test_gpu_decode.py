@@ -142,6 +142,17 @@ CASES = {
     # 33 with T = 3), or into a slot before the last (65 with T = 3), at 128 and 384 query rows
     "mtp_t16_h8_first_slot_masked": dict(seed=122, batch=4, heads=8, seqlens=[33, 40, 47, 64], tokens_per_seq=16),
     "mtp_t3_h128_first_slot_masked": dict(seed=123, batch=3, heads=128, seqlens=[33, 34, 65], tokens_per_seq=3),
+    # the same on the per-tensor FP8 register-fill path (masked first slot of a multi-slot segment)
+    "mtp_t16_h8_first_slot_masked_fp8t": dict(seed=124, batch=4, heads=8, seqlens=[33, 40, 47, 64],
+                                              tokens_per_seq=16, kv_format="fp8_tensor"),
+    "mtp_t3_h128_first_slot_masked_fp8t": dict(seed=125, batch=3, heads=128, seqlens=[33, 34, 65],
+                                               tokens_per_seq=3, kv_format="fp8_tensor"),
+    # segments of three or more slots with seqlen % 32 < T - 1: the hidden tail starts in the
+    # slot before the last, a masked slot that is neither the first nor the last (64 and 128 rows)
+    "mtp_t3_h64_fp8t_masked_mid_slot": dict(seed=126, batch=4, heads=64, seqlens=[97, 129, 226, 1025],
+                                            tokens_per_seq=3, kv_format="fp8_tensor"),
+    "mtp_t4_h32_fp8t_masked_mid_slot": dict(seed=127, batch=3, heads=32, seqlens=[66, 130, 1026],
+                                            tokens_per_seq=4, kv_format="fp8_tensor"),
     "mtp_topk_t2_h64_fp8": dict(seed=119, batch=3, heads=64, seqlens=[3000, 800, 40], tokens_per_seq=2,
                                 kv_format="fp8", topk=512, topk_pad_max=60),
     "mtp_topk_t3_h128_bf16": dict(seed=120, batch=2, heads=128, seqlens=[2000, 300], tokens_per_seq=3, topk=256,
@@ -197,15 +208,21 @@ def test_running_max_jumps(heads):
     compare(inp, out, lse, rtol=2.0**-7, scale=abs_weighted_v(inp))
 
 
+@pytest.mark.parametrize("kv_format", ["bf16", "fp8_tensor"])
 @pytest.mark.parametrize("half", [0, 1])
-def test_running_max_jumps_in_one_token_half(half):
+def test_running_max_jumps_in_one_token_half(half, kv_format):
     """As above, but only the positions in one half of every 32-token slot
-    (p % 32 < 16, or >= 16) grow: with 128 heads the two waves of a head
-    group each take the softmax of one token half after a segment's first
-    slot, so only one wave sees the jumps and the restart must still use the
-    maximum over both halves."""
-    inp = synth.make_decode_inputs(131 + half, batch=3, heads=128, seqlens=[700, 1500, 129], pages_per_seq=24)
-    kv = codecs.bf16_bits_to_f64(inp["kv"]).reshape(-1, 576)
+    (p % 32 < 16, or >= 16) grow: with 128 heads each token half of a slot
+    has its own softmax wave after a segment's first slot, so only one wave
+    sees the jumps and the restart must still use the maximum over both
+    halves.  Run on the bf16 copy path and on the per-tensor FP8 register
+    fill (there the grown values are re-encoded as e4m3 codes)."""
+    inp = synth.make_decode_inputs(131 + half, batch=3, heads=128, seqlens=[700, 1500, 129], pages_per_seq=24,
+                                   kv_format=kv_format)
+    if kv_format == "bf16":
+        kv = codecs.bf16_bits_to_f64(inp["kv"]).reshape(-1, 576)
+    else:
+        kv = codecs.e4m3_to_f64(inp["kv"]).reshape(-1, 576)
     bt = inp["block_table"]
     for b in range(3):
         n = int(inp["seqlens"][b])
@@ -213,8 +230,11 @@ def test_running_max_jumps_in_one_token_half(half):
         rows = mo.physical_rows(bt[b], pos)
         grow = ((pos % 32) >= 16) == bool(half)
         kv[rows] *= np.where(grow, 1.0 + pos / 16.0, 1.0)[:, None]
-    inp["kv"] = codecs.f64_to_bf16_bits(kv).reshape(inp["kv"].shape)
-    _say(f"[decode growing scores, token half {half}] H=128")
+    if kv_format == "bf16":
+        inp["kv"] = codecs.f64_to_bf16_bits(kv).reshape(inp["kv"].shape)
+    else:
+        inp["kv"] = codecs.f64_to_e4m3(kv).reshape(inp["kv"].shape)
+    _say(f"[decode growing scores, token half {half}] H=128 kv={kv_format}")
     out, lse = run_gpu(inp)
     compare(inp, out, lse, rtol=2.0**-7, scale=abs_weighted_v(inp))
 
