@@ -18,10 +18,12 @@
 //    scores cross LDS; the wave forms its own exponentials and writes them as
 //    bf16 into a P tile in LDS.
 //  * value waves (4..7): wave 4+v owns output columns 128v .. +127 of all 64
-//    rows (v_mfma_f32_32x32x16_bf16: rows on M, columns on N, 128 fp32
-//    accumulators), reading P from the tile and V through transposing LDS
-//    reads; each V fragment serves both 32-row blocks.  They also issue the
-//    direct global->LDS copies of the KV slots.
+//    rows and forms O^T = V^T P^T (v_mfma_f32_32x32x16_bf16: columns on M,
+//    rows on N, 128 fp32 accumulators, so that a lane ends up holding runs of
+//    four consecutive columns of one row, stored 16 bytes at a time), reading
+//    P from the tile and V through transposing LDS reads; each V fragment
+//    serves both 32-row blocks.  They also issue the direct global->LDS
+//    copies of the KV slots.
 // One workgroup barrier per slot.  Between barriers B_i and B_i+1 the score
 // waves work on slot i, while the value waves multiply slot i-1 (its P was
 // written before B_i, its V fragments read into registers during i-1) and
@@ -159,6 +161,13 @@ struct WsLds {
   LDS_AS int* votes;   // [score wave]: redo votes
 };
 
+// A wave-uniform load of table data that no kernel writes (sequence
+// lengths): through the scalar cache rather than the vector memory pipeline,
+// where it would queue behind the workgroup's copies and query loads.
+__device__ __forceinline__ int32_t ld_uniform(const int32_t* p) {
+  return *(const __attribute__((address_space(4))) int32_t*)p;
+}
+
 // One segment of the range: sequence b, tokens [tok0, tok1).
 struct WsSeg {
   int b;
@@ -174,7 +183,9 @@ __device__ __forceinline__ void for_segments(const DecodeArgs& a, const Plan& pl
   int b = pl.b0, p = pl.p0;
   bool first = true;
   while (true) {
-    const int n = units_of(a, b);
+    // (dense decode: a sequence's units are its pages)
+    const int seglen = min(max(ld_uniform(a.seqlens + b), 0), a.max_pages * kPage);
+    const int n = (seglen + kPage - 1) / kPage;
     const int gs = max(pl.start, p), ge = min(pl.end, p + n);
     if (gs < ge) {
       if (!first) {
@@ -184,7 +195,7 @@ __device__ __forceinline__ void for_segments(const DecodeArgs& a, const Plan& pl
       first = false;
       WsSeg s;
       s.b = b;
-      s.seglen = min(max(a.seqlens[b], 0), a.max_pages * kPage);
+      s.seglen = seglen;
       s.sg.tok0 = (gs - p) * kPage;
       s.sg.tok1 = min((ge - p) * kPage, s.seglen);
       s.sg.nslots = (s.sg.tok1 - s.sg.tok0 + kTS - 1) / kTS;
@@ -238,6 +249,7 @@ __device__ __forceinline__ void score_role(const DecodeArgs& a, const Plan& pl, 
     for (int j = 0; j < 2; ++j) lim[j] = CAUSAL ? min(sgm.sg.tok1, sgm.seglen - lag[j]) : sgm.sg.tok1;
     const int lim_lo = min(lim[0], lim[1]);
 
+    barrier();  // X: the value waves' first copies are issued before these loads
     // queries (B operand): row qrow[j], columns 32k + 8(lane/16) .. +7
     bf16x8 qf[kQk][2];
 #pragma unroll
@@ -416,7 +428,12 @@ __device__ __forceinline__ void value_role(const DecodeArgs& a, const Plan& pl, 
         for (int cb = 0; cb < 4; ++cb) o[rb][cb] = f32x16{};
       // copy epochs -3 .. -1 (the prologue): slots 0 .. 2; slot 0 landed
       const int pre = min(nslots, 3);
-      for (int s = 0; s < pre; ++s) dma_cols(s, s);
+      // slot 0 first, then X: the score waves load their queries only after
+      // these copies are issued, so that slot 0 is not queued behind them
+      // (slots 1 and 2 follow, beside the query loads)
+      if (pre > 0) dma_cols(0, 0);
+      if (pass == 0) barrier();
+      for (int s = 1; s < pre; ++s) dma_cols(s, s);
       wait_ops_lgkm0(epoch_ops(-2, nslots) + epoch_ops(-1, nslots));
       barrier();  // B_0
       VFrag vx[4], vy[4];
@@ -440,8 +457,8 @@ __device__ __forceinline__ void value_role(const DecodeArgs& a, const Plan& pl, 
             const bf16x8 v1 = __builtin_shufflevector(vc[cb][2], vc[cb][3], 0, 1, 2, 3, 4, 5, 6, 7);
 #pragma unroll
             for (int rb = 0; rb < 2; ++rb) {
-              o[rb][cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pf[rb][0], v0, o[rb][cb], 0, 0, 0);
-              o[rb][cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pf[rb][1], v1, o[rb][cb], 0, 0, 0);
+              o[rb][cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(v0, pf[rb][0], o[rb][cb], 0, 0, 0);
+              o[rb][cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(v1, pf[rb][1], o[rb][cb], 0, 0, 0);
             }
             if (it < nslots) ws_vload(nbuf, va, cb, vn[cb]);
           }
@@ -463,35 +480,34 @@ __device__ __forceinline__ void value_role(const DecodeArgs& a, const Plan& pl, 
       barrier();  // the score waves' sums and votes
       const int votes = L.votes[0] | L.votes[1] | L.votes[2] | L.votes[3];
       if (__builtin_amdgcn_readfirstlane(votes) == 0) {
-        // normalise and store this wave's 128 columns of the 64 rows.  The
+        // normalise and store this wave's 128 columns of the 64 rows: the
+        // lane holds row 32rb + lane%32 and, per column block and register
+        // quad, four consecutive columns (one 16-byte or 8-byte store).  The
         // lane index is passed through an empty asm so that the compiler
-        // cannot hoist these per-lane store addresses out of the slot loop
-        // (they would hold ~70 registers across it).
+        // cannot hoist these per-lane store addresses out of the slot loop.
         int ln = lane;
         asm volatile("" : "+v"(ln));
         const int i32 = ln & 31, h2 = ln >> 5;
         const size_t pslot = (size_t)(b + r);
 #pragma unroll
         for (int rb = 0; rb < 2; ++rb) {
+          const int lr = 32 * rb + i32;
+          const float lt = L.xl[lr] + L.xl[64 + lr];
+          const float inv = lt > 0.0f ? 1.0f / lt : 0.0f;
+          const int row = row0 + lr;
+          if (row < a.heads) {
+            __bf16* orow = (__bf16*)a.out + ((size_t)b * a.heads + row) * kDV + 128 * v + 4 * h2;
+            float* prow = a.ws_o + (pslot * a.heads + row) * kDV + 128 * v + 4 * h2;
 #pragma unroll
-          for (int r4 = 0; r4 < 4; ++r4) {
-            // accumulator registers 4r4 + e: rows 32rb + 8r4 + 4h2 + e
-            const int lr = 32 * rb + 8 * r4 + 4 * h2;
-            const f32x4 l0 = *(const LDS_AS f32x4*)(L.xl + lr);
-            const f32x4 l1 = *(const LDS_AS f32x4*)(L.xl + 64 + lr);
+            for (int cb = 0; cb < 4; ++cb) {
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              const float lt = l0[e] + l1[e];
-              const float inv = lt > 0.0f ? 1.0f / lt : 0.0f;
-              const int row = row0 + lr + e;
-              if (row < a.heads) {
+              for (int q = 0; q < 4; ++q) {
+                // accumulator registers 4q .. 4q+3: columns 32cb + 8q + 4h2 .. +3
+                f32x4 val;
 #pragma unroll
-                for (int cb = 0; cb < 4; ++cb) {
-                  const int col = 128 * v + 32 * cb + i32;
-                  const float val = o[rb][cb][4 * r4 + e] * inv;
-                  if (sgm.nsplit == 1) ((__bf16*)a.out)[((size_t)b * a.heads + row) * kDV + col] = (__bf16)val;
-                  else a.ws_o[(pslot * a.heads + row) * kDV + col] = val;
-                }
+                for (int e = 0; e < 4; ++e) val[e] = o[rb][cb][4 * q + e] * inv;
+                if (sgm.nsplit == 1) *(bf16x4*)(orow + 32 * cb + 8 * q) = __builtin_convertvector(val, bf16x4);
+                else *(f32x4*)(prow + 32 * cb + 8 * q) = val;
               }
             }
           }
