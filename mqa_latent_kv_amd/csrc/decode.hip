@@ -1526,6 +1526,7 @@ hipError_t launch_decode(const DecodeLaunch& din, hipStream_t stream) {
   a.tq = causal ? din.tq : 1;
   a.heads_tok = din.heads;
   a.ranges = d.ranges;
+  a.seg_pad = 0;
   a.per_xcd = (d.ranges + 7) / 8;
   a.scale_log2 = d.softmax_scale * kLog2e;
   a.q_descale = d.q_descale;
@@ -1537,6 +1538,7 @@ hipError_t launch_decode(const DecodeLaunch& din, hipStream_t stream) {
   if (decode_ws_supported(d.kv_format, d.topk, d.heads)) {
     // dense bf16 pages with at least 64 rows per sequence: the wave-specialised
     // kernel (decode_ws.hip), the same plan, slabs of 64 rows and workspace
+    a.seg_pad = kWsSegPad;
     e = launch_decode_ws(a, d.q_fp8, causal, stream);
   } else {
     e = launch_decode_tiled(a, d, kvm, causal, stream);

@@ -98,6 +98,13 @@ struct Plan {
   int p0;     // global index of b0's first unit
 };
 
+// Units of sequence b on the split line: its pages (or top-k pages) plus
+// a.seg_pad virtual units at each end when it has any.
+__device__ __forceinline__ int line_units(const DecodeArgs& a, int b) {
+  const int n = units_of(a, b);
+  return n > 0 ? n + 2 * a.seg_pad : 0;
+}
+
 // (NT threads per workgroup; scratch holds NT + 2 ints)
 template <int NT>
 __device__ bool make_plan(const DecodeArgs& a, int r, int* scratch, Plan& pl) {
@@ -106,7 +113,7 @@ __device__ bool make_plan(const DecodeArgs& a, int r, int* scratch, Plan& pl) {
   const int per = (B + NT - 1) / NT;
   const int lo = tid * per, hi = min(B, lo + per);
   int local = 0;
-  for (int b = lo; b < hi; ++b) local += units_of(a, b);
+  for (int b = lo; b < hi; ++b) local += line_units(a, b);
   // inclusive scan of the per-thread sums: within each wave by cross-lane
   // reads (ds_bpermute moves data between lanes, it touches no LDS memory),
   // then the four wave totals through LDS behind a single barrier
@@ -136,7 +143,7 @@ __device__ bool make_plan(const DecodeArgs& a, int r, int* scratch, Plan& pl) {
   if (start >= excl && start < incl) {
     int p = excl;
     for (int b = lo; b < hi; ++b) {
-      int n = units_of(a, b);
+      int n = line_units(a, b);
       if (start < p + n) {
         scratch[NT] = b;
         scratch[NT + 1] = p;

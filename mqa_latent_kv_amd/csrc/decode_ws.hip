@@ -180,13 +180,16 @@ struct WsSeg {
 // between segments (every wave is done with the ring and the exchanges).
 template <class F>
 __device__ __forceinline__ void for_segments(const DecodeArgs& a, const Plan& pl, F&& body) {
+  // p: line position of sequence b; its pages are units [p + pad, p + pad + n)
+  const int pad = a.seg_pad;
   int b = pl.b0, p = pl.p0;
   bool first = true;
   while (true) {
     // (dense decode: a sequence's units are its pages)
     const int seglen = min(max(ld_uniform(a.seqlens + b), 0), a.max_pages * kPage);
     const int n = (seglen + kPage - 1) / kPage;
-    const int gs = max(pl.start, p), ge = min(pl.end, p + n);
+    const int q = p + pad;
+    const int gs = max(pl.start, q), ge = min(pl.end, q + n);
     if (gs < ge) {
       if (!first) {
         wait_vm_lgkm0<0>();
@@ -196,17 +199,17 @@ __device__ __forceinline__ void for_segments(const DecodeArgs& a, const Plan& pl
       WsSeg s;
       s.b = b;
       s.seglen = seglen;
-      s.sg.tok0 = (gs - p) * kPage;
-      s.sg.tok1 = min((ge - p) * kPage, s.seglen);
+      s.sg.tok0 = (gs - q) * kPage;
+      s.sg.tok1 = min((ge - q) * kPage, s.seglen);
       s.sg.nslots = (s.sg.tok1 - s.sg.tok0 + kTS - 1) / kTS;
       s.sg.npages = (s.sg.nslots + 1) / 2;
-      s.sg.bt_seg = a.block_table + (size_t)b * a.max_pages + (gs - p);
+      s.sg.bt_seg = a.block_table + (size_t)b * a.max_pages + (gs - q);
       s.sg.idx_seg = nullptr;
-      s.first_r = p / pl.C;
-      s.nsplit = (p + n - 1) / pl.C - s.first_r + 1;
+      s.first_r = q / pl.C;
+      s.nsplit = (q + n - 1) / pl.C - s.first_r + 1;
       body(s);
     }
-    p += n;
+    p += n > 0 ? n + 2 * pad : 0;
     ++b;
     if (p >= pl.end || b >= a.batch) break;
   }

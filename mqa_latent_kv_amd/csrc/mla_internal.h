@@ -46,6 +46,7 @@ struct DecodeArgs {
   int32_t tq;         // dense, several query tokens: T (rows of a sequence = T x heads_tok), else 1
   int32_t heads_tok;  // query heads per token
   int32_t ranges;    // KV ranges (workgroups per head slab)
+  int32_t seg_pad;   // virtual units at each end of a sequence on the split line (segment overhead)
   int32_t slabs;     // head slabs per range
   int32_t per_xcd;   // ranges per XCD in the block -> (range, slab) mapping
   float scale_log2;  // softmax_scale * log2(e)
@@ -74,6 +75,11 @@ hipError_t decode_scratch(void** ptr, size_t* bytes);
 // at least 64 query rows per sequence.
 bool decode_ws_supported(int32_t kv_format, int32_t topk, int32_t eff_heads);
 hipError_t launch_decode_ws(const DecodeArgs& a, bool q_fp8, bool causal, hipStream_t stream);
+// Split-line padding of the wave-specialised decode: a segment costs about
+// as much as this many pages at each of its two ends (query load, pipeline
+// fill, epilogue), so each sequence's pages sit between that many virtual
+// units on each side and the equal cut balances pages plus segment ends.
+constexpr int32_t kWsSegPad = 4;
 
 struct QueryLaunch {
   const void* qkv;
