@@ -55,8 +55,8 @@ METRIC = "MLA decode µs/step + achieved HBM GB/s (% of peak) at B=64,H=128,s_k=
 HBM_PEAK_GBS = 8000.0
 MFMA_BF16_PEAK_TFLOPS = 2500.0
 CALIB_BYTES = 256 << 20  # plain copy used to scale the HBM traffic counters
-KERNEL_SOURCES = [os.path.join(ROOT, "mqa_latent_kv_amd", "csrc", f)
-                  for f in ("decode_common.h", "decode.hip", "decode_ws.hip", "query.hip")]
+DECODE_SOURCES = ("decode_common.h", "decode.hip", "decode_ws.hip")
+QUERY_WORKLOADS = ("query_decode", "query_narrow_decode", "insert_decode")  # also run query.hip kernels
 COLD_FLUSH_BYTES = 512 << 20  # read between cold steps: twice the 256 MB Infinity Cache
 
 WORKLOADS = {
@@ -150,11 +150,17 @@ def query_flops(qin) -> int:
     return 2 * B * 1536 * H * 192 + 2 * B * H * 128 * 512
 
 
-def kernel_hash() -> str:
-    """Hash of the kernel sources with // comments dropped and whitespace runs
-    collapsed, so a comment edit does not disown counters taken on the same code."""
+def kernel_sources(workload: str):
+    names = DECODE_SOURCES + (("query.hip",) if workload in QUERY_WORKLOADS else ())
+    return [os.path.join(ROOT, "mqa_latent_kv_amd", "csrc", f) for f in names]
+
+
+def kernel_hash(workload: str) -> str:
+    """Hash of the sources of the workload's kernels with // comments dropped
+    and whitespace runs collapsed, so a comment edit does not disown counters
+    taken on the same code."""
     h = hashlib.sha256()
-    for p in KERNEL_SOURCES:
+    for p in kernel_sources(workload):
         text = re.sub(r"//[^\n]*", "", open(p, encoding="utf-8").read())
         h.update(re.sub(r"\s+", " ", text).encode())
     return h.hexdigest()[:16]
@@ -167,7 +173,7 @@ def measured_traffic(workload: str):
         d = json.load(open(traffic_file(workload)))
     except (OSError, ValueError):
         return None
-    if d.get("kernel_hash") != kernel_hash():
+    if d.get("kernel_hash") != kernel_hash(workload):
         return None
     return d.get("traffic_bytes_per_step")
 

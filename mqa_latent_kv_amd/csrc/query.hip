@@ -9,7 +9,9 @@
 //   out = e4m3(ql * qsi) | e4m3(qb[:, 128:] * qsi)  qsi = q_scale_inv[0]
 // with e4m3 rounded to nearest even and saturated to +-448.
 //
-// Three kernels, the products on v_mfma_f32_32x32x16_bf16 with 32 tokens as M:
+// Above 128 tokens, three kernels, the products on v_mfma_f32_32x32x16_bf16
+// with 32 tokens as M (from 9 to 128 tokens, the two kernels of the medium
+// form further below):
 //  * mla_norm_kernel: the RMSNorm of every token, once, into the workspace.
 //  * mla_qb_kernel: a workgroup owns 32 tokens, 32 rows of W_qb and (when
 //    the tiles alone would not fill the chip, e.g. 64 tokens x 8 heads) a
@@ -67,6 +69,7 @@ struct QueryArgs {
   __bf16* qn;   // workspace, narrow batch: [B][H][128] bf16 nope rows of Q_B
   __bf16* xn;   // workspace, tiled: [B][1536] normalised q_a rows
   float* qbp;   // workspace, tiled: [ksplit][B][H*192] fp32 partial Q_B products
+  __bf16* qbm;  // workspace, medium batch: [B][H*192] bf16 Q_B
   int32_t batch, heads, qkv_stride;
   float eps;
 };
@@ -535,6 +538,171 @@ __global__ void __launch_bounds__(kThreads) mla_ql_gemv_kernel(QueryArgs a) {
     a.out[((size_t)t * a.heads + head) * kOut + c0 + c] = e4m3_of_product(v, qsi);
   }
 }
+
+// ---------------------------------------------------------------- medium batch: fused RMSNorm + Q_B, then W_UK
+
+// From kNarrow + 1 to kMedium tokens the 32 x 32 tiles are too few to spread
+// the weights over the chip, and the three-kernel form pays a launch and a
+// dependent load chain per step.  Two kernels instead, with small tiles:
+//  * mla_qbn_kernel: a workgroup owns 16 tokens and 32 W_qb rows over the
+//    whole 1536-long reduction, an eighth per wave.  It loads its tokens'
+//    q_a rows in full anyway (they are the A operand), so it forms their
+//    RMSNorm itself: per-wave sums of squares, added in wave order in LDS.
+//    v_mfma_f32_16x16x32_bf16 with tokens on M; the four partial tiles are
+//    added in wave order and Q_B is stored once, rounded to bf16.
+//  * mla_qlm_kernel: a one-wave workgroup owns 32 tokens, one head and 32
+//    output columns: W_uk[h][0..127][32 columns] staged in LDS and read with
+//    ds_read_b64_tr_b16, the nope rows of Q_B as the A operand, then FP8.
+constexpr int kMedium = 128;
+constexpr int kMTok = 16;                 // tokens per Q_B workgroup (MFMA M)
+constexpr int kMRows = 32;                // W_qb rows per Q_B workgroup (two MFMA N blocks)
+constexpr int kQbnThreads = 512;          // eight waves, an eighth of the reduction each
+constexpr int kMKs = kQA / 8 / 32;        // k-steps of 32 per wave
+constexpr int kUkCols = 32;               // W_UK output columns per workgroup
+
+__global__ void __launch_bounds__(kQbnThreads) mla_qbn_kernel(QueryArgs a) {
+  constexpr int W = kQbnThreads / 64;
+  __shared__ float ssp[W][kMTok];                               // per-wave sums of squares
+  __shared__ __attribute__((aligned(16))) f32x4 red[W][2][64];  // per-wave partial tiles
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int i16 = lane & 15, g = lane >> 4;
+  const int nrows = a.heads * kQB;
+  const int n0 = blockIdx.x * kMRows, m0 = blockIdx.y * kMTok;
+  // lane l: A = token m0 + l%16, B = W_qb rows n0 + 16nb + l%16 (nb = 0, 1),
+  // columns 192w + 32i + 8(l/16) .. +7 (clamped rows and tokens, zeroed below)
+  const int t = m0 + i16;
+  const bool t_ok = t < a.batch;
+  const int t_c = t_ok ? t : a.batch - 1;
+  bool row_ok[2];
+  int nrow_c[2];
+#pragma unroll
+  for (int nb = 0; nb < 2; ++nb) {
+    const int nrow = n0 + 16 * nb + i16;
+    row_ok[nb] = nrow < nrows;
+    nrow_c[nb] = row_ok[nb] ? nrow : nrows - 1;
+  }
+  const int k0 = w * (kQA / W) + 8 * g;
+  bf16x8 xr[kMKs], wq[kMKs], wr[2][kMKs];
+#pragma unroll
+  for (int i = 0; i < kMKs; ++i) {
+    xr[i] = *(const bf16x8*)(a.qkv + (size_t)t_c * a.qkv_stride + k0 + 32 * i);
+    wq[i] = *(const bf16x8*)(a.w_qa + k0 + 32 * i);
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb) wr[nb][i] = *(const bf16x8*)(a.w_qb + (size_t)nrow_c[nb] * kQA + k0 + 32 * i);
+  }
+  // sum of squares of token t over this wave's eighth: the lane's 48 values,
+  // then the four lanes l, l^16, l^32, l^48 that share the token
+  float ss = 0.0f;
+#pragma unroll
+  for (int i = 0; i < kMKs; ++i)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const float x = (float)xr[i][e];
+      ss = __builtin_fmaf(x, x, ss);
+    }
+  {
+    auto r16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(ss), __float_as_uint(ss), false, false);
+    ss = __uint_as_float(r16[0]) + __uint_as_float(r16[1]);
+    auto r32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(ss), __float_as_uint(ss), false, false);
+    ss = __uint_as_float(r32[0]) + __uint_as_float(r32[1]);
+  }
+  if (g == 0) ssp[w][i16] = ss;
+  __syncthreads();
+  float tot = 0.0f;
+#pragma unroll
+  for (int v = 0; v < W; ++v) tot += ssp[v][i16];
+  const float rr = 1.0f / __builtin_sqrtf(tot / (float)kQA + a.eps);
+  f32x4 acc[2] = {};
+#pragma unroll
+  for (int i = 0; i < kMKs; ++i) {
+    bf16x8 xn;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) xn[e] = (__bf16)(((float)xr[i][e] * rr) * (float)wq[i][e]);
+    const bf16x8 x = t_ok ? xn : bf16x8{};
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb) {
+      const bf16x8 y = row_ok[nb] ? wr[nb][i] : bf16x8{};
+      acc[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(x, y, acc[nb], 0, 0, 0);
+    }
+  }
+  red[w][0][lane] = acc[0];
+  red[w][1][lane] = acc[1];
+  __syncthreads();
+  // thread (nb, r, l): register r of lane l in block nb, i.e. token
+  // m0 + 4(l/16) + r and W_qb row n0 + 16nb + l%16; the waves' tiles added
+  // in wave order, rounded to bf16 once
+  const int l = tid & 63, r = (tid >> 6) & 3, nb = tid >> 8;
+  float v = 0.0f;
+#pragma unroll
+  for (int u = 0; u < W; ++u) v += red[u][nb][l][r];
+  const int tt = m0 + 4 * (l >> 4) + r, nn = n0 + 16 * nb + (l & 15);
+  if (tt < a.batch && nn < nrows) a.qbm[(size_t)tt * nrows + nn] = (__bf16)v;
+}
+
+__global__ void __launch_bounds__(64) mla_qlm_kernel(QueryArgs a) {
+  __shared__ __attribute__((aligned(16))) __bf16 uk[kNope][kUkCols];  // W_uk[h][p][c0 .. c0+31], 8 KB
+  const int lane = threadIdx.x;
+  const int head = blockIdx.x, c0 = blockIdx.y * kUkCols, m0 = blockIdx.z * kTok;
+  const int nrows = a.heads * kQB;
+  // W_uk rows: 128 rows of 64 bytes, four 16-byte chunks each; lane l takes
+  // chunk l%4 of rows l/4 + 16j
+  u32x4 wv[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const int p = (lane >> 2) + 16 * j;
+    wv[j] = *(const u32x4*)(a.w_uk + ((size_t)head * kNope + p) * kDV + c0 + 8 * (lane & 3));
+  }
+  // A fragments: token m0 + l%32 (tokens past the batch zeroed), nope rows
+  // 16ks + 8(l/32) .. +7 of its Q_B
+  const int b = m0 + (lane & 31);
+  const bool b_ok = b < a.batch;
+  const int b_c = b_ok ? b : a.batch - 1;
+  bf16x8 af[kNope / 16];
+#pragma unroll
+  for (int ks = 0; ks < kNope / 16; ++ks) {
+    const bf16x8 x = *(const bf16x8*)(a.qbm + (size_t)b_c * nrows + (size_t)head * kQB + 16 * ks + 8 * (lane >> 5));
+    af[ks] = b_ok ? x : bf16x8{};
+  }
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const int p = (lane >> 2) + 16 * j;
+    *(LDS_AS u32x4*)((LDS_AS char*)&uk[p][0] + 16 * (lane & 3)) = wv[j];
+  }
+  __syncthreads();
+  // B[k][n] = W_uk[head][16ks + k][c0 + n] by transposing reads: lane l gets
+  // column l%32 of rows 8(l/32) + i; within 16-lane group G lane 4j + q reads
+  // columns 16(G&1) + 4q .. +3 of row 8(G>>1) + 4tt + j for elements 4tt ..
+  const int G = lane >> 4, i16 = lane & 15, jj = i16 >> 2, q = i16 & 3;
+  f32x16 acc = {};
+#pragma unroll
+  for (int ks = 0; ks < kNope / 16; ++ks) {
+    const int m = 16 * ks + 8 * (G >> 1) + jj;
+    const bf16x4 r0 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((LDS_AS bf16x4*)&uk[m][16 * (G & 1) + 4 * q]);
+    const bf16x4 r1 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((LDS_AS bf16x4*)&uk[m + 4][16 * (G & 1) + 4 * q]);
+    const bf16x8 bfr = __builtin_shufflevector(r0, r1, 0, 1, 2, 3, 4, 5, 6, 7);
+    acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[ks], bfr, acc, 0, 0, 0);
+  }
+  // lane l, register r: token m0 + 8(r/4) + 4(l/32) + r%4, column c0 + l%32
+  const float qsi = a.q_scale_inv[0];
+  const int c = c0 + (lane & 31);
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const int bb = m0 + 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3);
+    if (bb >= a.batch) continue;
+    a.out[((size_t)bb * a.heads + head) * kOut + c] = e4m3_of_product((float)(__bf16)acc[i], qsi);
+  }
+  // the rope rows of Q_B, encoded as they are: column block y takes rope
+  // values 4y .. 4y+3 of the 32 tokens, lane l two of them for token m0 + l/2
+  {
+    const int t = m0 + (lane >> 1), r = 4 * blockIdx.y + 2 * (lane & 1);
+    if (t < a.batch) {
+      const __bf16* src = a.qbm + (size_t)t * nrows + (size_t)head * kQB + kNope + r;
+      uint8_t* dst = a.out + ((size_t)t * a.heads + head) * kOut + kDV + r;
+      dst[0] = e4m3_of_product((float)src[0], qsi);
+      dst[1] = e4m3_of_product((float)src[1], qsi);
+    }
+  }
+}
 }  // namespace
 
 hipError_t launch_kv_insert(const InsertLaunch& k, hipStream_t stream) {
@@ -564,6 +732,7 @@ int query_ksplit(int32_t batch, int32_t heads) {
 // then [ksplit][B][H*192] fp32 Q_B partials.
 size_t query_workspace_bytes(int32_t batch, int32_t heads) {
   if (batch <= kNarrow) return (size_t)batch * heads * kNope * 2 + 256;
+  if (batch <= kMedium) return (size_t)batch * heads * kQB * 2 + 256;
   return (((size_t)batch * kQA * 2 + 255) & ~(size_t)255) +
          (size_t)query_ksplit(batch, heads) * batch * heads * kQB * 4 + 256;
 }
@@ -579,6 +748,7 @@ hipError_t launch_query(const QueryLaunch& q, hipStream_t stream) {
   a.qn = (__bf16*)q.workspace;
   a.xn = (__bf16*)q.workspace;
   a.qbp = (float*)((char*)q.workspace + (((size_t)q.batch * kQA * 2 + 255) & ~(size_t)255));
+  a.qbm = (__bf16*)q.workspace;
   a.batch = q.batch;
   a.heads = q.heads;
   a.qkv_stride = q.qkv_stride;
@@ -592,6 +762,14 @@ hipError_t launch_query(const QueryLaunch& q, hipStream_t stream) {
     return hipGetLastError();
   }
   const int mt = (q.batch + kTok - 1) / kTok;
+  if (q.batch <= kMedium) {
+    hipLaunchKernelGGL(mla_qbn_kernel, dim3((q.heads * kQB + kMRows - 1) / kMRows, (q.batch + kMTok - 1) / kMTok),
+                       dim3(kQbnThreads), 0, stream, a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(mla_qlm_kernel, dim3(q.heads, kDV / kUkCols, mt), dim3(64), 0, stream, a);
+    return hipGetLastError();
+  }
   const int ksplit = query_ksplit(q.batch, q.heads);
   hipLaunchKernelGGL(mla_norm_kernel, dim3((q.batch + 3) / 4), dim3(kThreads), 0, stream, a);
   const dim3 qb_grid((q.heads * kQB + 31) / 32, mt, ksplit), ql_grid(q.heads, kDV / 128, mt);

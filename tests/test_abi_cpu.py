@@ -247,9 +247,10 @@ def test_binding_raises_without_library(monkeypatch):
 
 def test_query_workspace_sizes_per_form(L):
     """The query's workspace follows its form: up to 8 tokens the bf16 nope
-    rows [B][H][128]; above, the bf16 normalised rows [B][1536] (256-byte
-    aligned) then the fp32 Q_B partials [ksplit][B][H*192], with the
-    reduction split in four when the 32 x 32 tiles would number under 256."""
+    rows [B][H][128]; from 9 to 128 tokens the bf16 Q_B rows [B][H*192];
+    above, the bf16 normalised rows [B][1536] (256-byte aligned) then the
+    fp32 Q_B partials [ksplit][B][H*192], with the reduction split in four
+    when the 32 x 32 tiles would number under 256."""
     def size(b, h):
         n = ctypes.c_size_t(0)
         assert L.mla_query_workspace_size(ctypes.byref(mla.QueryParams(b, h, 1536, 1e-6)), ctypes.byref(n)) == 0
@@ -263,7 +264,9 @@ def test_query_workspace_sizes_per_form(L):
 
     for b, h in [(1, 1), (4, 128), (8, 8)]:
         assert size(b, h) == b * h * 128 * 2 + 256
-    for b, h in [(9, 8), (64, 8), (64, 128), (8192, 8)]:
+    for b, h in [(9, 8), (64, 8), (64, 128), (128, 3)]:
+        assert size(b, h) == b * h * 192 * 2 + 256, (b, h)
+    for b, h in [(129, 1), (129, 128), (8192, 8)]:
         ksplit = 4 if tiles(b, h) < 256 else 1
         assert size(b, h) == align(b * 1536 * 2) + ksplit * b * h * 192 * 4 + 256, (b, h)
-    assert tiles(64, 8) < 256 and tiles(64, 128) >= 256  # both forms of the split occur above
+    assert tiles(129, 1) < 256 and tiles(129, 128) >= 256  # both forms of the split occur above

@@ -60,6 +60,12 @@ CASES = {
     "narrow_b8_h16_qsi": dict(seed=63, batch=8, heads=16, q_scale_inv=0.3),
     "narrow_b3_h3_wide_rows": dict(seed=64, batch=3, heads=3, width=2112),
     "mfma_b9_h8": dict(seed=65, batch=9, heads=8),
+    # 9 to 128 tokens take the fused RMSNorm + Q_B form (16 x 16 tiles); above,
+    # the three-kernel 32 x 32 form, with the reduction split in four when the
+    # tiles are few (129 x 3) and whole otherwise (300 x 16)
+    "medium_b128_h5": dict(seed=66, batch=128, heads=5),
+    "tiled_b129_h3": dict(seed=67, batch=129, heads=3),
+    "tiled_b300_h16": dict(seed=68, batch=300, heads=16),
 }
 
 
