@@ -1539,7 +1539,7 @@ hipError_t launch_decode(const DecodeLaunch& din, hipStream_t stream) {
     // dense bf16 pages with at least 64 rows per sequence: the wave-specialised
     // kernel (decode_ws.hip), the same plan, slabs of 64 rows and workspace
     a.seg_pad = kWsSegPad;
-    e = launch_decode_ws(a, d.q_fp8, causal, stream);
+    e = launch_decode_ws(a, d.kv_format, d.q_fp8, causal, stream);
   } else {
     e = launch_decode_tiled(a, d, kvm, causal, stream);
   }

@@ -46,6 +46,8 @@
 // normalised partial and base-2 LSE to the workspace for mla_merge_kernel.
 #include "decode_common.h"
 
+#include <type_traits>
+
 namespace mla {
 namespace {
 
@@ -57,6 +59,38 @@ constexpr int kPRowBytes = 80;    // a row of the P tile: 32 bf16 + 16 bytes of 
 constexpr int kPTile = kWsRows * kPRowBytes;
 constexpr int kKRead = 4;         // K fragments in flight ahead of their MFMA
 
+// Cache layouts of this kernel.  The e4m3 rows stay codes in the ring (the
+// same direct copies, 128-byte column groups of 32 rows, the same swizzle)
+// and become bf16 as the MFMA fragments are read: K rows with plain 8-byte
+// reads, V^T with the 8-bit transposing read.
+constexpr int kFmtBf16 = 0;  // [P,64,576] bf16
+constexpr int kFmtFp8 = 1;   // [P,64,640]: 512 codes + 64 bf16 rope; fp32 scales [P,64,4], one per 128 columns
+constexpr int kFmtFp8T = 2;  // [P,64,576] codes; one per-tensor k_scale_inv
+template <int F>
+struct WsFmt;
+template <>
+struct WsFmt<kFmtBf16> {
+  static constexpr int kRow = kRowBytes;    // bytes per cache row
+  static constexpr int kSlot = kSlotBytes;  // ring slot: nine column groups
+  static constexpr int kOps = kDmaPerWave;  // copies per value wave and slot
+  static constexpr int kPTiles = 1;         // P tiles per slot
+};
+template <>
+struct WsFmt<kFmtFp8> {
+  static constexpr int kRow = kFp8RowBytes;
+  static constexpr int kScaleOff = 5 * kGroupBytes;     // four codes groups, the rope group, then scales
+  static constexpr int kSlot = kScaleOff + 4 * 1024;    // each value wave copies the 32 rows' scales
+  static constexpr int kOps = 6;
+  static constexpr int kPTiles = 4;                     // P scaled by each column tile's scale
+};
+template <>
+struct WsFmt<kFmtFp8T> {
+  static constexpr int kRow = kFp8TRowBytes;
+  static constexpr int kSlot = 5 * kGroupBytes;  // four codes groups, half a group of rope codes
+  static constexpr int kOps = 5;
+  static constexpr int kPTiles = 1;
+};
+
 // s_waitcnt vmcnt(N) alone (LDS reads stay in flight), GFX9 encoding
 template <int N>
 __device__ __forceinline__ void wait_vm() {
@@ -65,15 +99,42 @@ __device__ __forceinline__ void wait_vm() {
 }
 
 // vm operations of copy epoch e of an n-slot segment, per value wave: the
-// nine copies of slot e+3
-__device__ __forceinline__ int epoch_ops(int e, int n) { return e + 3 < n ? kDmaPerWave : 0; }
+// N copies of slot e+3
+template <int N>
+__device__ __forceinline__ int epoch_ops(int e, int n) { return e + 3 < n ? N : 0; }
 
 // s_waitcnt vmcnt(k) lgkmcnt(0) for the counts epoch_ops can add up to
 // (anything else waits for everything, which is always safe)
+template <int N>
 __device__ __forceinline__ void wait_ops_lgkm0(int k) {
-  if (k == 2 * kDmaPerWave) wait_vm_lgkm0<2 * kDmaPerWave>();
-  else if (k == kDmaPerWave) wait_vm_lgkm0<kDmaPerWave>();
+  if (k == 2 * N) wait_vm_lgkm0<2 * N>();
+  else if (k == N) wait_vm_lgkm0<N>();
   else wait_vm_lgkm0<0>();
+}
+
+// 8 e4m3 codes as bf16 (exact: every e4m3 value is a bf16 value)
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ bf16x8 codes_bf16(u32x2 c) {
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  const bf16x2 x0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c[0], 1.0f, false);
+  const bf16x2 x1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c[0], 1.0f, true);
+  const bf16x2 x2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c[1], 1.0f, false);
+  const bf16x2 x3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c[1], 1.0f, true);
+  return bf16x8{x0[0], x0[1], x1[0], x1[1], x2[0], x2[1], x3[0], x3[1]};
+}
+
+// The copy offsets of a cache with rows of ROW bytes: lane i of copy rb
+// writes row 8rb + i/8, position i%8 of a column group and so fetches
+// source chunk (i%8) ^ row_swz(row) (of at most CHUNKS chunks: beyond, the
+// last one again; rows at and beyond row_cap read row row_cap).
+template <int ROW, int CHUNKS>
+__device__ __forceinline__ uint32_t dma_lane_off_fmt(int lane, int rb, int row_cap) {
+  int row = 8 * rb + (lane >> 3);
+  int src_chunk = (lane & 7) ^ row_swz(row);
+  if constexpr (CHUNKS < 8) src_chunk = min(src_chunk, CHUNKS - 1);
+  row = row < row_cap ? row : row_cap;
+  return (uint32_t)(row * ROW + 16 * src_chunk);
 }
 
 // The P tile: [row][position] bf16, 80-byte rows (the 16-byte reads of 16
@@ -90,6 +151,26 @@ __device__ __forceinline__ uint32_t ws_kaddr(int th, int lane, int odd) {
   const int m = 16 * th + (lane & 15);
   const int c = 4 * odd + (lane >> 4);
   return m * 128 + 16 * (c ^ row_swz(m));
+}
+
+// LDS address (slot-relative) of the 8 codes a lane reads for k-step i
+// (0..3) of a 128-column group: row m = 16th + (lane & 15), columns 32i +
+// 8(lane/16) .. +7, i.e. chunk 2i + lane/32 of the group, half lane/16 % 2.
+__device__ __forceinline__ uint32_t ws_kaddr8(int th, int lane, int i) {
+  const int m = 16 * th + (lane & 15), g4 = lane >> 4;
+  return m * 128 + 16 * ((2 * i + (g4 >> 1)) ^ row_swz(m)) + 8 * (g4 & 1);
+}
+
+// 8-bit transposing V^T reads of value wave v (column group v): for k-step
+// ks the eight lane pairs of each 16-lane group G supply rows 16ks + 8(G>>1)
+// .. +7 (pair 2k, 2k+1: row k, bytes 16(G&1) + 8(lane&1) of the 32-column
+// block), and lane l receives column l%32 of those eight tokens in natural
+// order.  Column block cb only flips address bits 5 and 6 (the chunk bits
+// above the half-block bit): address = vaddr8 ^ 32cb.
+__device__ __forceinline__ uint32_t ws_vaddr8(int v, int lane, int ks) {
+  const int m = 16 * ks + 8 * (lane >> 5) + ((lane & 15) >> 1);
+  const int swz = row_swz(m), g1 = (lane >> 4) & 1;
+  return kGroupBytes * v + m * 128 + 32 * ((swz >> 1) & 3) + 16 * (g1 ^ (swz & 1)) + 8 * (lane & 1);
 }
 
 // Transposing V reads of value wave v: for column block cb (columns
@@ -149,6 +230,72 @@ __device__ __forceinline__ void ws_scores(const lds_char* buf, const uint32_t (&
     s[1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kb[g % kKRead], qf[g][1], g == 0 ? f32x4{} : s[1], 0, 0, 0);
   }
   __builtin_amdgcn_sched_barrier(0);
+}
+
+// Score wave, QK^T of one slot of e4m3 codes: S^T[16 tokens][32 rows], each
+// code fragment converted to bf16 as it is read.  Per-tile scales (F =
+// kFmtFp8): each 128-column tile sums into an accumulator of its own and is
+// added with the token's tile scale (sc[e][t]: token e of the lane, tile t);
+// the bf16 rope adds unscaled.  Per-tensor codes: one accumulation, the
+// scale applies outside.
+template <int F>
+__device__ __forceinline__ void ws_scores8(const lds_char* buf, const uint32_t (&ka)[4], const uint32_t (&kr)[2],
+                                           const bf16x8 (&qf)[kQk][2], const f32x4 (&sc)[4], f32x4 (&s)[2]) {
+  if constexpr (F == kFmtFp8) {
+    // rope first (bf16 as stored, group 4)
+#pragma unroll
+    for (int g = 0; g < 2; ++g) {
+      const bf16x8 kb = *(const LDS_AS bf16x8*)(buf + kr[g]);
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+        s[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kb, qf[16 + g][j], g == 0 ? f32x4{} : s[j], 0, 0, 0);
+    }
+    u32x2 raw[2][4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) raw[0][i] = *(const LDS_AS u32x2*)(buf + ka[i]);
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      if (t + 1 < 4) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) raw[(t + 1) & 1][i] = *(const LDS_AS u32x2*)(buf + ka[i] + kGroupBytes * (t + 1));
+      }
+      f32x4 tt[2];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const bf16x8 kb = codes_bf16(raw[t & 1][i]);
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+          tt[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kb, qf[4 * t + i][j], i == 0 ? f32x4{} : tt[j], 0, 0, 0);
+      }
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) s[j][e] = __builtin_fmaf(sc[e][t], tt[j][e], s[j][e]);
+    }
+  } else {
+    u32x2 raw[2][4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) raw[0][i] = *(const LDS_AS u32x2*)(buf + ka[i]);
+#pragma unroll
+    for (int t = 0; t < 5; ++t) {
+      // groups 0..3: codes of the 512 latent columns; group 4: the 64 rope codes
+      const int nk = t < 4 ? 4 : 2;
+      if (t + 1 < 5) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          if (t + 1 < 4 || i < 2) raw[(t + 1) & 1][i] = *(const LDS_AS u32x2*)(buf + ka[i] + kGroupBytes * (t + 1));
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        if (i >= nk) break;
+        const bf16x8 kb = codes_bf16(raw[t & 1][i]);
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+          s[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kb, qf[4 * t + i][j], t == 0 && i == 0 ? f32x4{} : s[j], 0, 0,
+                                                         0);
+      }
+    }
+  }
 }
 
 // LDS shared by the two roles.
@@ -217,7 +364,7 @@ __device__ __forceinline__ void for_segments(const DecodeArgs& a, const Plan& pl
 
 // ---------------------------------------------------------------- score waves
 
-template <bool Q_FP8, bool CAUSAL>
+template <int F, bool Q_FP8, bool CAUSAL>
 __device__ __forceinline__ void score_role(const DecodeArgs& a, const Plan& pl, const WsLds& L, int w, int lane,
                                            int row0, int r) {
   // (lane and wave pass through empty asm statements: nothing computed from
@@ -226,7 +373,8 @@ __device__ __forceinline__ void score_role(const DecodeArgs& a, const Plan& pl, 
   asm volatile("" : "+v"(lane), "+s"(w));
   const int hb = w & 1, th = w >> 1;
   const int i16 = lane & 15, g4 = lane >> 4;
-  const float scale_log2 = a.scale_log2;
+  // per-tensor codes: value = code / k_scale_inv, folded into the score scale
+  const float scale_log2 = F == kFmtFp8T ? a.scale_log2 * (1.0f / a.kv_scales[0]) : a.scale_log2;
   int qrow[2], lag[2] = {0, 0};
   bool qok[2];
 #pragma unroll
@@ -236,9 +384,18 @@ __device__ __forceinline__ void score_role(const DecodeArgs& a, const Plan& pl, 
     if constexpr (CAUSAL) lag[j] = a.tq - 1 - min(qrow[j], a.heads - 1) / a.heads_tok;
   }
   const uint32_t ka[2] = {ws_kaddr(th, lane, 0), ws_kaddr(th, lane, 1)};
+  uint32_t ka8[4], kr8[2];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) ka8[i] = ws_kaddr8(th, lane, i);
+  // rope of the tile format: bf16 in group 4, read as the bf16 cache's
+  // column groups are
+#pragma unroll
+  for (int i = 0; i < 2; ++i) kr8[i] = 4 * kGroupBytes + ws_kaddr(th, lane, i);
   // this lane's four p of block j: row 32hb + 16j + i16 of the P tile,
-  // positions 16th + 4*pi-group(lane / 16) .. +3
-  const int g4p = ((g4 & 1) << 1) | (g4 >> 1);
+  // positions 16th + 4*pi-group(lane / 16) .. +3 (bf16 cache: the order of
+  // the 16-bit transposing V reads) or 16th + 4(lane/16) .. +3 (codes: the
+  // 8-bit transposing reads keep the natural order)
+  const int g4p = F == kFmtBf16 ? ((g4 & 1) << 1) | (g4 >> 1) : g4;
   uint32_t pw[2];
 #pragma unroll
   for (int j = 0; j < 2; ++j) pw[j] = (32 * hb + 16 * j + i16) * kPRowBytes + (16 * th + 4 * g4p) * 2;
@@ -283,12 +440,18 @@ __device__ __forceinline__ void score_role(const DecodeArgs& a, const Plan& pl, 
       barrier();  // B_0: slot 0 landed
       for (int it = 0; it <= nslots; ++it) {
         if (it < nslots) {
-          const lds_char* buf = L.ring + (it & (kRing - 1)) * kSlotBytes;
+          const lds_char* buf = L.ring + (it & (kRing - 1)) * WsFmt<F>::kSlot;
           f32x4 s[2];
+          f32x4 sc[4];  // tile format: tile scales of this lane's tokens 16th + 4(lane/16) + e
+          if constexpr (F == kFmtFp8) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) sc[e] = *(const LDS_AS f32x4*)(buf + WsFmt<F>::kScaleOff + 16 * (16 * th + 4 * g4 + e));
+          }
           // the score MFMAs go first on the SIMD's matrix core; the value
           // wave's MFMAs then fill the time of this wave's softmax
           __builtin_amdgcn_s_setprio(1);
-          ws_scores(buf, ka, qf, s);
+          if constexpr (F == kFmtBf16) ws_scores(buf, ka, qf, s);
+          else ws_scores8<F>(buf, ka8, kr8, qf, sc, s);
           __builtin_amdgcn_s_setprio(0);
           const int tk = sgm.sg.tok0 + it * kTS + 16 * th + 4 * g4;  // this lane's first token
           if (sgm.sg.tok0 + it * kTS + kTS > lim_lo) {
@@ -320,7 +483,20 @@ __device__ __forceinline__ void score_role(const DecodeArgs& a, const Plan& pl, 
 #pragma unroll
             for (int e = 0; e < 4; ++e) pj[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[j][e], scale_log2, nref));
             lsum[j] += (pj[0] + pj[1]) + (pj[2] + pj[3]);
-            *(LDS_AS bf16x4*)(L.ptile + (it & 1) * kPTile + pw[j]) = __builtin_convertvector(pj, bf16x4);
+            lds_char* pt = L.ptile + (it & 1) * WsFmt<F>::kPTiles * kPTile + pw[j];
+            if constexpr (F == kFmtFp8) {
+              // one P tile per column tile, p times the token's tile scale
+              // rounded once to bf16: the codes then serve as that tile's V
+#pragma unroll
+              for (int t = 0; t < 4; ++t) {
+                f32x4 pt4;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) pt4[e] = pj[e] * sc[e][t];
+                *(LDS_AS bf16x4*)(pt + t * kPTile) = __builtin_convertvector(pt4, bf16x4);
+              }
+            } else {
+              *(LDS_AS bf16x4*)pt = __builtin_convertvector(pj, bf16x4);
+            }
           }
           wait_vm_lgkm0<0>();
         }
@@ -373,21 +549,34 @@ __device__ __forceinline__ void score_role(const DecodeArgs& a, const Plan& pl, 
 
 // ---------------------------------------------------------------- value waves
 
+typedef u32x2 VFrag8[2];  // [ks]: 8 codes of column lane%32, tokens 16ks + 8(lane/32) .. +7
+
+template <int F>
 __device__ __forceinline__ void value_role(const DecodeArgs& a, const Plan& pl, const WsLds& L, int v, int lane,
                                            int row0, int r) {
+  typedef WsFmt<F> Fm;
+  constexpr int N = Fm::kOps;
+  typedef typename std::conditional<F == kFmtBf16, VFrag, VFrag8>::type VF;
   asm volatile("" : "+v"(lane), "+s"(v));  // (as in score_role)
   const int i32 = lane & 31, h2 = lane >> 5;
   // P fragment (A operand) of row block rb, k-step ks: row 32rb + i32 of the
   // tile, positions 16ks + 8h2 .. +7
   const uint32_t prd = i32 * kPRowBytes + 16 * h2;
-  const uint32_t va[2] = {ws_vaddr(v, lane, 0), ws_vaddr(v, lane, 1)};
-  // copies: this wave takes column groups 2v and 2v+1 of all 32 rows (the V
-  // columns it multiplies) and rows 8v .. 8v+7 of the rope group 8, nine
-  // copies of 1 KB per slot
+  const uint32_t va[2] = {F == kFmtBf16 ? ws_vaddr(v, lane, 0) : ws_vaddr8(v, lane, 0),
+                          F == kFmtBf16 ? ws_vaddr(v, lane, 1) : ws_vaddr8(v, lane, 1)};
+  // P tile of this wave (tile format: the one scaled for its column tile v)
+  const uint32_t ptv = F == kFmtFp8 ? v * kPTile : 0;
+  // copies: this wave takes the column groups it multiplies (bf16: 2v and
+  // 2v+1; codes: v) of all 32 rows and rows 8v .. 8v+7 of the rope group
+  // (bf16: group 8; codes: group 4; the per-tensor rope codes fill half of
+  // it), plus, for the tile format, a copy of the 32 rows' scales
+  constexpr int kChunks = F == kFmtFp8T ? 4 : 8;  // source chunks of a row in the rope group
   uint32_t dfull[4];
 #pragma unroll
-  for (int rb = 0; rb < 4; ++rb) dfull[rb] = dma_lane_off(lane, rb, kTS);
-  const uint32_t dfull_r = dma_lane_off(lane, v, kTS);
+  for (int rb = 0; rb < 4; ++rb) dfull[rb] = dma_lane_off_fmt<Fm::kRow, 8>(lane, rb, kTS);
+  const uint32_t dfull_r = dma_lane_off_fmt<Fm::kRow, kChunks>(lane, v, kTS);
+  // per-tensor codes: value = code / k_scale_inv, applied at the output
+  const float kdesc = F == kFmtFp8T ? 1.0f / a.kv_scales[0] : 1.0f;
 
 
   for_segments(a, pl, [&](const WsSeg& sgm) {
@@ -399,7 +588,8 @@ __device__ __forceinline__ void value_role(const DecodeArgs& a, const Plan& pl, 
     // this wave's copies of slot s into ring position pos (s < nslots)
     auto dma_cols = [&](int s, int pos) {
       const int page = page_of(pc, sg.bt_seg, s >> 1, sg.npages, lane, a.num_pages);
-      const char* src = a.kv + ((size_t)page * kPage + (s & 1) * kTS) * kRowBytes;
+      const size_t row0s = (size_t)page * kPage + (s & 1) * kTS;  // cache row of the slot's token 0
+      const char* src = a.kv + row0s * Fm::kRow;
       const int nvalid = min(kTS, sg.tok1 - (sg.tok0 + s * kTS));
       uint32_t off[4], offr;
       if (nvalid >= kTS) {
@@ -409,19 +599,35 @@ __device__ __forceinline__ void value_role(const DecodeArgs& a, const Plan& pl, 
       } else {
         // rows at and beyond the valid count re-read the last valid row
 #pragma unroll
-        for (int rb = 0; rb < 4; ++rb) off[rb] = dma_lane_off(lane, rb, nvalid - 1);
-        offr = dma_lane_off(lane, v, nvalid - 1);
+        for (int rb = 0; rb < 4; ++rb) off[rb] = dma_lane_off_fmt<Fm::kRow, 8>(lane, rb, nvalid - 1);
+        offr = dma_lane_off_fmt<Fm::kRow, kChunks>(lane, v, nvalid - 1);
       }
-      const char* s0 = uniform_ptr(src + 256 * v);  // column group 2v
-      const char* s8 = uniform_ptr(src + 8 * 128);  // the rope group
-      const uint32_t base = __builtin_amdgcn_readfirstlane(lds_addr(L.ring + (pos & (kRing - 1)) * kSlotBytes));
+      const uint32_t base = __builtin_amdgcn_readfirstlane(lds_addr(L.ring + (pos & (kRing - 1)) * Fm::kSlot));
+      if constexpr (F == kFmtBf16) {
+        const char* s0 = uniform_ptr(src + 256 * v);  // column group 2v
+        const char* s8 = uniform_ptr(src + 8 * 128);  // the rope group
 #pragma unroll
-      for (int rb = 0; rb < 4; ++rb) {
-        // (the immediate offset moves the source and the destination alike)
-        dma16<0>(s0, off[rb], base + (2 * v) * kGroupBytes + rb * 1024);
-        dma16<128>(s0, off[rb], base + (2 * v + 1) * kGroupBytes + rb * 1024 - 128);
+        for (int rb = 0; rb < 4; ++rb) {
+          // (the immediate offset moves the source and the destination alike)
+          dma16<0>(s0, off[rb], base + (2 * v) * kGroupBytes + rb * 1024);
+          dma16<128>(s0, off[rb], base + (2 * v + 1) * kGroupBytes + rb * 1024 - 128);
+        }
+        dma16<0>(s8, offr, base + 8 * kGroupBytes + v * 1024);
+      } else {
+        const char* s0 = uniform_ptr(src + 128 * v);  // codes group v
+        const char* s4 = uniform_ptr(src + 512);      // rope group
+#pragma unroll
+        for (int rb = 0; rb < 4; ++rb) dma16<0>(s0, off[rb], base + v * kGroupBytes + rb * 1024);
+        dma16<0>(s4, offr, base + 4 * kGroupBytes + v * 1024);
+        if constexpr (F == kFmtFp8) {
+          // the slot's 32 rows of tile scales (16 bytes each): lanes 0..31
+          // rows 0..31, lanes 32..63 again (into the second half of this
+          // wave's 1 KB, never read); past the valid rows the last valid one
+          const char* ssrc = uniform_ptr((const char*)(a.kv_scales + row0s * 4));
+          const uint32_t soff = (uint32_t)(16 * min(lane & 31, nvalid - 1));
+          dma16<0>(ssrc, soff, base + Fm::kScaleOff + v * 1024);
+        }
       }
-      dma16<0>(s8, offr, base + 8 * kGroupBytes + v * 1024);
     };
     for (int pass = 0; pass < 2; ++pass) {
       f32x16 o[2][4];
@@ -437,18 +643,31 @@ __device__ __forceinline__ void value_role(const DecodeArgs& a, const Plan& pl, 
       if (pre > 0) dma_cols(0, 0);
       if (pass == 0) barrier();
       for (int s = 1; s < pre; ++s) dma_cols(s, s);
-      wait_ops_lgkm0(epoch_ops(-2, nslots) + epoch_ops(-1, nslots));
+      wait_ops_lgkm0<N>(epoch_ops<N>(-2, nslots) + epoch_ops<N>(-1, nslots));
       barrier();  // B_0
-      VFrag vx[4], vy[4];
+      VF vx[4], vy[4];
       // iteration it (between B_it and B_it+1): epoch it issues the copies of
       // slot it+3 (into the ring position of slot it-1, whose last reads were
       // in iteration it-1); PV of slot it-1 from vc, while the V fragments of
       // slot it (landed before B_it) are read into vn for the next iteration
-      auto iteration = [&](int it, VFrag (&vc)[4], VFrag (&vn)[4]) {
+      auto iteration = [&](int it, VF (&vc)[4], VF (&vn)[4]) {
         if (it + 3 < nslots) dma_cols(it + 3, it + 3);
-        const lds_char* nbuf = L.ring + (it & (kRing - 1)) * kSlotBytes;
+        const lds_char* nbuf = L.ring + (it & (kRing - 1)) * Fm::kSlot;
+        // this wave's V^T fragments of slot it, column block cb
+        auto vload = [&](int cb, VF& f) {
+          if constexpr (F == kFmtBf16) {
+            ws_vload(nbuf, va, cb, f);
+          } else {
+            typedef int v2i __attribute__((ext_vector_type(2)));
+#pragma unroll
+            for (int ks = 0; ks < 2; ++ks) {
+              const v2i x = __builtin_amdgcn_ds_read_tr8_b64_v2i32((LDS_AS v2i*)(nbuf + (va[ks] ^ (32u * cb))));
+              f[ks] = u32x2{(uint32_t)x[0], (uint32_t)x[1]};
+            }
+          }
+        };
         if (it >= 1) {
-          const lds_char* pt = L.ptile + ((it - 1) & 1) * kPTile;
+          const lds_char* pt = L.ptile + ((it - 1) & 1) * Fm::kPTiles * kPTile + ptv;
           bf16x8 pf[2][2];
 #pragma unroll
           for (int rb = 0; rb < 2; ++rb)
@@ -456,24 +675,30 @@ __device__ __forceinline__ void value_role(const DecodeArgs& a, const Plan& pl, 
             for (int ks = 0; ks < 2; ++ks) pf[rb][ks] = *(const LDS_AS bf16x8*)(pt + prd + rb * 32 * kPRowBytes + 32 * ks);
 #pragma unroll
           for (int cb = 0; cb < 4; ++cb) {
-            const bf16x8 v0 = __builtin_shufflevector(vc[cb][0], vc[cb][1], 0, 1, 2, 3, 4, 5, 6, 7);
-            const bf16x8 v1 = __builtin_shufflevector(vc[cb][2], vc[cb][3], 0, 1, 2, 3, 4, 5, 6, 7);
+            bf16x8 v0, v1;
+            if constexpr (F == kFmtBf16) {
+              v0 = __builtin_shufflevector(vc[cb][0], vc[cb][1], 0, 1, 2, 3, 4, 5, 6, 7);
+              v1 = __builtin_shufflevector(vc[cb][2], vc[cb][3], 0, 1, 2, 3, 4, 5, 6, 7);
+            } else {
+              v0 = codes_bf16(vc[cb][0]);
+              v1 = codes_bf16(vc[cb][1]);
+            }
 #pragma unroll
             for (int rb = 0; rb < 2; ++rb) {
               o[rb][cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(v0, pf[rb][0], o[rb][cb], 0, 0, 0);
               o[rb][cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(v1, pf[rb][1], o[rb][cb], 0, 0, 0);
             }
-            if (it < nslots) ws_vload(nbuf, va, cb, vn[cb]);
+            if (it < nslots) vload(cb, vn[cb]);
           }
         } else if (it < nslots) {
 #pragma unroll
-          for (int cb = 0; cb < 4; ++cb) ws_vload(nbuf, va, cb, vn[cb]);
+          for (int cb = 0; cb < 4; ++cb) vload(cb, vn[cb]);
         }
         if (pass == 0 && it == 0) barrier();  // the score waves' reference exchange
         // slot it+1 landed (the operations of epochs it-1 and it may stay in
         // flight), and this wave's LDS reads of slot it are done before the
         // next iteration's copies refill the ring position of slot it-1
-        wait_ops_lgkm0(epoch_ops(it - 1, nslots) + epoch_ops(it, nslots));
+        wait_ops_lgkm0<N>(epoch_ops<N>(it - 1, nslots) + epoch_ops<N>(it, nslots));
         barrier();  // B_it+1
       };
       for (int it = 0; it <= nslots; it += 2) {
@@ -496,7 +721,7 @@ __device__ __forceinline__ void value_role(const DecodeArgs& a, const Plan& pl, 
         for (int rb = 0; rb < 2; ++rb) {
           const int lr = 32 * rb + i32;
           const float lt = L.xl[lr] + L.xl[64 + lr];
-          const float inv = lt > 0.0f ? 1.0f / lt : 0.0f;
+          const float inv = lt > 0.0f ? kdesc / lt : 0.0f;
           const int row = row0 + lr;
           if (row < a.heads) {
             __bf16* orow = (__bf16*)a.out + ((size_t)b * a.heads + row) * kDV + 128 * v + 4 * h2;
@@ -524,11 +749,12 @@ __device__ __forceinline__ void value_role(const DecodeArgs& a, const Plan& pl, 
   });
 }
 
-template <bool Q_FP8, bool CAUSAL>
+template <int F, bool Q_FP8, bool CAUSAL>
 __global__ void __attribute__((amdgpu_flat_work_group_size(kWsThreads, kWsThreads), amdgpu_waves_per_eu(2, 2)))
 mla_decode_ws_kernel(DecodeArgs a) {
-  __shared__ __attribute__((aligned(1024))) char ring_mem[kRing * kSlotBytes];  // KV ring, 4 x 36 KB
-  __shared__ __attribute__((aligned(16))) char ptile_mem[2 * kPTile];           // P tiles, 2 x 5 KB
+  // KV ring (4 slots) and P tiles (two slots' worth)
+  __shared__ __attribute__((aligned(1024))) char ring_mem[kRing * WsFmt<F>::kSlot];
+  __shared__ __attribute__((aligned(16))) char ptile_mem[2 * WsFmt<F>::kPTiles * kPTile];
   __shared__ __attribute__((aligned(16))) float xs[512];                        // row exchanges, votes
   WsLds L;
   L.ring = (lds_char*)ring_mem;
@@ -560,22 +786,35 @@ mla_decode_ws_kernel(DecodeArgs a) {
   }
   if (!has_work) return;
   const int row0 = slab * kWsRows;
-  if (w < 4) score_role<Q_FP8, CAUSAL>(a, pl, L, w, lane, row0, r);
-  else value_role(a, pl, L, w - 4, lane, row0, r);
+  if (w < 4) score_role<F, Q_FP8, CAUSAL>(a, pl, L, w, lane, row0, r);
+  else value_role<F>(a, pl, L, w - 4, lane, row0, r);
 }
 
 }  // namespace
 
 bool decode_ws_supported(int32_t kv_format, int32_t topk, int32_t eff_heads) {
-  return kv_format == kKvFormatBf16 && topk == 0 && eff_heads >= kWsRows;
+  return topk == 0 && eff_heads >= kWsRows;
 }
 
-hipError_t launch_decode_ws(const DecodeArgs& a, bool q_fp8, bool causal, hipStream_t stream) {
+hipError_t launch_decode_ws(const DecodeArgs& a, int32_t kv_format, bool q_fp8, bool causal, hipStream_t stream) {
   const dim3 grid(a.per_xcd * 8 * a.slabs), block(kWsThreads);
-  if (!q_fp8 && !causal) hipLaunchKernelGGL((mla_decode_ws_kernel<false, false>), grid, block, 0, stream, a);
-  if (!q_fp8 && causal) hipLaunchKernelGGL((mla_decode_ws_kernel<false, true>), grid, block, 0, stream, a);
-  if (q_fp8 && !causal) hipLaunchKernelGGL((mla_decode_ws_kernel<true, false>), grid, block, 0, stream, a);
-  if (q_fp8 && causal) hipLaunchKernelGGL((mla_decode_ws_kernel<true, true>), grid, block, 0, stream, a);
+#define MLA_WS_LAUNCH(F, QF, C)                                                                          \
+  if (fmt == F && q_fp8 == QF && causal == C)                                                            \
+    hipLaunchKernelGGL((mla_decode_ws_kernel<F, QF, C>), grid, block, 0, stream, a);
+  const int fmt = kv_format == kKvFormatFp8Tile ? kFmtFp8 : kv_format == kKvFormatFp8Tensor ? kFmtFp8T : kFmtBf16;
+  MLA_WS_LAUNCH(kFmtBf16, false, false)
+  MLA_WS_LAUNCH(kFmtBf16, false, true)
+  MLA_WS_LAUNCH(kFmtBf16, true, false)
+  MLA_WS_LAUNCH(kFmtBf16, true, true)
+  MLA_WS_LAUNCH(kFmtFp8, false, false)
+  MLA_WS_LAUNCH(kFmtFp8, false, true)
+  MLA_WS_LAUNCH(kFmtFp8, true, false)
+  MLA_WS_LAUNCH(kFmtFp8, true, true)
+  MLA_WS_LAUNCH(kFmtFp8T, false, false)
+  MLA_WS_LAUNCH(kFmtFp8T, false, true)
+  MLA_WS_LAUNCH(kFmtFp8T, true, false)
+  MLA_WS_LAUNCH(kFmtFp8T, true, true)
+#undef MLA_WS_LAUNCH
   return hipGetLastError();
 }
 
