@@ -417,11 +417,10 @@ __device__ __forceinline__ void score_role(const DecodeArgs& a, const Plan& pl, 
       const int rr = qok[j] ? qrow[j] : 0;
       if constexpr (!Q_FP8) {
         const bf16x8* qp = (const bf16x8*)((const __bf16*)a.q + ((size_t)b * a.heads + rr) * kD);
+        // (rows past the heads read row 0: finite scores for rows that are
+        // never stored, and no use of the loaded data before barrier Y)
 #pragma unroll
-        for (int k = 0; k < kQk; ++k) {
-          const bf16x8 x = qp[4 * k + g4];
-          qf[k][j] = qok[j] ? x : bf16x8{};
-        }
+        for (int k = 0; k < kQk; ++k) qf[k][j] = qp[4 * k + g4];
       } else {
         const uint2* qp = (const uint2*)((const uint8_t*)a.q + ((size_t)b * a.heads + rr) * kD);
 #pragma unroll
@@ -431,6 +430,7 @@ __device__ __forceinline__ void score_role(const DecodeArgs& a, const Plan& pl, 
         }
       }
     }
+    barrier();  // Y: the query loads are issued; the value waves copy slots 1 and 2 behind them
     wait_vm_lgkm0<0>();
 
     float ref[2] = {-INFINITY, -INFINITY};  // base-2 reference per row
@@ -638,10 +638,14 @@ __device__ __forceinline__ void value_role(const DecodeArgs& a, const Plan& pl, 
       // copy epochs -3 .. -1 (the prologue): slots 0 .. 2; slot 0 landed
       const int pre = min(nslots, 3);
       // slot 0 first, then X: the score waves load their queries only after
-      // these copies are issued, so that slot 0 is not queued behind them
-      // (slots 1 and 2 follow, beside the query loads)
+      // these copies are issued, so that slot 0 is not queued behind them;
+      // slots 1 and 2 follow after Y, behind the query loads, which the first
+      // slot needs sooner
       if (pre > 0) dma_cols(0, 0);
-      if (pass == 0) barrier();
+      if (pass == 0) {
+        barrier();  // X
+        barrier();  // Y
+      }
       for (int s = 1; s < pre; ++s) dma_cols(s, s);
       wait_ops_lgkm0<N>(epoch_ops<N>(-2, nslots) + epoch_ops<N>(-1, nslots));
       barrier();  // B_0
