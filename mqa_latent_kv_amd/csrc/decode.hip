@@ -1535,7 +1535,7 @@ hipError_t launch_decode(const DecodeLaunch& din, hipStream_t stream) {
                   : d.kv_format == kKvFormatFp8Tensor ? (d.topk > 0 ? kKvFp8TTopK : kKvFp8T)
                                                       : (d.topk > 0 ? kKvBf16TopK : kKvBf16);
   hipError_t e;
-  if (decode_ws_supported(d.kv_format, d.topk, d.heads)) {
+  if (decode_ws_supported(d.kv_format, d.topk, d.heads, d.num_pages)) {
     // dense bf16 pages with at least 64 rows per sequence: the wave-specialised
     // kernel (decode_ws.hip), the same plan, slabs of 64 rows and workspace
     a.seg_pad = kWsSegPad;

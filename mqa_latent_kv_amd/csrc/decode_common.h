@@ -96,15 +96,48 @@ struct Plan {
   int end;    // one past the last
   int b0;     // first sequence overlapping [start, end)
   int p0;     // global index of b0's first unit
+  int pad;    // virtual units at each end of every non-empty sequence on the line
 };
 
-// Units of sequence b on the split line: its pages (or top-k pages) plus
-// a.seg_pad virtual units at each end when it has any.
-__device__ __forceinline__ int line_units(const DecodeArgs& a, int b) {
-  const int n = units_of(a, b);
-  return n > 0 ? n + 2 * a.seg_pad : 0;
+// inclusive scan over the lanes of a wave (ds_bpermute moves data between
+// lanes; it touches no LDS memory)
+__device__ __forceinline__ int wave_incl_scan(int v, int lane) {
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int t = __builtin_amdgcn_ds_bpermute((lane - off) << 2, v);
+    v += lane >= off ? t : 0;
+  }
+  return v;
 }
 
+// Block-wide exclusive scan of one int per thread (NT threads); every
+// thread also gets the total.  scratch: NT/64 ints; two barriers.
+template <int NT>
+__device__ __forceinline__ int block_excl_scan(int v, int* scratch, int& total) {
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int incl = wave_incl_scan(v, lane);
+  if (lane == 63) scratch[wv] = incl;
+  __syncthreads();
+  int before = 0;
+  total = 0;
+#pragma unroll
+  for (int i = 0; i < (NT / 64); ++i) {
+    const int t = scratch[i];
+    before += i < wv ? t : 0;
+    total += t;
+  }
+  __syncthreads();
+  return before + incl - v;
+}
+
+// The range of workgroup r.  The units of all sequences (pages, or top-k
+// chunks of 64 entries) are laid end to end and cut into a.ranges equal
+// ranges.  With a.seg_pad > 0 each non-empty sequence also gets that many
+// virtual units at each end (the cost of a segment's start and end), but
+// only when some sequence starts strictly inside a range of the unpadded
+// cut: when every boundary falls on a cut (sequences of equal length, a
+// whole number of ranges each), every range runs one segment and the pads
+// would only unbalance them.
 // (NT threads per workgroup; scratch holds NT + 2 ints)
 template <int NT>
 __device__ bool make_plan(const DecodeArgs& a, int r, int* scratch, Plan& pl) {
@@ -112,38 +145,41 @@ __device__ bool make_plan(const DecodeArgs& a, int r, int* scratch, Plan& pl) {
   const int B = a.batch;
   const int per = (B + NT - 1) / NT;
   const int lo = tid * per, hi = min(B, lo + per);
-  int local = 0;
-  for (int b = lo; b < hi; ++b) local += line_units(a, b);
-  // inclusive scan of the per-thread sums: within each wave by cross-lane
-  // reads (ds_bpermute moves data between lanes, it touches no LDS memory),
-  // then the four wave totals through LDS behind a single barrier
-  const int lane = tid & 63, wv = tid >> 6;
-  int incl = local;
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const int v = __builtin_amdgcn_ds_bpermute((lane - off) << 2, incl);
-    incl += lane >= off ? v : 0;
+  int units = 0, seqs = 0;
+  for (int b = lo; b < hi; ++b) {
+    const int n = units_of(a, b);
+    units += n;
+    seqs += n > 0 ? 1 : 0;
   }
-  if (lane == 63) scratch[wv] = incl;
-  __syncthreads();
-  int before = 0, total = 0;
-#pragma unroll
-  for (int i = 0; i < (NT / 64); ++i) {
-    const int t = scratch[i];
-    before += i < wv ? t : 0;
-    total += t;
+  int total0 = 0, nseq = 0;
+  const int excl0 = block_excl_scan<NT>(units, scratch, total0);
+  const int exclq = block_excl_scan<NT>(seqs, scratch, nseq);
+  if (total0 == 0) return false;
+  int pad = 0;
+  if (a.seg_pad > 0) {
+    const int C0 = (total0 + a.ranges - 1) / a.ranges;
+    int inside = 0, p = excl0;
+    for (int b = lo; b < hi; ++b) {
+      const int n = units_of(a, b);
+      inside += (n > 0 && p % C0 != 0) ? 1 : 0;
+      p += n;
+    }
+    int any = 0;
+    block_excl_scan<NT>(inside, scratch, any);
+    pad = any > 0 ? a.seg_pad : 0;
   }
-  incl += before;
-  const int excl = incl - local;
-  __syncthreads();
-  if (total == 0) return false;
+  // padded line: sequence b starts at (its unpadded start) + 2 pad (non-empty sequences before it)
+  const int total = total0 + 2 * pad * nseq;
+  const int excl = excl0 + 2 * pad * exclq;
+  const int incl = excl + units + 2 * pad * seqs;
   const int C = (total + a.ranges - 1) / a.ranges;
   const int start = r * C;
   if (start >= total) return false;
   if (start >= excl && start < incl) {
     int p = excl;
     for (int b = lo; b < hi; ++b) {
-      int n = line_units(a, b);
+      const int u = units_of(a, b);
+      const int n = u > 0 ? u + 2 * pad : 0;
       if (start < p + n) {
         scratch[NT] = b;
         scratch[NT + 1] = p;
@@ -159,6 +195,7 @@ __device__ bool make_plan(const DecodeArgs& a, int r, int* scratch, Plan& pl) {
   pl.end = __builtin_amdgcn_readfirstlane(min(start + C, total));
   pl.b0 = __builtin_amdgcn_readfirstlane(scratch[NT]);
   pl.p0 = __builtin_amdgcn_readfirstlane(scratch[NT + 1]);
+  pl.pad = __builtin_amdgcn_readfirstlane(pad);
   __syncthreads();
   return true;
 }

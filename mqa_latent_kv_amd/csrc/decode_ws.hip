@@ -111,6 +111,26 @@ __device__ __forceinline__ void wait_ops_lgkm0(int k) {
   else if (k == N) wait_vm_lgkm0<N>();
   else wait_vm_lgkm0<0>();
 }
+// the same with x (2 or 4) more operations allowed in flight: the top-k
+// staging loads of one or two epochs
+template <int N>
+__device__ __forceinline__ void wait_ops_lgkm0(int k, int x) {
+  if (x == 4) {
+    if (k == 2 * N) wait_vm_lgkm0<2 * N + 4>();
+    else if (k == N) wait_vm_lgkm0<N + 4>();
+    else wait_vm_lgkm0<4>();
+  } else {
+    if (k == 2 * N) wait_vm_lgkm0<2 * N + 2>();
+    else if (k == N) wait_vm_lgkm0<N + 2>();
+    else wait_vm_lgkm0<2>();
+  }
+}
+
+// One direct global->LDS copy of 4 bytes per lane (lane i's word lands at
+// lds_base + 4i), issued and accounted like the 16-byte copies.
+__device__ __forceinline__ void dma4(const char* sbase, uint32_t voff, uint32_t lds_base) {
+  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dword %0, %1" ::"v"(voff), "s"(sbase), "s"(lds_base) : "memory");
+}
 
 // 8 e4m3 codes as bf16 (exact: every e4m3 value is a bf16 value)
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
@@ -306,7 +326,11 @@ struct WsLds {
   LDS_AS float* xl;    // [half][row]: sums of p
   LDS_AS float* xm;    // [half][row]: largest scores seen (base 2)
   LDS_AS int* votes;   // [score wave]: redo votes
+  LDS_AS uint32_t* tkmask;  // top-k: [ring position] validity of the slot's 32 entries
+  LDS_AS int32_t* tk;       // top-k: per value wave, entries [8][64] then their pages [8][64]
 };
+
+constexpr int kTkWords = 8 * 64 + 8 * 64;  // top-k staging words per value wave
 
 // A wave-uniform load of table data that no kernel writes (sequence
 // lengths): through the scalar cache rather than the vector memory pipeline,
@@ -325,15 +349,15 @@ struct WsSeg {
 
 // Calls body(seg) for every segment of the range, in order, with a barrier
 // between segments (every wave is done with the ring and the exchanges).
-template <class F>
+template <bool TOPK, class F>
 __device__ __forceinline__ void for_segments(const DecodeArgs& a, const Plan& pl, F&& body) {
   // p: line position of sequence b; its pages are units [p + pad, p + pad + n)
-  const int pad = a.seg_pad;
+  const int pad = pl.pad;
   int b = pl.b0, p = pl.p0;
   bool first = true;
   while (true) {
-    // (dense decode: a sequence's units are its pages)
-    const int seglen = min(max(ld_uniform(a.seqlens + b), 0), a.max_pages * kPage);
+    // dense: a sequence's units are its pages; top-k: a list's 64-entry chunks
+    const int seglen = TOPK ? a.topk : min(max(ld_uniform(a.seqlens + b), 0), a.max_pages * kPage);
     const int n = (seglen + kPage - 1) / kPage;
     const int q = p + pad;
     const int gs = max(pl.start, q), ge = min(pl.end, q + n);
@@ -351,7 +375,7 @@ __device__ __forceinline__ void for_segments(const DecodeArgs& a, const Plan& pl
       s.sg.nslots = (s.sg.tok1 - s.sg.tok0 + kTS - 1) / kTS;
       s.sg.npages = (s.sg.nslots + 1) / 2;
       s.sg.bt_seg = a.block_table + (size_t)b * a.max_pages + (gs - q);
-      s.sg.idx_seg = nullptr;
+      s.sg.idx_seg = TOPK ? a.topk_idx + (size_t)b * a.topk + s.sg.tok0 : nullptr;
       s.first_r = q / pl.C;
       s.nsplit = (q + n - 1) / pl.C - s.first_r + 1;
       body(s);
@@ -364,7 +388,7 @@ __device__ __forceinline__ void for_segments(const DecodeArgs& a, const Plan& pl
 
 // ---------------------------------------------------------------- score waves
 
-template <int F, bool Q_FP8, bool CAUSAL>
+template <int F, bool Q_FP8, bool CAUSAL, bool TOPK>
 __device__ __forceinline__ void score_role(const DecodeArgs& a, const Plan& pl, const WsLds& L, int w, int lane,
                                            int row0, int r) {
   // (lane and wave pass through empty asm statements: nothing computed from
@@ -401,7 +425,7 @@ __device__ __forceinline__ void score_role(const DecodeArgs& a, const Plan& pl, 
   for (int j = 0; j < 2; ++j) pw[j] = (32 * hb + 16 * j + i16) * kPRowBytes + (16 * th + 4 * g4p) * 2;
   const int xrow = 32 * hb + i16;  // + 16j: this lane's rows in the exchange arrays
 
-  for_segments(a, pl, [&](const WsSeg& sgm) {
+  for_segments<TOPK>(a, pl, [&](const WsSeg& sgm) {
     const int b = sgm.b;
     const int nslots = sgm.sg.nslots;
     int lim[2];
@@ -453,6 +477,15 @@ __device__ __forceinline__ void score_role(const DecodeArgs& a, const Plan& pl, 
           if constexpr (F == kFmtBf16) ws_scores(buf, ka, qf, s);
           else ws_scores8<F>(buf, ka8, kr8, qf, sc, s);
           __builtin_amdgcn_s_setprio(0);
+          if constexpr (TOPK) {
+            // list entries that are padding, negative or past the token's
+            // limit: the validity word the value waves wrote with the copies
+            const uint32_t vm = L.tkmask[it & (kRing - 1)] >> (16 * th + 4 * g4);
+#pragma unroll
+            for (int j = 0; j < 2; ++j)
+#pragma unroll
+              for (int e = 0; e < 4; ++e) s[j][e] = (vm >> e) & 1u ? s[j][e] : -INFINITY;
+          }
           const int tk = sgm.sg.tok0 + it * kTS + 16 * th + 4 * g4;  // this lane's first token
           if (sgm.sg.tok0 + it * kTS + kTS > lim_lo) {
 #pragma unroll
@@ -551,7 +584,7 @@ __device__ __forceinline__ void score_role(const DecodeArgs& a, const Plan& pl, 
 
 typedef u32x2 VFrag8[2];  // [ks]: 8 codes of column lane%32, tokens 16ks + 8(lane/32) .. +7
 
-template <int F>
+template <int F, bool TOPK>
 __device__ __forceinline__ void value_role(const DecodeArgs& a, const Plan& pl, const WsLds& L, int v, int lane,
                                            int row0, int r) {
   typedef WsFmt<F> Fm;
@@ -579,14 +612,82 @@ __device__ __forceinline__ void value_role(const DecodeArgs& a, const Plan& pl, 
   const float kdesc = F == kFmtFp8T ? 1.0f / a.kv_scales[0] : 1.0f;
 
 
-  for_segments(a, pl, [&](const WsSeg& sgm) {
+  // top-k staging of this wave: entries of slot s at [s % 8][64], their
+  // block-table entries at [s % 8][64] (lane l: entry 32s + l % 32)
+  LDS_AS int32_t* const tk_idx = L.tk + v * kTkWords;
+  LDS_AS int32_t* const tk_pg = tk_idx + 8 * 64;
+
+  for_segments<TOPK>(a, pl, [&](const WsSeg& sgm) {
     const int b = sgm.b;
     const SegCtx& sg = sgm.sg;
     const int nslots = sg.nslots;
     PageCache pc;
-    page_cache_load(pc, sg.bt_seg, 0, sg.npages, lane);
+    if constexpr (!TOPK) page_cache_load(pc, sg.bt_seg, 0, sg.npages, lane);
+    // top-k: list b belongs to query token b % T of sequence b / T, which
+    // sees positions [0, seqlen - T + 1 + t); entries outside, and padding,
+    // are masked and copy a fallback row of the sequence (page 0, row 0)
+    int tk_nent = 0, tk_limit = 0, tk_fallback = 0;
+    const char* tk_lst = nullptr;
+    const char* tk_bt = nullptr;
+    if constexpr (TOPK) {
+      const int bq = b / a.topk_tq, tq = b - bq * a.topk_tq;
+      const int32_t* bt = a.block_table + (size_t)bq * a.max_pages;
+      const int seqlen = min(max(ld_uniform(a.seqlens + bq), 0), a.max_pages * kPage);
+      tk_limit = seqlen - a.topk_tq + 1 + tq;
+      tk_nent = sg.tok1 - sg.tok0;
+      tk_fallback = clamp_page(ld_uniform(bt), a.num_pages) * kPage;
+      tk_lst = uniform_ptr((const char*)sg.idx_seg);
+      tk_bt = uniform_ptr((const char*)bt);
+    }
+    // entries of slot s (clamped to the segment) into the staging
+    auto tk_idx_dma = [&](int s) {
+      const uint32_t off = 4u * (uint32_t)min(32 * s + (lane & 31), tk_nent - 1);
+      dma4(tk_lst, off, __builtin_amdgcn_readfirstlane(lds_addr((lds_char*)(tk_idx + (s & 7) * 64))));
+    };
+    // block-table entries of slot s's entries (landed) into the staging
+    auto tk_pg_dma = [&](int s) {
+      const int idx = tk_idx[(s & 7) * 64 + lane];
+      const int p = min(max(idx >> 6, 0), a.max_pages - 1);
+      dma4(tk_bt, 4u * (uint32_t)p, __builtin_amdgcn_readfirstlane(lds_addr((lds_char*)(tk_pg + (s & 7) * 64))));
+    };
+    // cache row of entry j of slot s (its entry and page landed)
+    auto tk_row = [&](int s, int j, bool& ok) -> int {
+      const int idx = tk_idx[(s & 7) * 64 + j];
+      const int pg = tk_pg[(s & 7) * 64 + j];
+      ok = 32 * s + j < tk_nent && idx >= 0 && idx < tk_limit;
+      return ok ? clamp_page(pg, a.num_pages) * kPage + (idx & 63) : tk_fallback;
+    };
     // this wave's copies of slot s into ring position pos (s < nslots)
     auto dma_cols = [&](int s, int pos) {
+      if constexpr (TOPK) {
+        // gathered rows: lane i of copy rb fetches row 8rb + i/8 of the slot,
+        // position i%8 of the column group, from that entry's cache row
+        const uint32_t base = __builtin_amdgcn_readfirstlane(lds_addr(L.ring + (pos & (kRing - 1)) * Fm::kSlot));
+        const char* kvu = uniform_ptr(a.kv);
+        bool ok;
+#pragma unroll
+        for (int rb = 0; rb < 4; ++rb) {
+          const int j = 8 * rb + (lane >> 3);
+          const int row = tk_row(s, j, ok);
+          const uint32_t off = (uint32_t)row * Fm::kRow + 128u * v + 16u * ((lane & 7) ^ row_swz(j));
+          dma16<0>(kvu, off, base + v * kGroupBytes + rb * 1024);
+        }
+        {
+          const int j = 8 * v + (lane >> 3);
+          const int row = tk_row(s, j, ok);
+          const int c = min((lane & 7) ^ row_swz(j), kChunks - 1);
+          dma16<0>(kvu, (uint32_t)row * Fm::kRow + 512u + 16u * c, base + 4 * kGroupBytes + v * 1024);
+        }
+        {
+          const int j = lane & 31;
+          const int row = tk_row(s, j, ok);
+          if constexpr (F == kFmtFp8)
+            dma16<0>(uniform_ptr((const char*)a.kv_scales), 16u * (uint32_t)row, base + Fm::kScaleOff + v * 1024);
+          const uint64_t vm = __ballot(ok);
+          if (v == 0 && lane == 0) L.tkmask[pos & (kRing - 1)] = (uint32_t)vm;
+        }
+        return;
+      }
       const int page = page_of(pc, sg.bt_seg, s >> 1, sg.npages, lane, a.num_pages);
       const size_t row0s = (size_t)page * kPage + (s & 1) * kTS;  // cache row of the slot's token 0
       const char* src = a.kv + row0s * Fm::kRow;
@@ -637,6 +738,20 @@ __device__ __forceinline__ void value_role(const DecodeArgs& a, const Plan& pl, 
         for (int cb = 0; cb < 4; ++cb) o[rb][cb] = f32x16{};
       // copy epochs -3 .. -1 (the prologue): slots 0 .. 2; slot 0 landed
       const int pre = min(nslots, 3);
+      if constexpr (TOPK) {
+        // translate slots 0..4 (entries, then their pages) and stage the
+        // entries of slots 5 and 6; the slot loop keeps the pages five and
+        // the entries seven slots ahead
+        // (each wait is followed by a compiler barrier: the copies write LDS
+        // behind the compiler's back, and the waits alone do not keep the
+        // LDS reads of the staged words below them)
+        for (int s = 0; s < 7; ++s) tk_idx_dma(s);
+        wait_vm_lgkm0<0>();
+        asm volatile("" ::: "memory");
+        for (int s = 0; s < 5; ++s) tk_pg_dma(s);
+        wait_vm_lgkm0<0>();
+        asm volatile("" ::: "memory");
+      }
       // slot 0 first, then X: the score waves load their queries only after
       // these copies are issued, so that slot 0 is not queued behind them;
       // slots 1 and 2 follow after Y, behind the query loads, which the first
@@ -655,6 +770,20 @@ __device__ __forceinline__ void value_role(const DecodeArgs& a, const Plan& pl, 
       // in iteration it-1); PV of slot it-1 from vc, while the V fragments of
       // slot it (landed before B_it) are read into vn for the next iteration
       auto iteration = [&](int it, VF (&vc)[4], VF (&vn)[4]) {
+        if constexpr (TOPK) {
+          // the entries of slot it+5 and the pages of slot it+3, both staged
+          // two iterations ago, landed: everything of this wave's but the
+          // copies of slots it+1 and it+2 and the two staging loads between
+          // them (completion is in order); then stage the pages of slot it+5
+          // and the entries of slot it+7
+          const int k = (it >= 2 ? epoch_ops<N>(it - 2, nslots) : 0) + epoch_ops<N>(it - 1, nslots);
+          if (k == 2 * N) wait_vm_lgkm0<2 * N + 2>();
+          else if (k == N) wait_vm_lgkm0<N + 2>();
+          else wait_vm_lgkm0<2>();
+          asm volatile("" ::: "memory");
+          tk_pg_dma(it + 5);
+          tk_idx_dma(it + 7);
+        }
         if (it + 3 < nslots) dma_cols(it + 3, it + 3);
         const lds_char* nbuf = L.ring + (it & (kRing - 1)) * Fm::kSlot;
         // this wave's V^T fragments of slot it, column block cb
@@ -702,7 +831,14 @@ __device__ __forceinline__ void value_role(const DecodeArgs& a, const Plan& pl, 
         // slot it+1 landed (the operations of epochs it-1 and it may stay in
         // flight), and this wave's LDS reads of slot it are done before the
         // next iteration's copies refill the ring position of slot it-1
-        wait_ops_lgkm0<N>(epoch_ops<N>(it - 1, nslots) + epoch_ops<N>(it, nslots));
+        if constexpr (TOPK) {
+          // slot it+1 landed; the copies of the two later epochs and their
+          // staging loads (two per iteration; the prologue issues none after
+          // its copies) may stay in flight
+          wait_ops_lgkm0<N>(epoch_ops<N>(it - 1, nslots) + epoch_ops<N>(it, nslots), it >= 1 ? 4 : 2);
+        } else {
+          wait_ops_lgkm0<N>(epoch_ops<N>(it - 1, nslots) + epoch_ops<N>(it, nslots));
+        }
         barrier();  // B_it+1
       };
       for (int it = 0; it <= nslots; it += 2) {
@@ -746,21 +882,26 @@ __device__ __forceinline__ void value_role(const DecodeArgs& a, const Plan& pl, 
         }
         break;
       }
-      if (sg.npages > 64) page_cache_load(pc, sg.bt_seg, 0, sg.npages, lane);
+      if constexpr (!TOPK) {
+        if (sg.npages > 64) page_cache_load(pc, sg.bt_seg, 0, sg.npages, lane);
+      }
       wait_vm_lgkm0<0>();
       barrier();  // every wave has read the votes
     }
   });
 }
 
-template <int F, bool Q_FP8, bool CAUSAL>
+template <int F, bool Q_FP8, bool CAUSAL, bool TOPK>
 __global__ void __attribute__((amdgpu_flat_work_group_size(kWsThreads, kWsThreads), amdgpu_waves_per_eu(2, 2)))
 mla_decode_ws_kernel(DecodeArgs a) {
   // KV ring (4 slots) and P tiles (two slots' worth)
   __shared__ __attribute__((aligned(1024))) char ring_mem[kRing * WsFmt<F>::kSlot];
   __shared__ __attribute__((aligned(16))) char ptile_mem[2 * WsFmt<F>::kPTiles * kPTile];
   __shared__ __attribute__((aligned(16))) float xs[512];                        // row exchanges, votes
+  __shared__ __attribute__((aligned(16))) int32_t tk_mem[TOPK ? 4 * kTkWords : 4];  // top-k staging
   WsLds L;
+  L.tkmask = (LDS_AS uint32_t*)xs + 448;
+  L.tk = (LDS_AS int32_t*)tk_mem;
   L.ring = (lds_char*)ring_mem;
   L.ptile = (lds_char*)ptile_mem;
   L.xref = (LDS_AS float*)xs;
@@ -790,21 +931,29 @@ mla_decode_ws_kernel(DecodeArgs a) {
   }
   if (!has_work) return;
   const int row0 = slab * kWsRows;
-  if (w < 4) score_role<F, Q_FP8, CAUSAL>(a, pl, L, w, lane, row0, r);
-  else value_role<F>(a, pl, L, w - 4, lane, row0, r);
+  if (w < 4) score_role<F, Q_FP8, CAUSAL, TOPK>(a, pl, L, w, lane, row0, r);
+  else value_role<F, TOPK>(a, pl, L, w - 4, lane, row0, r);
 }
 
 }  // namespace
 
-bool decode_ws_supported(int32_t kv_format, int32_t topk, int32_t eff_heads) {
-  return topk == 0 && eff_heads >= kWsRows;
+bool decode_ws_supported(int32_t kv_format, int32_t topk, int32_t eff_heads, int32_t num_pages) {
+  if (eff_heads < kWsRows) return false;
+  if (topk == 0) return true;
+  // top-k lists: the FP8 caches (the bf16 ring leaves no room for the
+  // staging), with every cache row reachable by a 32-bit byte offset
+  const int64_t row_bytes = kv_format == kKvFormatFp8Tile ? kFp8RowBytes : kFp8TRowBytes;
+  return kv_format != kKvFormatBf16 && (int64_t)num_pages * kPage * row_bytes < ((int64_t)1 << 32);
 }
 
 hipError_t launch_decode_ws(const DecodeArgs& a, int32_t kv_format, bool q_fp8, bool causal, hipStream_t stream) {
   const dim3 grid(a.per_xcd * 8 * a.slabs), block(kWsThreads);
 #define MLA_WS_LAUNCH(F, QF, C)                                                                          \
-  if (fmt == F && q_fp8 == QF && causal == C)                                                            \
-    hipLaunchKernelGGL((mla_decode_ws_kernel<F, QF, C>), grid, block, 0, stream, a);
+  if (fmt == F && q_fp8 == QF && causal == C && !topk)                                                   \
+    hipLaunchKernelGGL((mla_decode_ws_kernel<F, QF, C, false>), grid, block, 0, stream, a);
+#define MLA_WS_LAUNCH_TOPK(F, QF)                                                                        \
+  if (fmt == F && q_fp8 == QF && topk) hipLaunchKernelGGL((mla_decode_ws_kernel<F, QF, false, true>), grid, block, 0, stream, a);
+  const bool topk = a.topk > 0;
   const int fmt = kv_format == kKvFormatFp8Tile ? kFmtFp8 : kv_format == kKvFormatFp8Tensor ? kFmtFp8T : kFmtBf16;
   MLA_WS_LAUNCH(kFmtBf16, false, false)
   MLA_WS_LAUNCH(kFmtBf16, false, true)
@@ -818,7 +967,12 @@ hipError_t launch_decode_ws(const DecodeArgs& a, int32_t kv_format, bool q_fp8, 
   MLA_WS_LAUNCH(kFmtFp8T, false, true)
   MLA_WS_LAUNCH(kFmtFp8T, true, false)
   MLA_WS_LAUNCH(kFmtFp8T, true, true)
+  MLA_WS_LAUNCH_TOPK(kFmtFp8, false)
+  MLA_WS_LAUNCH_TOPK(kFmtFp8, true)
+  MLA_WS_LAUNCH_TOPK(kFmtFp8T, false)
+  MLA_WS_LAUNCH_TOPK(kFmtFp8T, true)
 #undef MLA_WS_LAUNCH
+#undef MLA_WS_LAUNCH_TOPK
   return hipGetLastError();
 }
 

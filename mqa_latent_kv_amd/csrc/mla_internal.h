@@ -73,7 +73,7 @@ hipError_t launch_decode(const DecodeLaunch& d, hipStream_t stream);
 hipError_t decode_scratch(void** ptr, size_t* bytes);
 // The wave-specialised decode (decode_ws.hip): bf16 paged caches, dense,
 // at least 64 query rows per sequence.
-bool decode_ws_supported(int32_t kv_format, int32_t topk, int32_t eff_heads);
+bool decode_ws_supported(int32_t kv_format, int32_t topk, int32_t eff_heads, int32_t num_pages);
 hipError_t launch_decode_ws(const DecodeArgs& a, int32_t kv_format, bool q_fp8, bool causal, hipStream_t stream);
 // Split-line padding of the wave-specialised decode: a segment costs about
 // as much as this many pages at each of its two ends (query load, pipeline
