@@ -1331,6 +1331,8 @@ mla_decode_kernel(DecodeArgs a) {
 struct MergeArgs {
   const int2* seq;   // [B] {workspace slot of piece 0, pieces}
   const float* ws_o;
+  const _Float16* ws_o16;  // scaled fp16 partials and their factors (wave-specialised kernel)
+  const float* ws_sc;
   const float* ws_lse;
   void* out;
   float* lse;
@@ -1347,22 +1349,39 @@ constexpr int kMergeHeads = 4;  // heads per merge workgroup, 64 threads each
 // and O columns are all requested together (one memory latency per chunk);
 // a later chunk with a larger max rescales the sums so far (up to eight
 // pieces, M is the max of all of them, as written above).
+// Partials come as fp32 (F16 false) or, from the wave-specialised kernel, as
+// fp16 values v with a power-of-two factor f per row and 128 columns, O_s =
+// v * f exactly as the piece rounded it.
 constexpr int kMergeChunk = 8;
 constexpr int kMergeU = kDV / 4 / (kThreads / kMergeHeads);  // float4 columns per thread
 
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+
 // Pieces s0 .. s0+N-1 of one column group: every load issued before any is
-// used (a fixed count, so no branch separates them).
-template <int N>
-__device__ __forceinline__ void merge_chunk(const float* lse_col, const f32x4* src0, size_t pstride, int heads,
+// used (a fixed count, so no branch separates them).  `col` is the first
+// column of the thread's group u = 0 (group u starts 4 * TPH * u later).
+template <int N, bool F16>
+__device__ __forceinline__ void merge_chunk(const MergeArgs& m, const float* lse_col, size_t head_slot0, int col,
                                             int s0, f32x4 (&acc)[kMergeU], float& mx, float& wsum) {
   constexpr int TPH = kThreads / kMergeHeads;
+  const int heads = m.heads;
   float l[N];
   f32x4 v[N][kMergeU];
 #pragma unroll
   for (int i = 0; i < N; ++i) {
     l[i] = lse_col[(size_t)(s0 + i) * heads];
+    const size_t row = head_slot0 + (size_t)(s0 + i) * heads;  // (slot, head) row of piece s0 + i
 #pragma unroll
-    for (int u = 0; u < kMergeU; ++u) v[i][u] = src0[(s0 + i) * pstride + u * TPH];
+    for (int u = 0; u < kMergeU; ++u) {
+      const int c = col + 4 * TPH * u;
+      if constexpr (F16) {
+        const f16x4 h = *(const f16x4*)(m.ws_o16 + row * kDV + c);
+        const float f = m.ws_sc[row * 4 + c / 128];
+        v[i][u] = __builtin_convertvector(h, f32x4) * f;
+      } else {
+        v[i][u] = *(const f32x4*)(m.ws_o + row * kDV + c);
+      }
+    }
   }
   float cm = mx;
 #pragma unroll
@@ -1382,6 +1401,7 @@ __device__ __forceinline__ void merge_chunk(const float* lse_col, const f32x4* s
   mx = cm;
 }
 
+template <bool F16>
 __global__ void __launch_bounds__(kThreads) mla_merge_kernel(MergeArgs m) {
   const int b = blockIdx.x;
   const int2 info = m.seq[b];
@@ -1391,8 +1411,8 @@ __global__ void __launch_bounds__(kThreads) mla_merge_kernel(MergeArgs m) {
   const int head = blockIdx.y * kMergeHeads + threadIdx.x / TPH, sub = threadIdx.x % TPH;
   if (head >= m.heads) return;
   const float* lse_col = m.ws_lse + (size_t)first * m.heads + head;
-  const size_t pstride = (size_t)m.heads * (kDV / 4);  // float4 per piece
-  const f32x4* src0 = (const f32x4*)(m.ws_o + ((size_t)first * m.heads + head) * kDV) + sub;
+  const size_t row0 = (size_t)first * m.heads + head;
+  const int col = 4 * sub;
   constexpr int U = kMergeU;
   f32x4 acc[U];
 #pragma unroll
@@ -1400,14 +1420,14 @@ __global__ void __launch_bounds__(kThreads) mla_merge_kernel(MergeArgs m) {
   float mx = -INFINITY, wsum = 0.0f;
   for (int s0 = 0; s0 < nsplit; s0 += kMergeChunk) {
     switch (min(kMergeChunk, nsplit - s0)) {  // uniform over the workgroup
-      case 1: merge_chunk<1>(lse_col, src0, pstride, m.heads, s0, acc, mx, wsum); break;
-      case 2: merge_chunk<2>(lse_col, src0, pstride, m.heads, s0, acc, mx, wsum); break;
-      case 3: merge_chunk<3>(lse_col, src0, pstride, m.heads, s0, acc, mx, wsum); break;
-      case 4: merge_chunk<4>(lse_col, src0, pstride, m.heads, s0, acc, mx, wsum); break;
-      case 5: merge_chunk<5>(lse_col, src0, pstride, m.heads, s0, acc, mx, wsum); break;
-      case 6: merge_chunk<6>(lse_col, src0, pstride, m.heads, s0, acc, mx, wsum); break;
-      case 7: merge_chunk<7>(lse_col, src0, pstride, m.heads, s0, acc, mx, wsum); break;
-      default: merge_chunk<8>(lse_col, src0, pstride, m.heads, s0, acc, mx, wsum); break;
+      case 1: merge_chunk<1, F16>(m, lse_col, row0, col, s0, acc, mx, wsum); break;
+      case 2: merge_chunk<2, F16>(m, lse_col, row0, col, s0, acc, mx, wsum); break;
+      case 3: merge_chunk<3, F16>(m, lse_col, row0, col, s0, acc, mx, wsum); break;
+      case 4: merge_chunk<4, F16>(m, lse_col, row0, col, s0, acc, mx, wsum); break;
+      case 5: merge_chunk<5, F16>(m, lse_col, row0, col, s0, acc, mx, wsum); break;
+      case 6: merge_chunk<6, F16>(m, lse_col, row0, col, s0, acc, mx, wsum); break;
+      case 7: merge_chunk<7, F16>(m, lse_col, row0, col, s0, acc, mx, wsum); break;
+      default: merge_chunk<8, F16>(m, lse_col, row0, col, s0, acc, mx, wsum); break;
     }
   }
   const float inv = wsum > 0.0f ? 1.0f / wsum : 0.0f;
@@ -1516,6 +1536,10 @@ hipError_t launch_decode(const DecodeLaunch& din, hipStream_t stream) {
   a.ws_lse = (float*)ws;
   ws += align256(sizeof(float) * slots * d.heads);
   a.ws_o = (float*)ws;
+  // the fp16 partials and their factors share the fp32 partials' region:
+  // 2 + 16/512 of its 4 bytes per value
+  a.ws_o16 = (_Float16*)ws;
+  a.ws_sc = (float*)(ws + align256(sizeof(_Float16) * slots * d.heads * kDV));
   ws += align256(sizeof(float) * slots * d.heads * kDV);
   a.topk_tq = din.topk > 0 ? din.tq : 1;
   a.batch = d.batch;
@@ -1535,7 +1559,8 @@ hipError_t launch_decode(const DecodeLaunch& din, hipStream_t stream) {
                   : d.kv_format == kKvFormatFp8Tensor ? (d.topk > 0 ? kKvFp8TTopK : kKvFp8T)
                                                       : (d.topk > 0 ? kKvBf16TopK : kKvBf16);
   hipError_t e;
-  if (decode_ws_supported(d.kv_format, d.topk, d.heads, d.num_pages)) {
+  const bool ws_kernel = decode_ws_supported(d.kv_format, d.topk, d.heads, d.num_pages);
+  if (ws_kernel) {
     // dense bf16 pages with at least 64 rows per sequence: the wave-specialised
     // kernel (decode_ws.hip), the same plan, slabs of 64 rows and workspace
     a.seg_pad = kWsSegPad;
@@ -1547,12 +1572,15 @@ hipError_t launch_decode(const DecodeLaunch& din, hipStream_t stream) {
   MergeArgs m;
   m.seq = a.ws_seq;
   m.ws_o = a.ws_o;
+  m.ws_o16 = a.ws_o16;
+  m.ws_sc = a.ws_sc;
   m.ws_lse = a.ws_lse;
   m.out = d.out;
   m.lse = d.lse;
   m.heads = d.heads;
-  hipLaunchKernelGGL(mla_merge_kernel, dim3(d.batch, (d.heads + kMergeHeads - 1) / kMergeHeads), dim3(kThreads), 0,
-                     stream, m);
+  const dim3 mgrid(d.batch, (d.heads + kMergeHeads - 1) / kMergeHeads);
+  if (ws_kernel) hipLaunchKernelGGL(mla_merge_kernel<true>, mgrid, dim3(kThreads), 0, stream, m);
+  else hipLaunchKernelGGL(mla_merge_kernel<false>, mgrid, dim3(kThreads), 0, stream, m);
   return hipGetLastError();
 }
 

@@ -582,6 +582,7 @@ __device__ __forceinline__ void score_role(const DecodeArgs& a, const Plan& pl, 
 
 // ---------------------------------------------------------------- value waves
 
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
 typedef u32x2 VFrag8[2];  // [ks]: 8 codes of column lane%32, tokens 16ks + 8(lane/32) .. +7
 
 template <int F, bool TOPK>
@@ -850,9 +851,9 @@ __device__ __forceinline__ void value_role(const DecodeArgs& a, const Plan& pl, 
       if (__builtin_amdgcn_readfirstlane(votes) == 0) {
         // normalise and store this wave's 128 columns of the 64 rows: the
         // lane holds row 32rb + lane%32 and, per column block and register
-        // quad, four consecutive columns (one 16-byte or 8-byte store).  The
-        // lane index is passed through an empty asm so that the compiler
-        // cannot hoist these per-lane store addresses out of the slot loop.
+        // quad, four consecutive columns (one 8-byte store).  The lane index
+        // is passed through an empty asm so that the compiler cannot hoist
+        // these per-lane store addresses out of the slot loop.
         int ln = lane;
         asm volatile("" : "+v"(ln));
         const int i32 = ln & 31, h2 = ln >> 5;
@@ -863,20 +864,50 @@ __device__ __forceinline__ void value_role(const DecodeArgs& a, const Plan& pl, 
           const float lt = L.xl[lr] + L.xl[64 + lr];
           const float inv = lt > 0.0f ? kdesc / lt : 0.0f;
           const int row = row0 + lr;
-          if (row < a.heads) {
-            __bf16* orow = (__bf16*)a.out + ((size_t)b * a.heads + row) * kDV + 128 * v + 4 * h2;
-            float* prow = a.ws_o + (pslot * a.heads + row) * kDV + 128 * v + 4 * h2;
+          if (sgm.nsplit == 1) {
+            if (row < a.heads) {
+              __bf16* orow = (__bf16*)a.out + ((size_t)b * a.heads + row) * kDV + 128 * v + 4 * h2;
 #pragma unroll
-            for (int cb = 0; cb < 4; ++cb) {
+              for (int cb = 0; cb < 4; ++cb)
 #pragma unroll
-              for (int q = 0; q < 4; ++q) {
-                // accumulator registers 4q .. 4q+3: columns 32cb + 8q + 4h2 .. +3
-                f32x4 val;
+                for (int q = 0; q < 4; ++q) {
+                  // accumulator registers 4q .. 4q+3: columns 32cb + 8q + 4h2 .. +3
+                  f32x4 val;
 #pragma unroll
-                for (int e = 0; e < 4; ++e) val[e] = o[rb][cb][4 * q + e] * inv;
-                if (sgm.nsplit == 1) *(bf16x4*)(orow + 32 * cb + 8 * q) = __builtin_convertvector(val, bf16x4);
-                else *(f32x4*)(prow + 32 * cb + 8 * q) = val;
-              }
+                  for (int e = 0; e < 4; ++e) val[e] = o[rb][cb][4 * q + e] * inv;
+                  *(bf16x4*)(orow + 32 * cb + 8 * q) = __builtin_convertvector(val, bf16x4);
+                }
+            }
+          } else {
+            // a piece of a split sequence: the normalised values v of this
+            // row's 128 columns as fp16 of v / 2^e, with e chosen from their
+            // largest magnitude m (= f 2^x, f in [0.5, 1)) as x - 15, which
+            // puts m / 2^e in [2^14, 2^15) below the fp16 maximum; the
+            // scaling is exact, so each value carries one fp16 rounding, at
+            // most 2^-11 m.  (Zero, inf and NaN maxima give x = 0: the values
+            // pass unchanged in range or as inf and NaN.)  The clamp keeps
+            // 2^-e and 2^e normal fp32 numbers.
+            // (the largest |o| times inv is the largest |o inv|: inv > 0 and
+            // rounding is monotonic)
+            float mx = 0.0f;
+#pragma unroll
+            for (int cb = 0; cb < 4; ++cb)
+#pragma unroll
+              for (int k = 0; k < 16; ++k) mx = fmaxf(mx, fabsf(o[rb][cb][k]));
+            mx = max_halves(mx) * inv;  // lanes l and l^32 hold the same row
+            const int ex = min(max(__builtin_amdgcn_frexp_expf(mx) - 15, -110), 113);
+            if (row < a.heads) {
+              _Float16* prow = a.ws_o16 + (pslot * a.heads + row) * kDV + 128 * v + 4 * h2;
+#pragma unroll
+              for (int cb = 0; cb < 4; ++cb)
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                  f32x4 val;
+#pragma unroll
+                  for (int e = 0; e < 4; ++e) val[e] = __builtin_amdgcn_ldexpf(o[rb][cb][4 * q + e] * inv, -ex);
+                  *(f16x4*)(prow + 32 * cb + 8 * q) = __builtin_convertvector(val, f16x4);
+                }
+              if (h2 == 0) a.ws_sc[(pslot * a.heads + row) * 4 + v] = __builtin_amdgcn_ldexpf(1.0f, ex);
             }
           }
         }

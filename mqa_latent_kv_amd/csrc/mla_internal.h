@@ -38,7 +38,9 @@ struct DecodeArgs {
   const float* kv_scales;
   void* out;
   float* lse;
-  float* ws_o;    // [(ranges + B) slots][H][512] normalised partial O, fp32
+  float* ws_o;    // [(ranges + B) slots][H][512] normalised partial O, fp32 (split-reduction kernel)
+  _Float16* ws_o16;  // the same region as [(ranges + B)][H][512] fp16 of O / 2^e (wave-specialised kernel)
+  float* ws_sc;      // then [(ranges + B)][H][4] the factors 2^e, one per row and 128 columns
   float* ws_lse;  // [(ranges + B)][H] base-2 LSE of partials
   int2* ws_seq;   // [B] {workspace slot of piece 0, pieces}; pieces 0: nothing to attend
   int32_t topk_tq;           // top-k: lists per sequence (T); list b belongs to sequence b / T
