@@ -116,6 +116,35 @@ __host__ __device__ __forceinline__ uint8_t e4m3_of_product(float v, float q) {
   return (uint8_t)(sign | code);
 }
 
+// The same codes for two products v0 * q and v1 * q (bits 0..7 and 8..15),
+// mostly by the hardware conversion: it rounds its fp32 input to nearest
+// even, so fed the fp32 product hi clamped to +-448 (which it encodes as
+// 0x7E / 0xFE, the saturation above) it returns the exact product's code
+// unless hi is an e4m3 midpoint with lo != 0, the one case where the exact
+// value and hi round apart.  Those products, and NaN, take the encoder above
+// (rare: the branch is almost never taken by any lane).  Midpoints: in the
+// normal range the fp32 bits below the three kept mantissa bits are exactly
+// half (0x80000); below 2^-6, adding 2^-6 moves the subnormal step 2^-9 onto
+// that same mantissa bit, and a midpoint (k + 1/2) 2^-9 stays exact (an
+// inexact sum can only add a false alarm, which the exact encoder absorbs).
+// Computed without branches.
+__device__ __forceinline__ uint32_t e4m3_needs_exact(float v, float q, float hi) {
+  const float lo = __builtin_fmaf(v, q, -hi);
+  const float a = __builtin_fabsf(hi);
+  const float s = a < 0.015625f ? a + 0.015625f : a;
+  const uint32_t mid = (__builtin_bit_cast(uint32_t, s) & 0xFFFFFu) == 0x80000u;
+  return (uint32_t)(hi != hi) | ((uint32_t)(lo != 0.0f) & mid);
+}
+__device__ __forceinline__ uint32_t e4m3x2_of_products(float v0, float v1, float q) {
+  const float h0 = v0 * q, h1 = v1 * q;
+  const float c0 = __builtin_fminf(__builtin_fmaxf(h0, -448.0f), 448.0f);
+  const float c1 = __builtin_fminf(__builtin_fmaxf(h1, -448.0f), 448.0f);
+  uint32_t r = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(c0, c1, 0, false) & 0xFFFFu;
+  if (__builtin_expect(e4m3_needs_exact(v0, q, h0) | e4m3_needs_exact(v1, q, h1), 0))
+    r = (uint32_t)e4m3_of_product(v0, q) | ((uint32_t)e4m3_of_product(v1, q) << 8);
+  return r;
+}
+
 // Sum over the 64 lanes, every lane receiving it, in registers only: two
 // quad permutations, the half-row and row mirrors (16 lanes summed), then
 // the 16- and 32-lane swaps.  (A shuffle loop would go through ds_bpermute,
@@ -175,14 +204,11 @@ __global__ void __launch_bounds__(kThreads) mla_kv_insert_kernel(InsertArgs a) {
   ss = wave_sum(ss);
   // 1/512 is a power of two: the mean is the exact quotient
   const float rr = 1.0f / __builtin_sqrtf(ss * (1.0f / kLatent) + a.eps);
-  uint32_t lo = 0, hi = 0;
+  float n[8];
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const __bf16 n = (__bf16)(((float)x[i] * rr) * (float)wv[i]);  // round to nearest even
-    const uint32_t c = e4m3_of_product((float)n, ksi);
-    if (i < 4) lo |= c << (8 * i);
-    else hi |= c << (8 * (i - 4));
-  }
+  for (int i = 0; i < 8; ++i) n[i] = (float)(__bf16)(((float)x[i] * rr) * (float)wv[i]);  // round to nearest even
+  const uint32_t lo = e4m3x2_of_products(n[0], n[1], ksi) | (e4m3x2_of_products(n[2], n[3], ksi) << 16);
+  const uint32_t hi = e4m3x2_of_products(n[4], n[5], ksi) | (e4m3x2_of_products(n[6], n[7], ksi) << 16);
   uint8_t* dst = a.cache + (size_t)slot * kCacheRow;
   *(uint2*)(dst + 8 * lane) = uint2{lo, hi};
   dst[kLatent + lane] = e4m3_of_product(rope, ksi);
@@ -379,11 +405,13 @@ __global__ void __launch_bounds__(kThreads) mla_ql_kernel(QueryArgs a) {
   const float qsi = a.q_scale_inv[0];
   const int c = c0 + 32 * w + (lane & 31);
 #pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    const int bb = m0 + 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3);
-    if (bb >= a.batch) continue;
-    const float v = (float)(__bf16)acc[i];
-    a.out[((size_t)bb * a.heads + head) * kOut + c] = e4m3_of_product(v, qsi);
+  for (int i = 0; i < 16; i += 2) {
+    const uint32_t cc = e4m3x2_of_products((float)(__bf16)acc[i], (float)(__bf16)acc[i + 1], qsi);
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      const int bb = m0 + 8 * ((i + k) >> 2) + 4 * (lane >> 5) + ((i + k) & 3);
+      if (bb < a.batch) a.out[((size_t)bb * a.heads + head) * kOut + c] = (uint8_t)(cc >> (8 * k));
+    }
   }
   // the rope rows of Q_B go to the output as they are (bf16 of the summed
   // partials, then FP8): the workgroups of column block 0, eight values per
@@ -399,11 +427,14 @@ __global__ void __launch_bounds__(kThreads) mla_ql_kernel(QueryArgs a) {
         s1 += *(const f32x4*)(src + 4);
       }
       uint8_t* dst = a.out + ((size_t)t * a.heads + head) * kOut + kDV + (r0 - kNope);
+      uint32_t w4[2];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        dst[e] = e4m3_of_product((float)(__bf16)s0[e], qsi);
-        dst[4 + e] = e4m3_of_product((float)(__bf16)s1[e], qsi);
+      for (int h = 0; h < 2; ++h) {
+        const f32x4 sv = h ? s1 : s0;
+        w4[h] = e4m3x2_of_products((float)(__bf16)sv[0], (float)(__bf16)sv[1], qsi) |
+                (e4m3x2_of_products((float)(__bf16)sv[2], (float)(__bf16)sv[3], qsi) << 16);
       }
+      *(uint2*)dst = uint2{w4[0], w4[1]};
     }
   }
 }
@@ -560,35 +591,86 @@ constexpr int kQbnThreads = 512;          // eight waves, an eighth of the reduc
 constexpr int kMKs = kQA / 8 / 32;        // k-steps of 32 per wave
 constexpr int kUkCols = 32;               // W_UK output columns per workgroup
 
+// One direct global->LDS copy of 16 bytes per lane (lane i's bytes land at
+// lds + 16i): base and lds wave-uniform, voff the lane's byte offset.
+__device__ __forceinline__ void qdma16(const void* base, uint32_t voff, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(base), "s"(lds) : "memory", "m0");
+}
+__device__ __forceinline__ const void* qd_uniform(const void* p) {
+  const uint64_t v = (uint64_t)p;
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v), hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+  return (const void*)(((uint64_t)hi << 32) | lo);
+}
+
+// Staging of one wave's slice (192 columns = 384 bytes = three 128-byte lines
+// per row) of 8-row groups: copy j holds line j / G of rows 8(j % G) .. +7,
+// lane i of it row 8(j % G) + i/8 and, at position i % 8, source chunk
+// (i % 8) ^ qb_swz(row) of that line.  The XOR spreads the 16 rows that one
+// fragment read touches over all 64 banks.
+__device__ __forceinline__ int qb_swz(int r) { return (r & 7) ^ ((r >> 3) & 1); }
+// LDS byte offset of chunk c (0..23) of row r in a staging of G row groups
+template <int G>
+__device__ __forceinline__ uint32_t qb_stage_off(int r, int c) {
+  const int j = G * (c >> 3) + (r >> 3);
+  return 1024u * j + 16u * (8 * (r & 7) + ((c & 7) ^ qb_swz(r)));
+}
+
 __global__ void __launch_bounds__(kQbnThreads) mla_qbn_kernel(QueryArgs a) {
   constexpr int W = kQbnThreads / 64;
-  __shared__ float ssp[W][kMTok];                               // per-wave sums of squares
-  __shared__ __attribute__((aligned(16))) f32x4 red[W][2][64];  // per-wave partial tiles
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  constexpr int kXBytes = kMTok * 384, kWBytes = kMRows * 384;  // per wave: 6 + 12 KB, and 1 KB for w_qa
+  __shared__ __attribute__((aligned(1024))) char stage[W][kXBytes + kWBytes + 1024];
+  __shared__ float ssp[W][kMTok];  // per-wave sums of squares
+  const int tid = threadIdx.x, lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int i16 = lane & 15, g = lane >> 4;
   const int nrows = a.heads * kQB;
   const int n0 = blockIdx.x * kMRows, m0 = blockIdx.y * kMTok;
+  LDS_AS char* const xs = (LDS_AS char*)stage[w];
+  LDS_AS char* const wsg = xs + kXBytes;
+  const uint32_t xs_a = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)xs);
+  // copies of this wave's slice, columns 192w .. +191: the tokens' q_a rows
+  // (two row groups), then the w_qa slice (lanes 0..23; the others repeat
+  // it) and the 32 W_qb rows (four), whole 128-byte lines per eight lanes.
+  // Tokens past the batch and rows past the heads read the last valid one
+  // (zeroed below).  The RMSNorm only needs the first two, so the W_qb rows
+  // keep landing while it runs.
+  LDS_AS char* const wqs = xs + kXBytes + kWBytes;
+  {
+    const int rr = lane >> 3, ch = lane & 7;
+    const void* xb = qd_uniform(a.qkv);
+    const void* wb = qd_uniform(a.w_qb);
+#pragma unroll
+    for (int j = 0; j < 6; ++j) {
+      const int r = 8 * (j & 1) + rr, line = j >> 1;
+      const int t = min(m0 + r, a.batch - 1);
+      const uint32_t off = (uint32_t)t * (uint32_t)a.qkv_stride * 2u + 384u * w + 128u * line + 16u * (ch ^ qb_swz(r));
+      qdma16(xb, off, xs_a + 1024u * j);
+    }
+    qdma16(qd_uniform(a.w_qa), 384u * w + 16u * (lane % 24), xs_a + kXBytes + kWBytes);
+#pragma unroll
+    for (int j = 0; j < 12; ++j) {
+      const int r = 8 * (j & 3) + rr, line = j >> 2;
+      const int n = min(n0 + r, nrows - 1);
+      const uint32_t off = (uint32_t)n * (uint32_t)(kQA * 2) + 384u * w + 128u * line + 16u * (ch ^ qb_swz(r));
+      qdma16(wb, off, xs_a + kXBytes + 1024u * j);
+    }
+  }
   // lane l: A = token m0 + l%16, B = W_qb rows n0 + 16nb + l%16 (nb = 0, 1),
-  // columns 192w + 32i + 8(l/16) .. +7 (clamped rows and tokens, zeroed below)
+  // k-step i: columns 192w + 32i + 8(l/16) .. +7, i.e. chunk 4i + l/16 of the
+  // slice
   const int t = m0 + i16;
   const bool t_ok = t < a.batch;
-  const int t_c = t_ok ? t : a.batch - 1;
   bool row_ok[2];
-  int nrow_c[2];
 #pragma unroll
-  for (int nb = 0; nb < 2; ++nb) {
-    const int nrow = n0 + 16 * nb + i16;
-    row_ok[nb] = nrow < nrows;
-    nrow_c[nb] = row_ok[nb] ? nrow : nrows - 1;
-  }
-  const int k0 = w * (kQA / W) + 8 * g;
-  bf16x8 xr[kMKs], wq[kMKs], wr[2][kMKs];
+  for (int nb = 0; nb < 2; ++nb) row_ok[nb] = n0 + 16 * nb + i16 < nrows;
+  // vm operations complete in order: all but the twelve W_qb copies done
+  // means the q_a rows and the w_qa slice are in
+  __builtin_amdgcn_s_waitcnt((12 & 15) | (7 << 4) | (15 << 8));
+  asm volatile("" ::: "memory");
+  bf16x8 xr[kMKs], wq[kMKs];
 #pragma unroll
   for (int i = 0; i < kMKs; ++i) {
-    xr[i] = *(const bf16x8*)(a.qkv + (size_t)t_c * a.qkv_stride + k0 + 32 * i);
-    wq[i] = *(const bf16x8*)(a.w_qa + k0 + 32 * i);
-#pragma unroll
-    for (int nb = 0; nb < 2; ++nb) wr[nb][i] = *(const bf16x8*)(a.w_qb + (size_t)nrow_c[nb] * kQA + k0 + 32 * i);
+    xr[i] = *(const LDS_AS bf16x8*)(xs + qb_stage_off<2>(i16, 4 * i + g));
+    wq[i] = *(const LDS_AS bf16x8*)(wqs + 16 * (4 * i + g));  // columns 192w + 32i + 8g .. +7
   }
   // sum of squares of token t over this wave's eighth: the lane's 48 values,
   // then the four lanes l, l^16, l^32, l^48 that share the token
@@ -612,21 +694,34 @@ __global__ void __launch_bounds__(kQbnThreads) mla_qbn_kernel(QueryArgs a) {
 #pragma unroll
   for (int v = 0; v < W; ++v) tot += ssp[v][i16];
   const float rr = 1.0f / __builtin_sqrtf(tot / (float)kQA + a.eps);
-  f32x4 acc[2] = {};
+  bf16x8 xq[kMKs];
 #pragma unroll
   for (int i = 0; i < kMKs; ++i) {
     bf16x8 xn;
 #pragma unroll
     for (int e = 0; e < 8; ++e) xn[e] = (__bf16)(((float)xr[i][e] * rr) * (float)wq[i][e]);
-    const bf16x8 x = t_ok ? xn : bf16x8{};
+    xq[i] = t_ok ? xn : bf16x8{};
+  }
+  // (the empty asm takes the normalised rows, so that the compiler cannot
+  // sink their computation below the wait for the W_qb rows)
+  asm volatile("" ::"v"(xq[0]), "v"(xq[1]), "v"(xq[2]), "v"(xq[3]), "v"(xq[4]), "v"(xq[5]));
+  __builtin_amdgcn_s_waitcnt(0);  // the W_qb rows landed
+  asm volatile("" ::: "memory");
+  f32x4 acc[2] = {};
+#pragma unroll
+  for (int i = 0; i < kMKs; ++i) {
 #pragma unroll
     for (int nb = 0; nb < 2; ++nb) {
-      const bf16x8 y = row_ok[nb] ? wr[nb][i] : bf16x8{};
-      acc[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(x, y, acc[nb], 0, 0, 0);
+      const bf16x8 wv = *(const LDS_AS bf16x8*)(wsg + qb_stage_off<4>(16 * nb + i16, 4 * i + g));
+      const bf16x8 y = row_ok[nb] ? wv : bf16x8{};
+      acc[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xq[i], y, acc[nb], 0, 0, 0);
     }
   }
-  red[w][0][lane] = acc[0];
-  red[w][1][lane] = acc[1];
+  // this wave's partial tiles into its own staging (read into registers
+  // above; nothing else reads it)
+  LDS_AS f32x4* const red = (LDS_AS f32x4*)xs;
+  red[lane] = acc[0];
+  red[64 + lane] = acc[1];
   __syncthreads();
   // thread (nb, r, l): register r of lane l in block nb, i.e. token
   // m0 + 4(l/16) + r and W_qb row n0 + 16nb + l%16; the waves' tiles added
@@ -634,7 +729,7 @@ __global__ void __launch_bounds__(kQbnThreads) mla_qbn_kernel(QueryArgs a) {
   const int l = tid & 63, r = (tid >> 6) & 3, nb = tid >> 8;
   float v = 0.0f;
 #pragma unroll
-  for (int u = 0; u < W; ++u) v += red[u][nb][l][r];
+  for (int u = 0; u < W; ++u) v += ((const LDS_AS f32x4*)stage[u])[64 * nb + l][r];
   const int tt = m0 + 4 * (l >> 4) + r, nn = n0 + 16 * nb + (l & 15);
   if (tt < a.batch && nn < nrows) a.qbm[(size_t)tt * nrows + nn] = (__bf16)v;
 }
@@ -644,6 +739,12 @@ __global__ void __launch_bounds__(64) mla_qlm_kernel(QueryArgs a) {
   const int lane = threadIdx.x;
   const int head = blockIdx.x, c0 = blockIdx.y * kUkCols, m0 = blockIdx.z * kTok;
   const int nrows = a.heads * kQB;
+  // the scale and this lane's two rope values (below) load with everything else
+  const float qsi = a.q_scale_inv[0];
+  const int rt = m0 + (lane >> 1), rr = 4 * blockIdx.y + 2 * (lane & 1);
+  const bool rt_ok = rt < a.batch;
+  const __bf16* rsrc = a.qbm + (size_t)min(rt, a.batch - 1) * nrows + (size_t)head * kQB + kNope + rr;
+  const __bf16 rv[2] = {rsrc[0], rsrc[1]};
   // W_uk rows: 128 rows of 64 bytes, four 16-byte chunks each; lane l takes
   // chunk l%4 of rows l/4 + 16j
   u32x4 wv[8];
@@ -682,25 +783,30 @@ __global__ void __launch_bounds__(64) mla_qlm_kernel(QueryArgs a) {
     const bf16x8 bfr = __builtin_shufflevector(r0, r1, 0, 1, 2, 3, 4, 5, 6, 7);
     acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[ks], bfr, acc, 0, 0, 0);
   }
-  // lane l, register r: token m0 + 8(r/4) + 4(l/32) + r%4, column c0 + l%32
-  const float qsi = a.q_scale_inv[0];
-  const int c = c0 + (lane & 31);
+  // lane l, register r: token tb + 8(r/4) + r%4 with tb = m0 + 4(l/32),
+  // column c0 + l%32; byte offsets fit 32 bits (at most 128 tokens here)
+  const int tb = m0 + 4 * (lane >> 5);
+  const uint32_t tstride = (uint32_t)a.heads * kOut;
+  const uint32_t o0 = ((uint32_t)tb * a.heads + head) * kOut + c0 + (lane & 31);
+  uint32_t cc[8];
 #pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    const int bb = m0 + 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3);
-    if (bb >= a.batch) continue;
-    a.out[((size_t)bb * a.heads + head) * kOut + c] = e4m3_of_product((float)(__bf16)acc[i], qsi);
+  for (int i = 0; i < 16; i += 2) cc[i / 2] = e4m3x2_of_products((float)(__bf16)acc[i], (float)(__bf16)acc[i + 1], qsi);
+  if (m0 + kTok <= a.batch) {  // (uniform) every token of the tile exists
+#pragma unroll
+    for (int i = 0; i < 16; ++i)
+      a.out[o0 + (uint32_t)(8 * (i >> 2) + (i & 3)) * tstride] = (uint8_t)(cc[i / 2] >> (8 * (i & 1)));
+  } else {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int ti = 8 * (i >> 2) + (i & 3);
+      if (tb + ti < a.batch) a.out[o0 + (uint32_t)ti * tstride] = (uint8_t)(cc[i / 2] >> (8 * (i & 1)));
+    }
   }
   // the rope rows of Q_B, encoded as they are: column block y takes rope
   // values 4y .. 4y+3 of the 32 tokens, lane l two of them for token m0 + l/2
   {
-    const int t = m0 + (lane >> 1), r = 4 * blockIdx.y + 2 * (lane & 1);
-    if (t < a.batch) {
-      const __bf16* src = a.qbm + (size_t)t * nrows + (size_t)head * kQB + kNope + r;
-      uint8_t* dst = a.out + ((size_t)t * a.heads + head) * kOut + kDV + r;
-      dst[0] = e4m3_of_product((float)src[0], qsi);
-      dst[1] = e4m3_of_product((float)src[1], qsi);
-    }
+    const uint32_t cc = e4m3x2_of_products((float)rv[0], (float)rv[1], qsi);
+    if (rt_ok) *(uint16_t*)(a.out + ((size_t)rt * a.heads + head) * kOut + kDV + rr) = (uint16_t)cc;
   }
 }
 }  // namespace

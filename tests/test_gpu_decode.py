@@ -239,6 +239,33 @@ def test_running_max_jumps_in_one_token_half(half, kv_format):
     compare(inp, out, lse, rtol=2.0**-7, scale=abs_weighted_v(inp))
 
 
+@pytest.mark.parametrize("heads,e", [(128, 40), (128, -40), (64, 40), (8, 40)])
+def test_split_partials_far_from_unit_scale(heads, e):
+    """V scaled by 2^e (latent columns times 2^e, the queries' latent columns
+    times 2^-e: every score, and so every p, stays the same bit for bit) on
+    sequences that split over several ranges.  O scales by 2^e exactly, so
+    the bar is the usual one times 2^e.  At 64 and more rows the pieces store
+    fp16 partials with a power-of-two factor per row and 128 columns: without
+    the factor 2^40 would overflow fp16 and 2^-40 would fall below its
+    subnormals."""
+    inp = synth.make_decode_inputs(151 + heads + e, batch=3, heads=heads, seqlens=[20000, 3000, 129])
+    kv = codecs.bf16_bits_to_f64(inp["kv"]).reshape(-1, 576)
+    kv[:, :512] *= 2.0**e
+    inp["kv"] = codecs.f64_to_bf16_bits(kv).reshape(inp["kv"].shape)
+    q = codecs.bf16_bits_to_f64(inp["q"])
+    q[..., :512] *= 2.0**-e
+    inp["q"] = codecs.f64_to_bf16_bits(q)
+    _say(f"[decode split partials, V x 2^{e}] H={heads}")
+    out, lse = run_gpu(inp)
+    ref = run_oracle(inp)
+    go = out.float().cpu().numpy().astype(np.float64)
+    assert np.all(np.isfinite(go)), "non-finite output"
+    err_o = np.max(np.abs(go - ref["O"])) * 2.0**-e
+    err_l = np.max(np.abs(lse.cpu().numpy().astype(np.float64) - ref["LSE"]))
+    _say(f"   max|dO|/2^e={err_o:.3e} (max|O|/2^e={np.max(np.abs(ref['O'])) * 2.0**-e:.3e})  max|dLSE|={err_l:.3e}")
+    assert err_o <= O_TOL and err_l <= LSE_TOL
+
+
 def test_topk_masking_rules():
     """Entries that are -1, negative, or at/after seqlen contribute nothing; a
     sequence whose entries are all masked gets O = 0 and LSE = -inf."""

@@ -15,7 +15,9 @@ import torch
 
 import mqa_latent_kv_amd as mla
 from mqa_latent_kv_amd import synth
+from oracle import codecs
 from oracle import mla_oracle as mo
+from oracle.codecs import f64_to_e4m3
 
 pytestmark = pytest.mark.gpu
 
@@ -147,3 +149,32 @@ def test_insert_full_size_in_benchmark_configuration():
     ins.update(cache=dec["kv"], slots=slots, k_scale_inv=float(dec["kv_scales"][0]))
     _say(f"[insert full-size] T={ins['tokens']} pages={dec['kv'].shape[0]}")
     check_insert(ins, run_insert(ins))
+
+
+@pytest.mark.parametrize("ksi", [0.3, 1.0 / 3.0, 0.125, 448.0 / 3.0, 1e-3, 7.0, 3.0517578125e-05 * 1.7])
+def test_insert_encodes_every_bf16_value(ksi):
+    """The device FP8 encoder on every finite bf16 value: 1024 tokens whose 64
+    rope values run through all 65536 bf16 bit patterns (non-finite ones
+    replaced by 0), with latent inputs of 1 and eps = 0 so that the RMSNorm
+    factor is exactly 1 and the latent values are the w_kva weights
+    themselves.  Every code must equal the e4m3 code of the exact product
+    value * k_scale_inv, bit for bit; scales 0.3 and 1/3 put fp32 products on
+    e4m3 midpoints, where the exact product decides."""
+    T = 1024
+    bits = np.arange(T * 64, dtype=np.uint32).astype(np.uint16)
+    bits[(bits & 0x7F80) == 0x7F80] = 0
+    rng = np.random.default_rng(7)
+    wbits = rng.integers(0, 1 << 16, 512).astype(np.uint16)
+    wbits[(wbits & 0x7F80) == 0x7F80] = 0x3F80
+    qkv = np.zeros((T, 2112), dtype=np.uint16)
+    qkv[:, 1536:2048] = 0x3F80  # 1.0
+    qkv[:, 2048:] = bits.reshape(T, 64)
+    inp = {"qkv": qkv, "w_kva": wbits, "cache": np.zeros((16, 64, 576), dtype=np.uint8),
+           "slots": np.arange(T, dtype=np.int64), "k_scale_inv": float(ksi), "eps": 0.0, "tokens": T}
+    _say(f"[insert encoder sweep] k_scale_inv={ksi!r}")
+    got = run_insert(inp).reshape(T, 576)
+    q = float(np.float32(ksi))
+    want_rope = f64_to_e4m3(codecs.bf16_bits_to_f64(bits) * q).reshape(T, 64)
+    want_lat = f64_to_e4m3(codecs.bf16_bits_to_f64(wbits) * q)
+    np.testing.assert_array_equal(got[:, 512:], want_rope)
+    np.testing.assert_array_equal(got[:, :512], np.broadcast_to(want_lat, (T, 512)))
