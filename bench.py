@@ -424,7 +424,21 @@ def main():
     c1.record(stream)
     torch.cuda.synchronize()
     copy_gbs = 5 * 2 * (1 << 30) / (c0.elapsed_time(c1) / 1e3) / 1e9
-    del flush, sweep_acc, src, dst
+    # and a read-only stream: the library GEMV of torch.mv over the same 1 GiB
+    # as a [2^19, 1024] bf16 matrix (writes 1 MB), the fastest read-only
+    # primitive at hand here, which bounds what a kernel that only reads HBM
+    # reaches (torch's reductions stay near 3.8 TB/s)
+    rd = src.view(torch.bfloat16).view(-1, 1024)
+    xv = torch.ones(1024, dtype=torch.bfloat16, device=dev)
+    yv = torch.empty(rd.shape[0], dtype=torch.bfloat16, device=dev)
+    torch.mv(rd, xv, out=yv)
+    c0.record(stream)
+    for _ in range(5):
+        torch.mv(rd, xv, out=yv)
+    c1.record(stream)
+    torch.cuda.synchronize()
+    read_gbs = 5 * (1 << 30) / (c0.elapsed_time(c1) / 1e3) / 1e9
+    del flush, sweep_acc, src, dst, rd, xv, yv
 
     nbytes = decode_bytes(inp) + (query_bytes(qin) if qin else 0) + (insert_bytes(B) if ins else 0)
     flops = decode_flops(inp) + (query_flops(qin) if qin else 0) + (insert_flops(B) if ins else 0)
@@ -432,14 +446,16 @@ def main():
     achieved = nbytes / kern_avg_s / 1e9
     tflops = flops / kern_avg_s / 1e12
     value = nbytes / (ms_per_step / 1e3) / 1e9
-    ws_kernel = "mla_decode_ws_kernel<{},{}> + mla_merge_kernel"
-    kernels = {"topk_sparse": "mla_decode_kernel<2,false,2,false> + mla_merge_kernel",
-               "fp8_cache": "mla_decode_kernel<2,false,1,false> + mla_merge_kernel",
-               "query_decode": "mla_qb_kernel + mla_ql_kernel + mla_decode_kernel<4,true,0,false> + mla_merge_kernel",
-               "query_narrow_decode": "mla_qb_gemv_kernel + mla_ql_gemv_kernel + " + ws_kernel.format("true", "false"),
-               "insert_decode": "mla_kv_insert_kernel + mla_decode_kernel<2,false,4,false> + mla_merge_kernel",
-               "mtp_bf16": ws_kernel.format("false", "true")}
-    kernel = kernels.get(name, ws_kernel.format("false", "false"))
+    kernels = {"topk_sparse": "mla_decode_ws_kernel<1,false,false,true> + mla_merge_kernel<true>",
+               "fp8_cache": "mla_decode_ws_kernel<1,false,false,false> + mla_merge_kernel<true>",
+               "query_decode": "mla_qbn_kernel + mla_qlm_kernel + mla_decode_kernel<4,true,0,false> + "
+                               "mla_merge_kernel<false>",
+               "query_narrow_decode": "mla_qb_gemv_kernel + mla_ql_gemv_kernel + "
+                                      "mla_decode_ws_kernel<0,true,false,false> + mla_merge_kernel<true>",
+               "insert_decode": "mla_kv_insert_kernel + mla_decode_ws_kernel<2,false,false,false> + "
+                                "mla_merge_kernel<true>",
+               "mtp_bf16": "mla_decode_ws_kernel<0,false,true,false> + mla_merge_kernel<true>"}
+    kernel = kernels.get(name, "mla_decode_ws_kernel<0,false,false,false> + mla_merge_kernel<true>")
     # above the ridge (2.5 PFLOP/s over 8 TB/s = 312.5 flop/B) the step is bound by the bf16 MFMA rate:
     # top-k (345 flop/B) and the per-tensor FP8 cache at 128 heads (432 flop/B)
     mfma_bound = flops / nbytes > MFMA_BF16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9)
@@ -455,6 +471,7 @@ def main():
         "hbm_gbs": round(achieved, 1),
         "mfma_tflops": round(tflops, 1),
         "copy_ceiling_gbs": round(copy_gbs, 1),
+        "read_ceiling_gbs": round(read_gbs, 1),
     }
     seq = inp["seqlens"]
     res = {

@@ -273,25 +273,35 @@ __device__ __forceinline__ void ws_scores8(const lds_char* buf, const uint32_t (
     u32x2 raw[2][4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) raw[0][i] = *(const LDS_AS u32x2*)(buf + ka[i]);
+    // tile t's dot products go to tt[t & 1]; their scaled sum into s waits
+    // until tile t+1's MFMAs are issued, so the matrix core does not drain
+    // between tiles
+    f32x4 tt[2][2];
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
       if (t + 1 < 4) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) raw[(t + 1) & 1][i] = *(const LDS_AS u32x2*)(buf + ka[i] + kGroupBytes * (t + 1));
       }
-      f32x4 tt[2];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const bf16x8 kb = codes_bf16(raw[t & 1][i]);
 #pragma unroll
         for (int j = 0; j < 2; ++j)
-          tt[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kb, qf[4 * t + i][j], i == 0 ? f32x4{} : tt[j], 0, 0, 0);
+          tt[t & 1][j] =
+              __builtin_amdgcn_mfma_f32_16x16x32_bf16(kb, qf[4 * t + i][j], i == 0 ? f32x4{} : tt[t & 1][j], 0, 0, 0);
       }
+      if (t > 0) {
 #pragma unroll
-      for (int j = 0; j < 2; ++j)
+        for (int j = 0; j < 2; ++j)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) s[j][e] = __builtin_fmaf(sc[e][t], tt[j][e], s[j][e]);
+          for (int e = 0; e < 4; ++e) s[j][e] = __builtin_fmaf(sc[e][t - 1], tt[(t - 1) & 1][j][e], s[j][e]);
+      }
     }
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) s[j][e] = __builtin_fmaf(sc[e][3], tt[1][j][e], s[j][e]);
   } else {
     u32x2 raw[2][4];
 #pragma unroll
