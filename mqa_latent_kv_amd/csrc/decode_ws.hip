@@ -443,9 +443,14 @@ __device__ __forceinline__ void score_role(const DecodeArgs& a, const Plan& pl, 
     for (int j = 0; j < 2; ++j) lim[j] = CAUSAL ? min(sgm.sg.tok1, sgm.seglen - lag[j]) : sgm.sg.tok1;
     const int lim_lo = min(lim[0], lim[1]);
 
-    barrier();  // X: the value waves' first copies are issued before these loads
-    // queries (B operand): row qrow[j], columns 32k + 8(lane/16) .. +7
+    // queries (B operand): row qrow[j], columns 32k + 8(lane/16) .. +7.
+    // Dense pages: after barrier X, so that they queue behind the value
+    // waves' copies of slot 0.  Top-k lists (bf16 queries): before it, where
+    // they load while the value waves wait for the list entries and their
+    // pages, two round trips before any copy can be issued.
     bf16x8 qf[kQk][2];
+    constexpr bool kEarlyQ = TOPK && !Q_FP8;
+    if constexpr (!kEarlyQ) barrier();  // X
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
       const int rr = qok[j] ? qrow[j] : 0;
@@ -464,6 +469,7 @@ __device__ __forceinline__ void score_role(const DecodeArgs& a, const Plan& pl, 
         }
       }
     }
+    if constexpr (kEarlyQ) barrier();  // X
     barrier();  // Y: the query loads are issued; the value waves copy slots 1 and 2 behind them
     wait_vm_lgkm0<0>();
 
@@ -859,67 +865,83 @@ __device__ __forceinline__ void value_role(const DecodeArgs& a, const Plan& pl, 
       barrier();  // the score waves' sums and votes
       const int votes = L.votes[0] | L.votes[1] | L.votes[2] | L.votes[3];
       if (__builtin_amdgcn_readfirstlane(votes) == 0) {
-        // normalise and store this wave's 128 columns of the 64 rows: the
+        // normalise this wave's 128 columns of the 64 rows, round them (bf16
+        // output, or the fp16 partial below), and store them through LDS: the
         // lane holds row 32rb + lane%32 and, per column block and register
-        // quad, four consecutive columns (one 8-byte store).  The lane index
-        // is passed through an empty asm so that the compiler cannot hoist
-        // these per-lane store addresses out of the slot loop.
+        // quad, four consecutive columns, so direct stores would scatter each
+        // instruction over 32 rows; the wave writes its 64 x 128 block into
+        // the ring (idle after the last slot; the next segment's copies start
+        // after a workgroup barrier), then stores two whole 256-byte rows per
+        // instruction.  The lane index is passed through an empty asm so
+        // that the compiler cannot hoist these per-lane addresses out of the
+        // slot loop.
         int ln = lane;
         asm volatile("" : "+v"(ln));
         const int i32 = ln & 31, h2 = ln >> 5;
         const size_t pslot = (size_t)(b + r);
+        constexpr int kPitch = 264;  // bytes per staged row: 256 + 8, so that 32 rows spread over the banks
+        static_assert(4 * 64 * kPitch <= kRing * Fm::kSlot, "the four waves' staging fits in the ring");
+        LDS_AS char* const stg = (LDS_AS char*)L.ring + v * (64 * kPitch);
+        const bool split = sgm.nsplit > 1;
+        char* const gbase = split ? (char*)(a.ws_o16 + pslot * a.heads * kDV)
+                                  : (char*)((__bf16*)a.out + (size_t)b * a.heads * kDV);
 #pragma unroll
         for (int rb = 0; rb < 2; ++rb) {
           const int lr = 32 * rb + i32;
           const float lt = L.xl[lr] + L.xl[64 + lr];
           const float inv = lt > 0.0f ? kdesc / lt : 0.0f;
-          const int row = row0 + lr;
-          if (sgm.nsplit == 1) {
-            if (row < a.heads) {
-              __bf16* orow = (__bf16*)a.out + ((size_t)b * a.heads + row) * kDV + 128 * v + 4 * h2;
-#pragma unroll
-              for (int cb = 0; cb < 4; ++cb)
-#pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                  // accumulator registers 4q .. 4q+3: columns 32cb + 8q + 4h2 .. +3
-                  f32x4 val;
-#pragma unroll
-                  for (int e = 0; e < 4; ++e) val[e] = o[rb][cb][4 * q + e] * inv;
-                  *(bf16x4*)(orow + 32 * cb + 8 * q) = __builtin_convertvector(val, bf16x4);
-                }
-            }
-          } else {
-            // a piece of a split sequence: the normalised values v of this
-            // row's 128 columns as fp16 of v / 2^e, with e chosen from their
-            // largest magnitude m (= f 2^x, f in [0.5, 1)) as x - 15, which
-            // puts m / 2^e in [2^14, 2^15) below the fp16 maximum; the
-            // scaling is exact, so each value carries one fp16 rounding, at
-            // most 2^-11 m.  (Zero, inf and NaN maxima give x = 0: the values
-            // pass unchanged in range or as inf and NaN.)  The clamp keeps
-            // 2^-e and 2^e normal fp32 numbers.
-            // (the largest |o| times inv is the largest |o inv|: inv > 0 and
-            // rounding is monotonic)
+          // a piece of a split sequence stores the normalised values v of
+          // this row's 128 columns as fp16 of v / 2^e, with e chosen from
+          // their largest magnitude m (= f 2^x, f in [0.5, 1)) as x - 15,
+          // which puts m / 2^e in [2^14, 2^15) below the fp16 maximum; the
+          // scaling is exact, so each value carries one fp16 rounding, at
+          // most 2^-11 m.  (Zero, inf and NaN maxima give x = 0: the values
+          // pass unchanged in range or as inf and NaN.)  The clamp keeps
+          // 2^-e and 2^e normal fp32 numbers.  (The largest |o| times inv is
+          // the largest |o inv|: inv > 0 and rounding is monotonic.)  The
+          // scaling folds into inv: o (inv 2^-e) = (o inv) 2^-e exactly
+          // while inv 2^-e stays a normal number, that is unless the values
+          // reach 2^100.
+          float sinv = inv;
+          int ex = 0;
+          if (split) {
             float mx = 0.0f;
 #pragma unroll
             for (int cb = 0; cb < 4; ++cb)
 #pragma unroll
               for (int k = 0; k < 16; ++k) mx = fmaxf(mx, fabsf(o[rb][cb][k]));
             mx = max_halves(mx) * inv;  // lanes l and l^32 hold the same row
-            const int ex = min(max(__builtin_amdgcn_frexp_expf(mx) - 15, -110), 113);
-            if (row < a.heads) {
-              _Float16* prow = a.ws_o16 + (pslot * a.heads + row) * kDV + 128 * v + 4 * h2;
+            ex = min(max(__builtin_amdgcn_frexp_expf(mx) - 15, -110), 113);
+            sinv = __builtin_amdgcn_ldexpf(inv, -ex);
+          }
 #pragma unroll
-              for (int cb = 0; cb < 4; ++cb)
+          for (int cb = 0; cb < 4; ++cb)
 #pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                  f32x4 val;
+            for (int q = 0; q < 4; ++q) {
+              // accumulator registers 4q .. 4q+3: columns 32cb + 8q + 4h2 .. +3
+              f32x4 val;
 #pragma unroll
-                  for (int e = 0; e < 4; ++e) val[e] = __builtin_amdgcn_ldexpf(o[rb][cb][4 * q + e] * inv, -ex);
-                  *(f16x4*)(prow + 32 * cb + 8 * q) = __builtin_convertvector(val, f16x4);
-                }
-              if (h2 == 0) a.ws_sc[(pslot * a.heads + row) * 4 + v] = __builtin_amdgcn_ldexpf(1.0f, ex);
+              for (int e = 0; e < 4; ++e) val[e] = o[rb][cb][4 * q + e] * sinv;
+              LDS_AS char* const dst = stg + lr * kPitch + 2 * (32 * cb + 8 * q + 4 * h2);
+              if (split) *(LDS_AS f16x4*)dst = __builtin_convertvector(val, f16x4);
+              else *(LDS_AS bf16x4*)dst = __builtin_convertvector(val, bf16x4);
+            }
+          // this block's 32 rows: rows 32rb + 2k and +1 from lanes 0..31 and
+          // 32..63, four columns each (the stores drain while the next
+          // block is formed)
+#pragma unroll
+          for (int k0 = 0; k0 < 16; k0 += 8) {
+            u32x2 x[8];
+#pragma unroll
+            for (int k = 0; k < 8; ++k) x[k] = *(const LDS_AS u32x2*)(stg + (32 * rb + 2 * (k0 + k) + h2) * kPitch + 8 * i32);
+#pragma unroll
+            for (int k = 0; k < 8; ++k) {
+              const int row = row0 + 32 * rb + 2 * (k0 + k) + h2;
+              if (row < a.heads) *(u32x2*)(gbase + ((size_t)row * kDV + 128 * v + 4 * i32) * 2) = x[k];
             }
           }
+          if (split && h2 == 0 && row0 + lr < a.heads)
+            a.ws_sc[(pslot * a.heads + row0 + lr) * 4 + v] = __builtin_amdgcn_ldexpf(1.0f, ex);
         }
         break;
       }
