@@ -63,11 +63,13 @@ __device__ __forceinline__ void wait_vm_lgkm0() {
 
 __device__ __forceinline__ void barrier() { asm volatile("s_barrier" ::: "memory"); }
 
-__device__ __forceinline__ int units_of(const DecodeArgs& a, int b) {
-  if (a.topk > 0) return (a.topk + kPage - 1) / kPage;
-  int s = a.seqlens[b];
+__device__ __forceinline__ int units_of_len(const DecodeArgs& a, int s) {
   s = s < 0 ? 0 : (s > a.max_pages * kPage ? a.max_pages * kPage : s);
   return (s + kPage - 1) / kPage;
+}
+__device__ __forceinline__ int units_of(const DecodeArgs& a, int b) {
+  if (a.topk > 0) return (a.topk + kPage - 1) / kPage;
+  return units_of_len(a, a.seqlens[b]);
 }
 
 __device__ __forceinline__ int clamp_page(int p, int num_pages) {
@@ -101,13 +103,17 @@ struct Plan {
 
 // inclusive scan over the lanes of a wave (ds_bpermute moves data between
 // lanes; it touches no LDS memory)
+// (in registers: shifts by 1, 2, 4 and 8 lanes inside each 16-lane row by
+// DPP row_shr, lanes shifted in from outside the row adding 0, then the
+// three row totals taken by readlane and added to the rows after them)
 __device__ __forceinline__ int wave_incl_scan(int v, int lane) {
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const int t = __builtin_amdgcn_ds_bpermute((lane - off) << 2, v);
-    v += lane >= off ? t : 0;
-  }
-  return v;
+  v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xF, 0xF, false);  // row_shr:1
+  v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xF, 0xF, false);  // row_shr:2
+  v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xF, 0xF, false);  // row_shr:4
+  v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xF, 0xF, false);  // row_shr:8
+  const int r0 = __builtin_amdgcn_readlane(v, 15), r1 = __builtin_amdgcn_readlane(v, 31),
+            r2 = __builtin_amdgcn_readlane(v, 47);
+  return v + (lane >= 16 ? r0 : 0) + (lane >= 32 ? r1 : 0) + (lane >= 48 ? r2 : 0);
 }
 
 // Block-wide exclusive scan of one int per thread (NT threads); every
@@ -130,6 +136,21 @@ __device__ __forceinline__ int block_excl_scan(int v, int* scratch, int& total) 
   return before + incl - v;
 }
 
+// Whether any thread's v is nonzero, for every thread (NT threads; scratch:
+// NT/64 ints; two barriers).
+template <int NT>
+__device__ __forceinline__ bool block_any(int v, int* scratch) {
+  const int tid = threadIdx.x, wv = tid >> 6;
+  const bool w_any = __builtin_amdgcn_ballot_w64(v != 0) != 0;
+  if ((tid & 63) == 0) scratch[wv] = w_any ? 1 : 0;
+  __syncthreads();
+  int any = 0;
+#pragma unroll
+  for (int i = 0; i < (NT / 64); ++i) any |= scratch[i];
+  __syncthreads();
+  return any != 0;
+}
+
 // The range of workgroup r.  The units of all sequences (pages, or top-k
 // chunks of 64 entries) are laid end to end and cut into a.ranges equal
 // ranges.  With a.seg_pad > 0 each non-empty sequence also gets that many
@@ -140,14 +161,42 @@ __device__ __forceinline__ int block_excl_scan(int v, int* scratch, int& total) 
 // would only unbalance them.
 // (NT threads per workgroup; scratch holds NT + 2 ints)
 template <int NT>
-__device__ bool make_plan(const DecodeArgs& a, int r, int* scratch, Plan& pl) {
+__device__ bool make_plan(const DecodeArgs& a, int r, int* scratch, Plan& pl, int& units_g) {
   const int tid = threadIdx.x;
   const int B = a.batch;
   const int per = (B + NT - 1) / NT;
   const int lo = tid * per, hi = min(B, lo + per);
+  // a thread's first kCache sequences' units stay in registers for the two
+  // later passes (one sequence per thread up to NT sequences)
+  // (the loads go out together, from clamped indices, and are selected
+  // afterwards; the same pass loads the length of sequence blockIdx.x, which
+  // the kernel checks for emptiness: units_g, 1 past the batch)
+  constexpr int kCache = 2;
+  int uc[kCache];
+  const int bg = blockIdx.x;
+  if (a.topk > 0) {
+#pragma unroll
+    for (int i = 0; i < kCache; ++i) uc[i] = (a.topk + kPage - 1) / kPage;
+    units_g = uc[0];
+  } else {
+    int sl[kCache + 1];
+#pragma unroll
+    for (int i = 0; i < kCache; ++i) sl[i] = a.seqlens[min(lo + i, B - 1)];
+    sl[kCache] = a.seqlens[min(bg, B - 1)];
+#pragma unroll
+    for (int i = 0; i < kCache; ++i) uc[i] = units_of_len(a, sl[i]);
+    units_g = units_of_len(a, sl[kCache]);
+  }
+  units_g = bg < B ? units_g : 1;
+#pragma unroll
+  for (int i = 0; i < kCache; ++i) uc[i] = lo + i < hi ? uc[i] : 0;
+  auto units_at = [&](int b) {
+    const int i = b - lo;
+    return i == 0 ? uc[0] : i == 1 ? uc[1] : units_of(a, b);
+  };
   int units = 0, seqs = 0;
   for (int b = lo; b < hi; ++b) {
-    const int n = units_of(a, b);
+    const int n = units_at(b);
     units += n;
     seqs += n > 0 ? 1 : 0;
   }
@@ -160,13 +209,11 @@ __device__ bool make_plan(const DecodeArgs& a, int r, int* scratch, Plan& pl) {
     const int C0 = (total0 + a.ranges - 1) / a.ranges;
     int inside = 0, p = excl0;
     for (int b = lo; b < hi; ++b) {
-      const int n = units_of(a, b);
+      const int n = units_at(b);
       inside += (n > 0 && p % C0 != 0) ? 1 : 0;
       p += n;
     }
-    int any = 0;
-    block_excl_scan<NT>(inside, scratch, any);
-    pad = any > 0 ? a.seg_pad : 0;
+    pad = block_any<NT>(inside, scratch) ? a.seg_pad : 0;
   }
   // padded line: sequence b starts at (its unpadded start) + 2 pad (non-empty sequences before it)
   const int total = total0 + 2 * pad * nseq;
@@ -178,7 +225,7 @@ __device__ bool make_plan(const DecodeArgs& a, int r, int* scratch, Plan& pl) {
   if (start >= excl && start < incl) {
     int p = excl;
     for (int b = lo; b < hi; ++b) {
-      const int u = units_of(a, b);
+      const int u = units_at(b);
       const int n = u > 0 ? u + 2 * pad : 0;
       if (start < p + n) {
         scratch[NT] = b;

@@ -982,10 +982,12 @@ mla_decode_ws_kernel(DecodeArgs a) {
   const int r = (g % 8) * a.per_xcd + idx / a.slabs;
   const int slab = idx % a.slabs;
   Plan pl;
-  const bool has_work = r < a.ranges && make_plan<kWsThreads>(a, r, (int*)ring_mem, pl);
+  // (the plan also loads the length of sequence g, checked for emptiness below)
+  int units_g = 1;
+  const bool has_work = make_plan<kWsThreads>(a, r, (int*)ring_mem, pl, units_g) && r < a.ranges;
   // sequences with nothing to attend: O = 0, LSE = -inf
   for (int b = g; b < a.batch; b += gridDim.x) {
-    if (units_of(a, b) == 0) {
+    if ((b == g ? units_g : units_of(a, b)) == 0) {
       for (int i = tid; i < a.heads * (kDV / 4); i += kWsThreads)
         *(bf16x4*)((__bf16*)a.out + ((size_t)b * a.heads) * kDV + 4 * i) = bf16x4{};
       for (int i = tid; i < a.heads; i += kWsThreads) a.lse[(size_t)b * a.heads + i] = -INFINITY;
