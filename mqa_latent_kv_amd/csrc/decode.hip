@@ -1296,7 +1296,7 @@ mla_decode_kernel(DecodeArgs a) {
       const float inv = l_tot > 0.0f ? kdesc / l_tot : 0.0f;
       const float lse2 = l_tot > 0.0f ? st.m_ref + __builtin_amdgcn_logf(l_tot) : -INFINITY;
       if (head_ok) {
-        const size_t pslot = (size_t)(b + r);
+        const size_t pslot = piece_slot(a, b, r, first_r);
         __bf16* orow = (__bf16*)a.out + ((size_t)b * a.heads + head) * kDV;
         float* prow = a.ws_o + (pslot * a.heads + head) * kDV;
 #pragma unroll
@@ -1320,7 +1320,7 @@ mla_decode_kernel(DecodeArgs a) {
       }
       // where the pieces of b sit (every piece writes the same record); the
       // merge kernel that follows on the stream combines split sequences
-      if (tid == 0) a.ws_seq[b] = int2{b + first_r, nsplit};
+      if (tid == 0) a.ws_seq[b] = int2{first_r, nsplit};
     }
     p += n;
     ++b;
@@ -1339,7 +1339,14 @@ struct MergeArgs {
   void* out;
   float* lse;
   int32_t heads;
+  int32_t compact;  // the slot layout of DecodeArgs::compact
 };
+
+// workspace slot of piece s of sequence b whose first range is first_r
+__device__ __forceinline__ size_t merge_slot(const MergeArgs& m, int b, int first_r, int s) {
+  const int r = first_r + s;
+  return m.compact ? (size_t)(2 * r + (s == 0 ? 1 : 0)) : (size_t)(b + r);
+}
 
 constexpr int kMergeHeads = 4;  // heads per merge workgroup, 64 threads each
 
@@ -1363,7 +1370,7 @@ typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
 // used (a fixed count, so no branch separates them).  `col` is the first
 // column of the thread's group u = 0 (group u starts 4 * TPH * u later).
 template <int N, bool F16>
-__device__ __forceinline__ void merge_chunk(const MergeArgs& m, const float* lse_col, size_t head_slot0, int col,
+__device__ __forceinline__ void merge_chunk(const MergeArgs& m, int b, int first_r, int head, int col,
                                             int s0, f32x4 (&acc)[kMergeU], float& mx, float& wsum) {
   constexpr int TPH = kThreads / kMergeHeads;
   const int heads = m.heads;
@@ -1371,8 +1378,8 @@ __device__ __forceinline__ void merge_chunk(const MergeArgs& m, const float* lse
   f32x4 v[N][kMergeU];
 #pragma unroll
   for (int i = 0; i < N; ++i) {
-    l[i] = lse_col[(size_t)(s0 + i) * heads];
-    const size_t row = head_slot0 + (size_t)(s0 + i) * heads;  // (slot, head) row of piece s0 + i
+    const size_t row = merge_slot(m, b, first_r, s0 + i) * heads + head;  // (slot, head) row of piece s0 + i
+    l[i] = m.ws_lse[row];
 #pragma unroll
     for (int u = 0; u < kMergeU; ++u) {
       const int c = col + 4 * TPH * u;
@@ -1412,8 +1419,6 @@ __global__ void __launch_bounds__(kThreads) mla_merge_kernel(MergeArgs m) {
   constexpr int TPH = kThreads / kMergeHeads;
   const int head = blockIdx.y * kMergeHeads + threadIdx.x / TPH, sub = threadIdx.x % TPH;
   if (head >= m.heads) return;
-  const float* lse_col = m.ws_lse + (size_t)first * m.heads + head;
-  const size_t row0 = (size_t)first * m.heads + head;
   const int col = 4 * sub;
   constexpr int U = kMergeU;
   f32x4 acc[U];
@@ -1422,14 +1427,14 @@ __global__ void __launch_bounds__(kThreads) mla_merge_kernel(MergeArgs m) {
   float mx = -INFINITY, wsum = 0.0f;
   for (int s0 = 0; s0 < nsplit; s0 += kMergeChunk) {
     switch (min(kMergeChunk, nsplit - s0)) {  // uniform over the workgroup
-      case 1: merge_chunk<1, F16>(m, lse_col, row0, col, s0, acc, mx, wsum); break;
-      case 2: merge_chunk<2, F16>(m, lse_col, row0, col, s0, acc, mx, wsum); break;
-      case 3: merge_chunk<3, F16>(m, lse_col, row0, col, s0, acc, mx, wsum); break;
-      case 4: merge_chunk<4, F16>(m, lse_col, row0, col, s0, acc, mx, wsum); break;
-      case 5: merge_chunk<5, F16>(m, lse_col, row0, col, s0, acc, mx, wsum); break;
-      case 6: merge_chunk<6, F16>(m, lse_col, row0, col, s0, acc, mx, wsum); break;
-      case 7: merge_chunk<7, F16>(m, lse_col, row0, col, s0, acc, mx, wsum); break;
-      default: merge_chunk<8, F16>(m, lse_col, row0, col, s0, acc, mx, wsum); break;
+      case 1: merge_chunk<1, F16>(m, b, first, head, col, s0, acc, mx, wsum); break;
+      case 2: merge_chunk<2, F16>(m, b, first, head, col, s0, acc, mx, wsum); break;
+      case 3: merge_chunk<3, F16>(m, b, first, head, col, s0, acc, mx, wsum); break;
+      case 4: merge_chunk<4, F16>(m, b, first, head, col, s0, acc, mx, wsum); break;
+      case 5: merge_chunk<5, F16>(m, b, first, head, col, s0, acc, mx, wsum); break;
+      case 6: merge_chunk<6, F16>(m, b, first, head, col, s0, acc, mx, wsum); break;
+      case 7: merge_chunk<7, F16>(m, b, first, head, col, s0, acc, mx, wsum); break;
+      default: merge_chunk<8, F16>(m, b, first, head, col, s0, acc, mx, wsum); break;
     }
   }
   const float inv = wsum > 0.0f ? 1.0f / wsum : 0.0f;
@@ -1469,9 +1474,10 @@ int32_t decode_ranges(int32_t cus, int32_t batch, int32_t max_pages, int32_t top
 }
 
 
-// Workspace: [B] int2 piece records | [(ranges + B)][H] fp32 LSE | [(ranges + B)][H][512] fp32 O.
+// Workspace: [B] int2 piece records | [slots][H] fp32 LSE | [slots][H][512] fp32 O, with
+// slots = decode_partial_slots(ranges, B) (piece_slot gives a piece's slot).
 size_t decode_workspace_bytes(int32_t ranges, int32_t batch, int32_t heads, int32_t topk) {
-  const size_t slots = (size_t)ranges + (size_t)batch;
+  const size_t slots = (size_t)decode_partial_slots(ranges, batch);
   size_t n = align256(sizeof(int2) * (size_t)batch) + align256(sizeof(float) * slots * heads) +
              align256(sizeof(float) * slots * heads * kDV);
   (void)topk;
@@ -1532,7 +1538,8 @@ hipError_t launch_decode(const DecodeLaunch& din, hipStream_t stream) {
   a.lse = d.lse;
   a.slabs = slabs_for_heads(d.heads);
   char* ws = (char*)d.workspace;
-  const size_t slots = (size_t)d.ranges + (size_t)d.batch;
+  const size_t slots = (size_t)decode_partial_slots(d.ranges, d.batch);
+  a.compact = (int64_t)d.ranges + d.batch > 2 * (int64_t)d.ranges ? 1 : 0;
   a.ws_seq = (int2*)ws;
   ws += align256(sizeof(int2) * (size_t)d.batch);
   a.ws_lse = (float*)ws;
@@ -1580,6 +1587,7 @@ hipError_t launch_decode(const DecodeLaunch& din, hipStream_t stream) {
   m.out = d.out;
   m.lse = d.lse;
   m.heads = d.heads;
+  m.compact = a.compact;
   const dim3 mgrid(d.batch, (d.heads + kMergeHeads - 1) / kMergeHeads);
   if (ws_kernel) hipLaunchKernelGGL(mla_merge_kernel<true>, mgrid, dim3(kThreads), 0, stream, m);
   else hipLaunchKernelGGL(mla_merge_kernel<false>, mgrid, dim3(kThreads), 0, stream, m);

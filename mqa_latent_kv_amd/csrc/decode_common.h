@@ -63,6 +63,13 @@ __device__ __forceinline__ void wait_vm_lgkm0() {
 
 __device__ __forceinline__ void barrier() { asm volatile("s_barrier" ::: "memory"); }
 
+// Workspace slot of the piece of sequence b in range r (its first range
+// first_r): b + r, or in the compact layout 2r for a piece that continues a
+// sequence from an earlier range and 2r + 1 for one that starts in r.
+__device__ __forceinline__ size_t piece_slot(const DecodeArgs& a, int b, int r, int first_r) {
+  return a.compact ? (size_t)(2 * r + (r == first_r ? 1 : 0)) : (size_t)(b + r);
+}
+
 __device__ __forceinline__ int units_of_len(const DecodeArgs& a, int s) {
   s = s < 0 ? 0 : (s > a.max_pages * kPage ? a.max_pages * kPage : s);
   return (s + kPage - 1) / kPage;

@@ -572,7 +572,7 @@ __device__ __forceinline__ void score_role(const DecodeArgs& a, const Plan& pl, 
       if (__builtin_amdgcn_readfirstlane(votes) == 0) {
         // LSE of rows 32hb + 16j + i16 (token half 0 writes it)
         if (th == 0 && g4 == 0) {
-          const size_t pslot = (size_t)(b + r);
+          const size_t pslot = piece_slot(a, b, r, sgm.first_r);
 #pragma unroll
           for (int j = 0; j < 2; ++j) {
             const int lr = xrow + 16 * j;
@@ -584,7 +584,7 @@ __device__ __forceinline__ void score_role(const DecodeArgs& a, const Plan& pl, 
             }
           }
         }
-        if (w == 0 && lane == 0) a.ws_seq[b] = int2{b + sgm.first_r, sgm.nsplit};
+        if (w == 0 && lane == 0) a.ws_seq[b] = int2{sgm.first_r, sgm.nsplit};
         break;
       }
       // redo with the true maxima (then p <= 1)
@@ -878,7 +878,7 @@ __device__ __forceinline__ void value_role(const DecodeArgs& a, const Plan& pl, 
         int ln = lane;
         asm volatile("" : "+v"(ln));
         const int i32 = ln & 31, h2 = ln >> 5;
-        const size_t pslot = (size_t)(b + r);
+        const size_t pslot = piece_slot(a, b, r, sgm.first_r);
         constexpr int kPitch = 264;  // bytes per staged row: 256 + 8, so that 32 rows spread over the banks
         static_assert(4 * 64 * kPitch <= kRing * Fm::kSlot, "the four waves' staging fits in the ring");
         LDS_AS char* const stg = (LDS_AS char*)L.ring + v * (64 * kPitch);

@@ -42,7 +42,8 @@ struct DecodeArgs {
   _Float16* ws_o16;  // the same region as [(ranges + B)][H][512] fp16 of O / 2^e (wave-specialised kernel)
   float* ws_sc;      // then [(ranges + B)][H][4] the factors 2^e, one per row and 128 columns
   float* ws_lse;  // [(ranges + B)][H] base-2 LSE of partials
-  int2* ws_seq;   // [B] {workspace slot of piece 0, pieces}; pieces 0: nothing to attend
+  int2* ws_seq;   // [B] {range of piece 0, pieces}; pieces 0: nothing to attend
+  int32_t compact;   // partial slots: 2 per range (slot 2r + (r == first range)) instead of one per (b + r)
   int32_t topk_tq;           // top-k: lists per sequence (T); list b belongs to sequence b / T
   int32_t batch, heads, num_pages, max_pages, topk;
   int32_t tq;         // dense, several query tokens: T (rows of a sequence = T x heads_tok), else 1
@@ -67,6 +68,13 @@ void effective_dims(int32_t batch, int32_t heads, int32_t topk, int32_t tq, int3
 int32_t decode_ranges(int32_t cus, int32_t batch, int32_t max_pages, int32_t topk, int32_t heads);
 // Workspace bytes for a decode launch with `ranges` KV ranges.
 size_t decode_workspace_bytes(int32_t ranges, int32_t batch, int32_t heads, int32_t topk);
+// Partial slots of a decode workspace: one per (sequence + range) index, or,
+// when that is more, two per range (each range holds at most two pieces of
+// split sequences: one continuing from before its start, one running past
+// its end).
+inline int64_t decode_partial_slots(int32_t ranges, int32_t batch) {
+  return (int64_t)ranges + batch <= 2 * (int64_t)ranges ? (int64_t)ranges + batch : 2 * (int64_t)ranges;
+}
 // Clear the per-sequence piece records of a decode workspace (optional: every call rewrites them).
 hipError_t init_decode_workspace(void* workspace, int32_t batch, int32_t heads, hipStream_t stream);
 hipError_t launch_decode(const DecodeLaunch& d, hipStream_t stream);
