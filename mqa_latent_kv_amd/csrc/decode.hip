@@ -1340,6 +1340,13 @@ struct MergeArgs {
   float* lse;
   int32_t heads;
   int32_t compact;  // the slot layout of DecodeArgs::compact
+  // top-k lists (topk_units = ceil(topk / 64) > 0): the decode's cut of the
+  // line has a closed form (even_cut), so the pieces of a list are known
+  // without reading its record; 0 for pages
+  int32_t topk_units;
+  int32_t batch;
+  int32_t ranges;
+  int32_t seg_pad;
 };
 
 // workspace slot of piece s of sequence b whose first range is first_r
@@ -1413,8 +1420,19 @@ __device__ __forceinline__ void merge_chunk(const MergeArgs& m, int b, int first
 template <bool F16>
 __global__ void __launch_bounds__(kThreads) mla_merge_kernel(MergeArgs m) {
   const int b = blockIdx.x;
-  const int2 info = m.seq[b];
-  const int first = info.x, nsplit = info.y;
+  int first, nsplit;
+  if (m.topk_units > 0) {
+    // list b's units [q, q + u) on the padded line, q = b (u + 2 pad) + pad
+    int pad, C, total;
+    even_cut(m.batch, m.topk_units, m.ranges, m.seg_pad, pad, C, total);
+    const int q = b * (m.topk_units + 2 * pad) + pad;
+    first = q / C;
+    nsplit = (q + m.topk_units - 1) / C - first + 1;
+  } else {
+    const int2 info = m.seq[b];
+    first = info.x;
+    nsplit = info.y;
+  }
   if (nsplit <= 1) return;
   constexpr int TPH = kThreads / kMergeHeads;
   const int head = blockIdx.y * kMergeHeads + threadIdx.x / TPH, sub = threadIdx.x % TPH;
@@ -1588,6 +1606,10 @@ hipError_t launch_decode(const DecodeLaunch& din, hipStream_t stream) {
   m.lse = d.lse;
   m.heads = d.heads;
   m.compact = a.compact;
+  m.topk_units = d.topk > 0 ? (d.topk + kPage - 1) / kPage : 0;
+  m.batch = d.batch;
+  m.ranges = d.ranges;
+  m.seg_pad = a.seg_pad;
   const dim3 mgrid(d.batch, (d.heads + kMergeHeads - 1) / kMergeHeads);
   if (ws_kernel) hipLaunchKernelGGL(mla_merge_kernel<true>, mgrid, dim3(kThreads), 0, stream, m);
   else hipLaunchKernelGGL(mla_merge_kernel<false>, mgrid, dim3(kThreads), 0, stream, m);

@@ -123,39 +123,19 @@ __device__ __forceinline__ int wave_incl_scan(int v, int lane) {
   return v + (lane >= 16 ? r0 : 0) + (lane >= 32 ? r1 : 0) + (lane >= 48 ? r2 : 0);
 }
 
-// Block-wide exclusive scan of one int per thread (NT threads); every
-// thread also gets the total.  scratch: NT/64 ints; two barriers.
-template <int NT>
-__device__ __forceinline__ int block_excl_scan(int v, int* scratch, int& total) {
-  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-  const int incl = wave_incl_scan(v, lane);
-  if (lane == 63) scratch[wv] = incl;
-  __syncthreads();
-  int before = 0;
-  total = 0;
-#pragma unroll
-  for (int i = 0; i < (NT / 64); ++i) {
-    const int t = scratch[i];
-    before += i < wv ? t : 0;
-    total += t;
-  }
-  __syncthreads();
-  return before + incl - v;
-}
-
-// Whether any thread's v is nonzero, for every thread (NT threads; scratch:
-// NT/64 ints; two barriers).
-template <int NT>
-__device__ __forceinline__ bool block_any(int v, int* scratch) {
-  const int tid = threadIdx.x, wv = tid >> 6;
-  const bool w_any = __builtin_amdgcn_ballot_w64(v != 0) != 0;
-  if ((tid & 63) == 0) scratch[wv] = w_any ? 1 : 0;
-  __syncthreads();
-  int any = 0;
-#pragma unroll
-  for (int i = 0; i < (NT / 64); ++i) any |= scratch[i];
-  __syncthreads();
-  return any != 0;
+// The cut of the line when every sequence has the same number u of units
+// (top-k lists: u = ceil(topk / 64) for every list, whatever its length):
+// the plan below in closed form.  The unpadded line puts sequence b at b u,
+// so some sequence starts strictly inside a range of the unpadded cut
+// exactly when there are two or more and u is not a multiple of the cut
+// C0 = ceil(B u / ranges) (b = 1 is then such a start; otherwise every
+// start b u is a multiple of C0).
+__host__ __device__ __forceinline__ void even_cut(int batch, int u, int ranges, int seg_pad, int& pad, int& C,
+                                                  int& total) {
+  const int c0 = (batch * u + ranges - 1) / ranges;
+  pad = (seg_pad > 0 && batch >= 2 && u % c0 != 0) ? seg_pad : 0;
+  total = batch * (u + 2 * pad);
+  C = (total + ranges - 1) / ranges;
 }
 
 // The range of workgroup r.  The units of all sequences (pages, or top-k
@@ -166,11 +146,32 @@ __device__ __forceinline__ bool block_any(int v, int* scratch) {
 // cut: when every boundary falls on a cut (sequences of equal length, a
 // whole number of ranges each), every range runs one segment and the pads
 // would only unbalance them.
-// (NT threads per workgroup; scratch holds NT + 2 ints)
+// Top-k lists all have the same length, so their cut (even_cut) needs no
+// loads and no barriers.  Pages: the two block-wide scans (units and
+// non-empty sequences) share one pass and one barrier, the padding vote a
+// second, and the range's first sequence a third and fourth; every
+// exchange has its own scratch words, so no barrier guards a reuse.
+// (NT threads per workgroup; scratch holds 3 NT / 64 + 2 ints)
 template <int NT>
 __device__ bool make_plan(const DecodeArgs& a, int r, int* scratch, Plan& pl, int& units_g) {
   const int tid = threadIdx.x;
   const int B = a.batch;
+  if (a.topk > 0) {
+    const int u = (a.topk + kPage - 1) / kPage;
+    units_g = u;
+    int pad, C, total;
+    even_cut(B, u, a.ranges, a.seg_pad, pad, C, total);
+    const int start = r * C;
+    if (start >= total) return false;
+    const int line = u + 2 * pad;
+    pl.C = C;
+    pl.start = start;
+    pl.end = min(start + C, total);
+    pl.b0 = start / line;
+    pl.p0 = pl.b0 * line;
+    pl.pad = pad;
+    return true;
+  }
   const int per = (B + NT - 1) / NT;
   const int lo = tid * per, hi = min(B, lo + per);
   // a thread's first kCache sequences' units stay in registers for the two
@@ -181,11 +182,7 @@ __device__ bool make_plan(const DecodeArgs& a, int r, int* scratch, Plan& pl, in
   constexpr int kCache = 2;
   int uc[kCache];
   const int bg = blockIdx.x;
-  if (a.topk > 0) {
-#pragma unroll
-    for (int i = 0; i < kCache; ++i) uc[i] = (a.topk + kPage - 1) / kPage;
-    units_g = uc[0];
-  } else {
+  {
     int sl[kCache + 1];
 #pragma unroll
     for (int i = 0; i < kCache; ++i) sl[i] = a.seqlens[min(lo + i, B - 1)];
@@ -207,9 +204,27 @@ __device__ bool make_plan(const DecodeArgs& a, int r, int* scratch, Plan& pl, in
     units += n;
     seqs += n > 0 ? 1 : 0;
   }
-  int total0 = 0, nseq = 0;
-  const int excl0 = block_excl_scan<NT>(units, scratch, total0);
-  const int exclq = block_excl_scan<NT>(seqs, scratch, nseq);
+  // exclusive scans of units and of non-empty sequences, with their totals
+  constexpr int W = NT / 64;
+  const int lane = tid & 63, wv = tid >> 6;
+  const int iu = wave_incl_scan(units, lane), iq = wave_incl_scan(seqs, lane);
+  if (lane == 63) {
+    scratch[wv] = iu;
+    scratch[W + wv] = iq;
+  }
+  __syncthreads();
+  int bu = 0, bq = 0, total0 = 0, nseq = 0;
+#pragma unroll
+  for (int i = 0; i < W; ++i) {
+    const int tu = scratch[i], tq = scratch[W + i];
+    bu += i < wv ? tu : 0;
+    bq += i < wv ? tq : 0;
+    total0 += tu;
+    nseq += tq;
+  }
+  total0 = __builtin_amdgcn_readfirstlane(total0);
+  nseq = __builtin_amdgcn_readfirstlane(nseq);
+  const int excl0 = bu + iu - units, exclq = bq + iq - seqs;
   if (total0 == 0) return false;
   int pad = 0;
   if (a.seg_pad > 0) {
@@ -220,7 +235,13 @@ __device__ bool make_plan(const DecodeArgs& a, int r, int* scratch, Plan& pl, in
       inside += (n > 0 && p % C0 != 0) ? 1 : 0;
       p += n;
     }
-    pad = block_any<NT>(inside, scratch) ? a.seg_pad : 0;
+    const bool w_any = __builtin_amdgcn_ballot_w64(inside != 0) != 0;
+    if (lane == 0) scratch[2 * W + wv] = w_any ? 1 : 0;
+    __syncthreads();
+    int any = 0;
+#pragma unroll
+    for (int i = 0; i < W; ++i) any |= scratch[2 * W + i];
+    pad = __builtin_amdgcn_readfirstlane(any) != 0 ? a.seg_pad : 0;
   }
   // padded line: sequence b starts at (its unpadded start) + 2 pad (non-empty sequences before it)
   const int total = total0 + 2 * pad * nseq;
@@ -235,8 +256,8 @@ __device__ bool make_plan(const DecodeArgs& a, int r, int* scratch, Plan& pl, in
       const int u = units_at(b);
       const int n = u > 0 ? u + 2 * pad : 0;
       if (start < p + n) {
-        scratch[NT] = b;
-        scratch[NT + 1] = p;
+        scratch[3 * W] = b;
+        scratch[3 * W + 1] = p;
         break;
       }
       p += n;
@@ -247,8 +268,8 @@ __device__ bool make_plan(const DecodeArgs& a, int r, int* scratch, Plan& pl, in
   pl.C = __builtin_amdgcn_readfirstlane(C);
   pl.start = __builtin_amdgcn_readfirstlane(start);
   pl.end = __builtin_amdgcn_readfirstlane(min(start + C, total));
-  pl.b0 = __builtin_amdgcn_readfirstlane(scratch[NT]);
-  pl.p0 = __builtin_amdgcn_readfirstlane(scratch[NT + 1]);
+  pl.b0 = __builtin_amdgcn_readfirstlane(scratch[3 * W]);
+  pl.p0 = __builtin_amdgcn_readfirstlane(scratch[3 * W + 1]);
   pl.pad = __builtin_amdgcn_readfirstlane(pad);
   __syncthreads();
   return true;
