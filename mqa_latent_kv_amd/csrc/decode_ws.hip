@@ -667,40 +667,55 @@ __device__ __forceinline__ void value_role(const DecodeArgs& a, const Plan& pl, 
       const int p = min(max(idx >> 6, 0), a.max_pages - 1);
       dma4(tk_bt, 4u * (uint32_t)p, __builtin_amdgcn_readfirstlane(lds_addr((lds_char*)(tk_pg + (s & 7) * 64))));
     };
-    // cache row of entry j of slot s (its entry and page landed)
-    auto tk_row = [&](int s, int j, bool& ok) -> int {
-      const int idx = tk_idx[(s & 7) * 64 + j];
-      const int pg = tk_pg[(s & 7) * 64 + j];
-      ok = 32 * s + j < tk_nent && idx >= 0 && idx < tk_limit;
-      return ok ? clamp_page(pg, a.num_pages) * kPage + (idx & 63) : tk_fallback;
+    // cache rows of entries js[0..5] of slot s (their entries and pages
+    // landed).  The twelve LDS reads are all issued before any is used: the
+    // empty asm takes every loaded value at once, so the compiler neither
+    // waits after each read nor sinks the page read into the validity test
+    // (a lookup each, one LDS round trip after another).
+    auto tk_rows = [&](int s, const int (&js)[6], int (&row)[6], bool (&ok)[6]) {
+      int idx[6], pg[6];
+#pragma unroll
+      for (int i = 0; i < 6; ++i) {
+        idx[i] = tk_idx[(s & 7) * 64 + js[i]];
+        pg[i] = tk_pg[(s & 7) * 64 + js[i]];
+      }
+      asm volatile("" : "+v"(idx[0]), "+v"(idx[1]), "+v"(idx[2]), "+v"(idx[3]), "+v"(idx[4]), "+v"(idx[5]),
+                        "+v"(pg[0]), "+v"(pg[1]), "+v"(pg[2]), "+v"(pg[3]), "+v"(pg[4]), "+v"(pg[5]));
+#pragma unroll
+      for (int i = 0; i < 6; ++i) {
+        ok[i] = 32 * s + js[i] < tk_nent && idx[i] >= 0 && idx[i] < tk_limit;
+        row[i] = ok[i] ? clamp_page(pg[i], a.num_pages) * kPage + (idx[i] & 63) : tk_fallback;
+      }
     };
     // this wave's copies of slot s into ring position pos (s < nslots)
     auto dma_cols = [&](int s, int pos) {
       if constexpr (TOPK) {
         // gathered rows: lane i of copy rb fetches row 8rb + i/8 of the slot,
-        // position i%8 of the column group, from that entry's cache row
+        // position i%8 of the column group, from that entry's cache row.
+        // The six lookups go out together before the first copy (the copies
+        // are asm statements that no load moves across).
         const uint32_t base = __builtin_amdgcn_readfirstlane(lds_addr(L.ring + (pos & (kRing - 1)) * Fm::kSlot));
         const char* kvu = uniform_ptr(a.kv);
-        bool ok;
+        int js[6], row[6];
+        bool ok[6];
+#pragma unroll
+        for (int rb = 0; rb < 4; ++rb) js[rb] = 8 * rb + (lane >> 3);
+        js[4] = 8 * v + (lane >> 3);  // the rope group: rows 8v .. 8v+7
+        js[5] = lane & 31;            // the scales and the validity word: every row
+        tk_rows(s, js, row, ok);
 #pragma unroll
         for (int rb = 0; rb < 4; ++rb) {
-          const int j = 8 * rb + (lane >> 3);
-          const int row = tk_row(s, j, ok);
-          const uint32_t off = (uint32_t)row * Fm::kRow + 128u * v + 16u * ((lane & 7) ^ row_swz(j));
+          const uint32_t off = (uint32_t)row[rb] * Fm::kRow + 128u * v + 16u * ((lane & 7) ^ row_swz(js[rb]));
           dma16<0>(kvu, off, base + v * kGroupBytes + rb * 1024);
         }
         {
-          const int j = 8 * v + (lane >> 3);
-          const int row = tk_row(s, j, ok);
-          const int c = min((lane & 7) ^ row_swz(j), kChunks - 1);
-          dma16<0>(kvu, (uint32_t)row * Fm::kRow + 512u + 16u * c, base + 4 * kGroupBytes + v * 1024);
+          const int c = min((lane & 7) ^ row_swz(js[4]), kChunks - 1);
+          dma16<0>(kvu, (uint32_t)row[4] * Fm::kRow + 512u + 16u * c, base + 4 * kGroupBytes + v * 1024);
         }
         {
-          const int j = lane & 31;
-          const int row = tk_row(s, j, ok);
           if constexpr (F == kFmtFp8)
-            dma16<0>(uniform_ptr((const char*)a.kv_scales), 16u * (uint32_t)row, base + Fm::kScaleOff + v * 1024);
-          const uint64_t vm = __ballot(ok);
+            dma16<0>(uniform_ptr((const char*)a.kv_scales), 16u * (uint32_t)row[5], base + Fm::kScaleOff + v * 1024);
+          const uint64_t vm = __ballot(ok[5]);
           if (v == 0 && lane == 0) L.tkmask[pos & (kRing - 1)] = (uint32_t)vm;
         }
         return;
