@@ -447,28 +447,33 @@ __global__ void __launch_bounds__(kThreads) mla_ql_kernel(QueryArgs a) {
 // spread over many workgroups and reduced with wave FMAs; no MFMA tile would
 // be more than a quarter full.
 constexpr int kNarrow = 8;                                  // batches up to this size take this path
-constexpr int kQbRowsPerWave = 2;
-constexpr int kQbRowsPerWg = kQbRowsPerWave * (kThreads / 64);  // 8 W_qb rows per workgroup
+constexpr int kQbLanes = 8;                                 // lanes per W_qb row
+constexpr int kQbRowsPerWave = 64 / kQbLanes;               // 8
+constexpr int kQbRowsPerWg = kQbRowsPerWave * (kThreads / 64);  // 32 W_qb rows per workgroup
+constexpr int kQbLoads = kQA / (kQbLanes * 8);              // 24 loads of 8 weights per lane
 
-// RMSNorm + Q_B: a workgroup owns 8 rows of W_qb (2 per wave) for every
-// token.  Lane l holds columns 512k + 8l .. +7 (k = 0..2) of a W_qb row, of
-// w_qa and of a token's q_a row; each wave normalises tokens w, w + 4 into
-// LDS, then every wave forms its rows' dot products with every token: 24
-// FMAs per lane in fp32, then the wave sum.
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+// RMSNorm + Q_B: a workgroup owns 32 rows of W_qb (8 per wave) for every
+// token; eight lanes share a row, lane s of a row holding columns 64k + 8s
+// .. +7 (k = 0..23), so that each load instruction reads 128 contiguous
+// bytes of each of the wave's eight rows, and all 24 loads are issued before
+// anything else.  Each wave normalises tokens w, w + 4 into LDS (the
+// workgroup's every token), then every lane forms the dot products of its
+// 192 weights with every token (bf16 pairs multiplied and added in fp32 by
+// v_dot2c_f32_bf16, reading the token's matching 8 columns from LDS, the
+// same 128 bytes for all eight rows), and the eight lanes of a row add their
+// sums (three lane swaps).
 __global__ void __launch_bounds__(kThreads) mla_qb_gemv_kernel(QueryArgs a) {
   __shared__ __attribute__((aligned(16))) bf16x8 xn[kNarrow][kQA / 8];  // normalised tokens, 24 KB
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int nrows = a.heads * kQB;
-  const int n0 = blockIdx.x * kQbRowsPerWg + kQbRowsPerWave * w;
-  // every load first: this wave's W_qb rows (clamped, unconditional), w_qa
-  // and the q_a rows of the tokens it normalises
-  bf16x8 wr[kQbRowsPerWave][3];
-#pragma unroll
-  for (int j = 0; j < kQbRowsPerWave; ++j) {
-    const int row = min(n0 + j, nrows - 1);
-#pragma unroll
-    for (int k = 0; k < 3; ++k) wr[j][k] = *(const bf16x8*)(a.w_qb + (size_t)row * kQA + 512 * k + 8 * lane);
-  }
+  const int sub = lane & (kQbLanes - 1);
+  const int row = blockIdx.x * kQbRowsPerWg + kQbRowsPerWave * w + lane / kQbLanes;
+  // every load first: w_qa and the q_a rows of the tokens this wave
+  // normalises, then this lane's W_qb weights (row clamped, unconditional);
+  // loads complete in order, so the normalisation runs while the weights
+  // are still arriving, and the products follow them in
   bf16x8 wq[3], xr[2][3];
 #pragma unroll
   for (int k = 0; k < 3; ++k) wq[k] = *(const bf16x8*)(a.w_qa + 512 * k + 8 * lane);
@@ -477,6 +482,13 @@ __global__ void __launch_bounds__(kThreads) mla_qb_gemv_kernel(QueryArgs a) {
     const int t = min(w + 4 * i, a.batch - 1);
 #pragma unroll
     for (int k = 0; k < 3; ++k) xr[i][k] = *(const bf16x8*)(a.qkv + (size_t)t * a.qkv_stride + 512 * k + 8 * lane);
+  }
+  asm volatile("" ::: "memory");  // (keeps the weight loads behind these)
+  bf16x8 wr[kQbLoads];
+  {
+    const bf16x8* wrow = (const bf16x8*)(a.w_qb + (size_t)min(row, nrows - 1) * kQA) + sub;
+#pragma unroll
+    for (int k = 0; k < kQbLoads; ++k) wr[k] = wrow[8 * k];
   }
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
@@ -501,27 +513,36 @@ __global__ void __launch_bounds__(kThreads) mla_qb_gemv_kernel(QueryArgs a) {
     }
   }
   __syncthreads();
-  const float qsi = a.q_scale_inv[0];
+  float acc[kNarrow];
 #pragma unroll
-  for (int j = 0; j < kQbRowsPerWave; ++j) {
-    const int row = n0 + j;
-    if (row >= nrows) break;  // wave-uniform
-    const int head = row / kQB, r = row % kQB;
-    for (int t = 0; t < a.batch; ++t) {
-      float d = 0.0f;
+  for (int t = 0; t < kNarrow; ++t) acc[t] = 0.0f;
 #pragma unroll
-      for (int k = 0; k < 3; ++k) {
-        const bf16x8 xv = xn[t][64 * k + lane];
+  for (int k = 0; k < kQbLoads; ++k) {
 #pragma unroll
-        for (int e = 0; e < 8; ++e) d = __builtin_fmaf((float)xv[e], (float)wr[j][k][e], d);
-      }
-      d = wave_sum(d);
-      if (lane == 0) {
-        const __bf16 v = (__bf16)d;
-        if (r < kNope) a.qn[((size_t)t * a.heads + head) * kNope + r] = v;
-        else a.out[((size_t)t * a.heads + head) * kOut + kDV + (r - kNope)] = e4m3_of_product((float)v, qsi);
-      }
+    for (int t = 0; t < kNarrow; ++t) {
+      if (t >= a.batch) break;  // uniform
+      const bf16x8 xv = xn[t][8 * k + sub];
+#pragma unroll
+      for (int e = 0; e < 8; e += 2)
+        acc[t] = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{xv[e], xv[e + 1]}, bf16x2{wr[k][e], wr[k][e + 1]}, acc[t],
+                                                  false);
     }
+  }
+#pragma unroll
+  for (int t = 0; t < kNarrow; ++t) {
+    acc[t] += __shfl_xor(acc[t], 1);
+    acc[t] += __shfl_xor(acc[t], 2);
+    acc[t] += __shfl_xor(acc[t], 4);
+  }
+  if (sub != 0 || row >= nrows) return;
+  const float qsi = a.q_scale_inv[0];
+  const int head = row / kQB, r = row % kQB;
+#pragma unroll
+  for (int t = 0; t < kNarrow; ++t) {
+    if (t >= a.batch) break;
+    const __bf16 v = (__bf16)acc[t];
+    if (r < kNope) a.qn[((size_t)t * a.heads + head) * kNope + r] = v;
+    else a.out[((size_t)t * a.heads + head) * kOut + kDV + (r - kNope)] = e4m3_of_product((float)v, qsi);
   }
 }
 
