@@ -404,6 +404,47 @@ def test_page_permutation_invariance_bitwise():
     assert torch.equal(lse1.view(torch.int32), lse2.view(torch.int32))
 
 
+def _sweep_case(i):
+    """Configuration i of the seeded sweep: cache format, heads, query tokens
+    per sequence, top-k length, query format, batch and lengths drawn at
+    random (empty sequences and page-multiple lengths included), at sizes the
+    oracle finishes in about a second."""
+    rng = np.random.default_rng(1000 + i)
+    kv = str(rng.choice(["bf16", "fp8", "fp8_tensor"]))
+    heads = int(rng.choice([8, 16, 32, 64, 128], p=[0.15, 0.15, 0.15, 0.25, 0.3]))
+    topk = 0 if rng.random() < 0.6 else int(rng.choice([64, 200, 777, 1024]))
+    T = 1 if rng.random() < 0.6 else int(rng.integers(2, 5))
+    qf = "fp8" if rng.random() < 0.3 else "bf16"
+    big = heads * T >= 256
+    batch = int(rng.integers(1, 4 if big else 7))
+    seqlens = rng.integers(0, (1500 if big else 3000) + 1, batch)
+    if rng.random() < 0.3:
+        seqlens[rng.integers(0, batch)] = 0
+    if rng.random() < 0.3:
+        seqlens[rng.integers(0, batch)] = 64 * int(rng.integers(1, 24))
+    pps = max(1, -(-int(seqlens.max()) // 64)) + int(rng.integers(0, 3))
+    kw = dict(batch=batch, heads=heads, seqlens=seqlens.tolist(), pages_per_seq=pps,
+              num_pages=batch * pps + int(rng.integers(0, 17)), kv_format=kv, q_format=qf, topk=topk,
+              tokens_per_seq=T)
+    if qf == "fp8":
+        kw["q_descale"] = 8.0
+    return kw
+
+
+@pytest.mark.parametrize("i", range(40))
+def test_decode_random_configurations(i):
+    """A seeded sweep over the decode's configuration space, each against the
+    oracle element by element (the fixed cases above pin the named corners;
+    this covers their combinations: FP8 queries on per-tile caches, top-k
+    lists with several query tokens, empty sequences beside long ones)."""
+    kw = _sweep_case(i)
+    inp = synth.make_decode_inputs(2000 + i, **kw)
+    _say(f"[decode sweep] i={i} kv={kw['kv_format']} q={kw['q_format']} H={kw['heads']} T={kw['tokens_per_seq']} "
+         f"topk={kw['topk']} seqlens={kw['seqlens']}")
+    out, lse = run_gpu(inp)
+    compare(inp, out, lse)
+
+
 @pytest.mark.parametrize("name", ["paged_bf16_4096", "paged_bf16", "query_decode", "query_narrow_decode", "fp8_cache", "topk_sparse",
                                   "insert_decode", "mtp_bf16"])
 def test_full_size_workloads_sampled(name):
