@@ -6,6 +6,13 @@ Bar: every e4m3 code equals the oracle's or is its neighbour in value order
 0xFF or 0x7F (NaN) for finite input.  The summation order of the two
 contractions differs from the oracle's, and a tie at an intermediate bf16 or
 the final e4m3 rounding can go either way, hence the one-step allowance.
+Where the oracle's value is below 2^-5 in magnitude, two steps: there the
+e4m3 step is a fixed 2^-9, and one intermediate bf16 rounding of Q_B that
+lands on the other side (its exact sum within the fp32 sum's error of a bf16
+midpoint) moves the absorbed value by ulp(qb) |W_uk| before the scale, which
+cancellation leaves as large as the value itself: at q_scale_inv = 4 with
+these weights about 1.3 steps of 2^-9 (measured: two codes of 5.35 million
+at batch 344, 27 heads).
 """
 import numpy as np
 import pytest
@@ -13,6 +20,7 @@ import torch
 
 import mqa_latent_kv_amd as mla
 from mqa_latent_kv_amd import synth
+from oracle import codecs
 from oracle import mla_oracle as mo
 
 pytestmark = pytest.mark.gpu
@@ -41,8 +49,11 @@ def check_codes(got, want):
     assert not np.any(got == 0xFF) and not np.any(got == 0x7F), "NaN code for finite input"
     step = np.abs(code_rank(got) - code_rank(want))
     same = np.mean(step == 0)
-    _say(f"   codes identical {same * 100:.3f}%, max step {step.max()}")
-    assert step.max() <= 1
+    small = np.abs(codecs.e4m3_to_f64(want)) < 2.0**-5  # where the e4m3 step is 2^-9
+    _say(f"   codes identical {same * 100:.3f}%, max step {step.max()} "
+         f"(values >= 2^-5: {step[~small].max() if np.any(~small) else 0})")
+    assert np.all(step[~small] <= 1)
+    assert np.all(step[small] <= 2)
     assert same >= 0.999
 
 
@@ -67,6 +78,29 @@ CASES = {
     "tiled_b129_h3": dict(seed=67, batch=129, heads=3),
     "tiled_b300_h16": dict(seed=68, batch=300, heads=16),
 }
+
+
+def _sweep_case(i):
+    """Configuration i of the seeded sweep: batch drawn from each of the three
+    forms' ranges in turn (narrow up to 8 tokens, medium 9-128, wide beyond),
+    heads, q_a row width, scale and eps at random."""
+    rng = np.random.default_rng(3000 + i)
+    lo, hi = [(1, 8), (9, 128), (129, 400)][i % 3]
+    return dict(batch=int(rng.integers(lo, hi + 1)), heads=int(rng.integers(1, 33)),
+                width=int(rng.choice([1536, 2112, 2176])), q_scale_inv=float(rng.choice([0.125, 0.3, 1.0, 4.0])),
+                eps=float(rng.choice([1e-6, 1e-3])))
+
+
+@pytest.mark.parametrize("i", range(24))
+def test_query_random_configurations(i):
+    """A seeded sweep over the query front end's batch sizes (all three
+    forms), head counts, row widths, scales and eps, against the oracle."""
+    kw = _sweep_case(i)
+    inp = synth.make_query_inputs(4000 + i, **kw)
+    _say(f"[query sweep] i={i} {kw}")
+    got = run_query(inp)
+    ref = mo.mla_query(inp["qkv"], inp["w_qa"], inp["w_qb"], inp["w_uk"], inp["q_scale_inv"], eps=inp["eps"])
+    check_codes(got, ref["out"])
 
 
 @pytest.mark.parametrize("name", list(CASES))
