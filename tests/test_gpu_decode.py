@@ -431,6 +431,37 @@ def _sweep_case(i):
     return kw
 
 
+def _sweep_case_long(i):
+    """Configuration i of the second sweep: fewer, longer sequences (up to
+    6000 tokens) with up to 512 query rows (T up to 4 at 128 heads), so that
+    sequences split over many ranges and slabs."""
+    rng = np.random.default_rng(5000 + i)
+    kv = str(rng.choice(["bf16", "fp8", "fp8_tensor"]))
+    heads = int(rng.choice([64, 128]))
+    T = int(rng.choice([1, 1, 2, 4]))
+    topk = 0 if rng.random() < 0.7 else int(rng.choice([1024, 2048]))
+    qf = "fp8" if rng.random() < 0.3 else "bf16"
+    batch = int(rng.integers(1, 3))
+    seqlens = rng.integers(2000, 6001, batch)
+    pps = -(-int(seqlens.max()) // 64)
+    kw = dict(batch=batch, heads=heads, seqlens=seqlens.tolist(), pages_per_seq=pps,
+              num_pages=batch * pps + int(rng.integers(0, 9)), kv_format=kv, q_format=qf, topk=topk, tokens_per_seq=T)
+    if qf == "fp8":
+        kw["q_descale"] = 8.0
+    return kw
+
+
+@pytest.mark.parametrize("i", range(32))
+def test_decode_random_long_configurations(i):
+    """The second seeded sweep (long sequences, many rows), against the oracle."""
+    kw = _sweep_case_long(i)
+    inp = synth.make_decode_inputs(6000 + i, **kw)
+    _say(f"[decode sweep long] i={i} kv={kw['kv_format']} q={kw['q_format']} H={kw['heads']} T={kw['tokens_per_seq']} "
+         f"topk={kw['topk']} seqlens={kw['seqlens']}")
+    out, lse = run_gpu(inp)
+    compare(inp, out, lse)
+
+
 @pytest.mark.parametrize("i", range(40))
 def test_decode_random_configurations(i):
     """A seeded sweep over the decode's configuration space, each against the
