@@ -77,6 +77,26 @@ CASES = {
 }
 
 
+def _sweep_case(i):
+    """Configuration i of the seeded sweep: token count, pool size (from a
+    tight fit to a pool many times larger), skipped tokens, scale and eps at
+    random."""
+    rng = np.random.default_rng(7000 + i)
+    tokens = int(rng.integers(1, 601))
+    num_pages = -(-tokens // 64) + int(rng.integers(0, 30))
+    return dict(tokens=tokens, num_pages=num_pages, skipped=int(rng.integers(0, tokens // 4 + 1)),
+                k_scale_inv=float(rng.choice([0.01, 1.0, 3.0, 32.0, 37.0])), eps=float(rng.choice([1e-6, 1e-3, 0.5])))
+
+
+@pytest.mark.parametrize("i", range(16))
+def test_insert_random_configurations(i):
+    """A seeded sweep of the insert's sizes, skips, scales and eps."""
+    kw = _sweep_case(i)
+    inp = synth.make_insert_inputs(8000 + i, **kw)
+    _say(f"[insert sweep] i={i} {kw}")
+    check_insert(inp, run_insert(inp))
+
+
 @pytest.mark.parametrize("name", list(CASES))
 def test_insert_matches_oracle(name):
     kw = dict(CASES[name])
