@@ -1417,10 +1417,8 @@ __device__ __forceinline__ void merge_chunk(const MergeArgs& m, int b, int first
   mx = cm;
 }
 
-template <bool F16>
-__global__ void __launch_bounds__(kThreads) mla_merge_kernel(MergeArgs m) {
-  const int b = blockIdx.x;
-  int first, nsplit;
+// The pieces of sequence b: its first range and their count.
+__device__ __forceinline__ void merge_pieces(const MergeArgs& m, int b, int& first, int& nsplit) {
   if (m.topk_units > 0) {
     // list b's units [q, q + u) on the padded line, q = b (u + 2 pad) + pad
     int pad, C, total;
@@ -1433,18 +1431,14 @@ __global__ void __launch_bounds__(kThreads) mla_merge_kernel(MergeArgs m) {
     first = info.x;
     nsplit = info.y;
   }
-  if (nsplit <= 1) return;
-  constexpr int TPH = kThreads / kMergeHeads;
-  const int head = blockIdx.y * kMergeHeads + threadIdx.x / TPH, sub = threadIdx.x % TPH;
-  if (head >= m.heads) return;
-  const int col = 4 * sub;
-  constexpr int U = kMergeU;
-  f32x4 acc[U];
-#pragma unroll
-  for (int u = 0; u < U; ++u) acc[u] = f32x4{};
-  float mx = -INFINITY, wsum = 0.0f;
-  for (int s0 = 0; s0 < nsplit; s0 += kMergeChunk) {
-    switch (min(kMergeChunk, nsplit - s0)) {  // uniform over the workgroup
+}
+
+// Pieces s_begin .. s_end-1 of one column group into a running state.
+template <bool F16>
+__device__ __forceinline__ void merge_run(const MergeArgs& m, int b, int first, int head, int col, int s_begin,
+                                          int s_end, f32x4 (&acc)[kMergeU], float& mx, float& wsum) {
+  for (int s0 = s_begin; s0 < s_end; s0 += kMergeChunk) {
+    switch (min(kMergeChunk, s_end - s0)) {  // uniform over the wave
       case 1: merge_chunk<1, F16>(m, b, first, head, col, s0, acc, mx, wsum); break;
       case 2: merge_chunk<2, F16>(m, b, first, head, col, s0, acc, mx, wsum); break;
       case 3: merge_chunk<3, F16>(m, b, first, head, col, s0, acc, mx, wsum); break;
@@ -1455,11 +1449,82 @@ __global__ void __launch_bounds__(kThreads) mla_merge_kernel(MergeArgs m) {
       default: merge_chunk<8, F16>(m, b, first, head, col, s0, acc, mx, wsum); break;
     }
   }
+}
+
+template <bool F16>
+__global__ void __launch_bounds__(kThreads) mla_merge_kernel(MergeArgs m) {
+  const int b = blockIdx.x;
+  int first, nsplit;
+  merge_pieces(m, b, first, nsplit);
+  if (nsplit <= 1) return;
+  constexpr int TPH = kThreads / kMergeHeads;
+  const int head = blockIdx.y * kMergeHeads + threadIdx.x / TPH, sub = threadIdx.x % TPH;
+  if (head >= m.heads) return;
+  const int col = 4 * sub;
+  constexpr int U = kMergeU;
+  f32x4 acc[U];
+#pragma unroll
+  for (int u = 0; u < U; ++u) acc[u] = f32x4{};
+  float mx = -INFINITY, wsum = 0.0f;
+  merge_run<F16>(m, b, first, head, col, 0, nsplit, acc, mx, wsum);
   const float inv = wsum > 0.0f ? 1.0f / wsum : 0.0f;
   bf16x4* dst = (bf16x4*)((__bf16*)m.out + ((size_t)b * m.heads + head) * kDV) + sub;
 #pragma unroll
   for (int u = 0; u < U; ++u) dst[u * TPH] = __builtin_convertvector(acc[u] * inv, bf16x4);
   if (sub == 0) m.lse[(size_t)b * m.heads + head] = wsum > 0.0f ? (mx + __builtin_amdgcn_logf(wsum)) * kLn2 : -INFINITY;
+}
+
+// The same combine for sequences split into many pieces, or grids too small
+// to fill the chip: one workgroup per (sequence, head), its four waves taking
+// consecutive quarters of the pieces (each in chunks, as above), then their
+// running states (max, sum, O columns) combined through LDS in wave order.
+// A lane owns the same two float4 column groups as in mla_merge_kernel.
+template <bool F16>
+__global__ void __launch_bounds__(kThreads) mla_merge_wide_kernel(MergeArgs m) {
+  static_assert(kThreads / kMergeHeads == 64, "one wave per column set");
+  constexpr int W = kThreads / 64;
+  __shared__ f32x4 sacc[W][kMergeU][64];
+  __shared__ float smx[W], ssum[W];
+  const int b = blockIdx.x, head = blockIdx.y;
+  int first, nsplit;
+  merge_pieces(m, b, first, nsplit);
+  if (nsplit <= 1) return;  // (uniform over the workgroup, before its barrier)
+  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int per = (nsplit + W - 1) / W;
+  const int s_begin = min(nsplit, w * per), s_end = min(nsplit, s_begin + per);
+  f32x4 acc[kMergeU];
+#pragma unroll
+  for (int u = 0; u < kMergeU; ++u) acc[u] = f32x4{};
+  float mx = -INFINITY, wsum = 0.0f;
+  merge_run<F16>(m, b, first, head, 4 * lane, s_begin, s_end, acc, mx, wsum);
+#pragma unroll
+  for (int u = 0; u < kMergeU; ++u) sacc[w][u][lane] = acc[u];
+  if (lane == 0) {
+    smx[w] = mx;
+    ssum[w] = wsum;
+  }
+  __syncthreads();
+  if (w != 0) return;
+  float cm = -INFINITY;
+#pragma unroll
+  for (int v = 0; v < W; ++v) cm = fmaxf(cm, smx[v]);
+  f32x4 o[kMergeU];
+#pragma unroll
+  for (int u = 0; u < kMergeU; ++u) o[u] = f32x4{};
+  float tot = 0.0f;
+#pragma unroll
+  for (int v = 0; v < W; ++v) {
+    // a wave without pieces (or with only empty ones) has max -inf, sum 0
+    const float r = smx[v] == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(smx[v] - cm);
+    tot += r * ssum[v];
+#pragma unroll
+    for (int u = 0; u < kMergeU; ++u) o[u] += r * sacc[v][u][lane];
+  }
+  const float inv = tot > 0.0f ? 1.0f / tot : 0.0f;
+  bf16x4* dst = (bf16x4*)((__bf16*)m.out + ((size_t)b * m.heads + head) * kDV) + lane;
+#pragma unroll
+  for (int u = 0; u < kMergeU; ++u) dst[u * 64] = __builtin_convertvector(o[u] * inv, bf16x4);
+  if (lane == 0) m.lse[(size_t)b * m.heads + head] = tot > 0.0f ? (cm + __builtin_amdgcn_logf(tot)) * kLn2 : -INFINITY;
 }
 
 int nsplit_for_heads(int heads) { return heads > 32 ? 2 : 4; }
@@ -1610,9 +1675,19 @@ hipError_t launch_decode(const DecodeLaunch& din, hipStream_t stream) {
   m.batch = d.batch;
   m.ranges = d.ranges;
   m.seg_pad = a.seg_pad;
-  const dim3 mgrid(d.batch, (d.heads + kMergeHeads - 1) / kMergeHeads);
-  if (ws_kernel) hipLaunchKernelGGL(mla_merge_kernel<true>, mgrid, dim3(kThreads), 0, stream, m);
-  else hipLaunchKernelGGL(mla_merge_kernel<false>, mgrid, dim3(kThreads), 0, stream, m);
+  // many pieces per sequence (eight or more ranges per sequence on average)
+  // or a grid of under 256 workgroups: a workgroup per (sequence, head),
+  // the pieces split over its waves
+  const int64_t narrow_wgs = (int64_t)d.batch * ((d.heads + kMergeHeads - 1) / kMergeHeads);
+  const bool wide = d.ranges >= 8 * (int64_t)d.batch || narrow_wgs < 256;
+  const dim3 mgrid(d.batch, wide ? d.heads : (d.heads + kMergeHeads - 1) / kMergeHeads);
+  if (wide) {
+    if (ws_kernel) hipLaunchKernelGGL(mla_merge_wide_kernel<true>, mgrid, dim3(kThreads), 0, stream, m);
+    else hipLaunchKernelGGL(mla_merge_wide_kernel<false>, mgrid, dim3(kThreads), 0, stream, m);
+  } else {
+    if (ws_kernel) hipLaunchKernelGGL(mla_merge_kernel<true>, mgrid, dim3(kThreads), 0, stream, m);
+    else hipLaunchKernelGGL(mla_merge_kernel<false>, mgrid, dim3(kThreads), 0, stream, m);
+  }
   return hipGetLastError();
 }
 
