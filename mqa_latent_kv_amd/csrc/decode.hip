@@ -299,7 +299,6 @@ constexpr int kPipeDma = 1, kPipeSoft = 2, kPipeMask = 4;
 constexpr int kPipeHalf = 8;   // token-split softmax: this wave's 16 tokens (S^T registers 0..7) only
 constexpr int kPipeOwnL = 16;  // full softmax, but only registers 0..7 (this wave's tokens) enter l_sum
 constexpr int kPipePv2 = 32;   // the PV that follows reads two V^T blocks ahead (pv_slot2)
-constexpr int kFenceValu = 0x2 | 0x400;  // sched_barrier mask: VALU and transcendental may cross
 
 // Publish this wave's partial: [wave][r4][lane] 16-byte rows, lane-contiguous.
 __device__ __forceinline__ void put_partial(LDS_AS f32x4* xch, const f32x16& s, int w, int lane) {

@@ -295,13 +295,19 @@ __device__ __forceinline__ uint32_t dma_lane_off(int lane, int w, int row_cap) {
 // compiler's wait-count insertion does not see it: it cannot tell which ring
 // slot a DMA targets and would otherwise wait for every copy in flight before
 // each LDS read.  The ring accounts for these copies itself (explicit vmcnt
-// before each barrier).  The kernel keeps no other value in m0.
+// before each barrier).  m0 is declared clobbered, and one wait state (s_nop 0)
+// separates the scalar write of m0 from the copy that reads it, as the
+// hardware requires between an SALU write of m0 and a VMEM load to LDS.
+// (m0 is named in the clobber list on purpose: clang warns that it is reserved)
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
 template <int OFF>
 __device__ __forceinline__ void dma16(const char* sbase, uint32_t voff, uint32_t lds_base) {
-  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1 offset:%3" ::"v"(voff), "s"(sbase),
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1 offset:%3" ::"v"(voff), "s"(sbase),
                "s"(lds_base), "n"(OFF)
-               : "memory");
+               : "memory", "m0");
 }
+#pragma clang diagnostic pop
 
 __device__ __forceinline__ const char* uniform_ptr(const char* p) {
   const uint64_t v = (uint64_t)p;

@@ -128,9 +128,13 @@ __device__ __forceinline__ void wait_ops_lgkm0(int k, int x) {
 
 // One direct global->LDS copy of 4 bytes per lane (lane i's word lands at
 // lds_base + 4i), issued and accounted like the 16-byte copies.
+// (m0 is named in the clobber list on purpose: clang warns that it is reserved)
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
 __device__ __forceinline__ void dma4(const char* sbase, uint32_t voff, uint32_t lds_base) {
-  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dword %0, %1" ::"v"(voff), "s"(sbase), "s"(lds_base) : "memory");
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dword %0, %1" ::"v"(voff), "s"(sbase), "s"(lds_base) : "memory", "m0");
 }
+#pragma clang diagnostic pop
 
 // 8 e4m3 codes as bf16 (exact: every e4m3 value is a bf16 value)
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));

@@ -614,9 +614,14 @@ constexpr int kUkCols = 32;               // W_UK output columns per workgroup
 
 // One direct global->LDS copy of 16 bytes per lane (lane i's bytes land at
 // lds + 16i): base and lds wave-uniform, voff the lane's byte offset.
+// (one wait state between the write of m0 and the copy that reads it)
+// (m0 is named in the clobber list on purpose: clang warns that it is reserved)
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
 __device__ __forceinline__ void qdma16(const void* base, uint32_t voff, uint32_t lds) {
-  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(base), "s"(lds) : "memory", "m0");
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(base), "s"(lds) : "memory", "m0");
 }
+#pragma clang diagnostic pop
 __device__ __forceinline__ const void* qd_uniform(const void* p) {
   const uint64_t v = (uint64_t)p;
   const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v), hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
