@@ -447,11 +447,11 @@ def main():
     tflops = flops / kern_avg_s / 1e12
     value = nbytes / (ms_per_step / 1e3) / 1e9
     kernels = {"topk_sparse": "mla_decode_ws_kernel<1,false,false,true> + mla_merge_kernel<true>",
-               "fp8_cache": "mla_decode_ws_kernel<1,false,false,false> + mla_merge_kernel<true>",
+               "fp8_cache": "mla_decode_ws_kernel<1,false,false,false> + mla_merge_wide_kernel<true>",
                "query_decode": "mla_qbn_kernel + mla_qlm_kernel + mla_decode_kernel<4,true,0,false> + "
-                               "mla_merge_kernel<false>",
+                               "mla_merge_wide_kernel<false>",
                "query_narrow_decode": "mla_qb_gemv_kernel + mla_ql_gemv_kernel + "
-                                      "mla_decode_ws_kernel<0,true,false,false> + mla_merge_kernel<true>",
+                                      "mla_decode_ws_kernel<0,true,false,false> + mla_merge_wide_kernel<true>",
                "insert_decode": "mla_kv_insert_kernel + mla_decode_ws_kernel<2,false,false,false> + "
                                 "mla_merge_kernel<true>",
                "mtp_bf16": "mla_decode_ws_kernel<0,false,true,false> + mla_merge_kernel<true>"}

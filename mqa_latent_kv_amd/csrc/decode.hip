@@ -51,8 +51,9 @@
 //    scheduler the STAGE_D2 note describes under "Grid vs. Persistent Tile
 //    Scheduler").  A sequence inside one range is finished in place;
 //    otherwise each piece writes its normalised partial O and its base-2
-//    LSE (both fp32), and a second kernel (mla_merge_kernel) combines
-//    the pieces.  The merge is not done by the last piece to arrive: that
+//    LSE (both fp32), and a second kernel (mla_merge_kernel, or
+//    mla_merge_wide_kernel where sequences have many pieces) combines the
+//    pieces.  The merge is not done by the last piece to arrive: that
 //    would need a device-scope release fence per piece, which on gfx950
 //    writes back the whole XCD L2.
 //  * Cache formats: bf16 rows are copied by the DMA; FP8 rows (512 codes
