@@ -270,3 +270,29 @@ def test_query_workspace_sizes_per_form(L):
         ksplit = 4 if tiles(b, h) < 256 else 1
         assert size(b, h) == align(b * 1536 * 2) + ksplit * b * h * 192 * 4 + 256, (b, h)
     assert tiles(129, 1) < 256 and tiles(129, 128) >= 256  # both forms of the split occur above
+
+
+def test_lds_dma_assembly_waits_after_writing_m0():
+    """Every inline-assembly block of the kernels that writes m0 waits one
+    cycle (s_nop) before the instruction that reads it, and names m0 in its
+    clobber list: the ISA asks for one wait state between an SALU write of m0
+    and a VMEM load to LDS, which the compiler cannot insert inside a block."""
+    csrc = os.path.join(os.path.dirname(mla.__file__), "csrc")
+    blocks = 0
+    for name in sorted(os.listdir(csrc)):
+        if not name.endswith((".hip", ".h", ".cpp")):
+            continue
+        text = open(os.path.join(csrc, name)).read()
+        for m in re.finditer(r'asm\s+volatile\s*\((.*?)\);', text, re.S):
+            body = m.group(1)
+            lead = re.match(r'\s*((?:"(?:[^"\\]|\\.)*"\s*)+)', body)  # the template's string literals
+            template = "".join(re.findall(r'"((?:[^"\\]|\\.)*)"', lead.group(1))) if lead else ""
+            if "m0" not in template:
+                continue
+            blocks += 1
+            insts = [i.strip() for i in template.replace("\\n", "\n").replace("\\t", "").split("\n") if i.strip()]
+            for k, inst in enumerate(insts):
+                if inst.startswith("s_mov_b32 m0"):
+                    assert k + 1 < len(insts) and insts[k + 1].startswith("s_nop"), (name, insts)
+            assert '"m0"' in body, (name, "m0 not in the clobber list")
+    assert blocks >= 3
