@@ -153,6 +153,16 @@ CASES = {
                                             tokens_per_seq=3, kv_format="fp8_tensor"),
     "mtp_t4_h32_fp8t_masked_mid_slot": dict(seed=127, batch=3, heads=32, seqlens=[66, 130, 1026],
                                             tokens_per_seq=4, kv_format="fp8_tensor"),
+    # one sequence cut into one-page pieces (51 and 91 of them), combined by the many-piece merge,
+    # whose last piece holds only the final 2 (1) positions: rows of the first T - 2 (T - 1) tokens
+    # see none of it, a piece with LSE -inf for those rows; then the many-piece merge at 384 query
+    # rows over the per-tensor cache, two sequences in three-page pieces
+    "wide_merge_t4_h64_hidden_last_piece": dict(seed=131, batch=1, heads=64, seqlens=[64 * 50 + 2],
+                                                tokens_per_seq=4),
+    "wide_merge_t2_h64_hidden_last_piece": dict(seed=132, batch=1, heads=64, seqlens=[64 * 90 + 1],
+                                                tokens_per_seq=2),
+    "wide_merge_t3_h128_fp8t_hidden_last_piece": dict(seed=133, batch=2, heads=128, seqlens=[64 * 70 + 2, 64 * 3],
+                                                      tokens_per_seq=3, kv_format="fp8_tensor"),
     "mtp_topk_t2_h64_fp8": dict(seed=119, batch=3, heads=64, seqlens=[3000, 800, 40], tokens_per_seq=2,
                                 kv_format="fp8", topk=512, topk_pad_max=60),
     "mtp_topk_t3_h128_bf16": dict(seed=120, batch=2, heads=128, seqlens=[2000, 300], tokens_per_seq=3, topk=256,
